@@ -1,0 +1,185 @@
+"""CPU oracle for the expert-parallel layout / dispatch / combine path.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg may import this package; the product path never does.  The
+arithmetic lives in ``oracle.c`` (plain single-threaded C, built with gcc);
+this module only marshals numpy arrays into it.  Nothing here shares code
+with the HIP library.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no fast-math, no
+    FP contraction: every rounding step is the one the C source spells out)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        p, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.oracle_f32_to_bf16.argtypes = [p, p, i64]
+        lib.oracle_f32_to_bf16.restype = None
+        lib.oracle_layout.argtypes = [i64] * 5 + [p] * 9 + [i64]
+        lib.oracle_layout.restype = i64
+        lib.oracle_dispatch.argtypes = [i64] * 5 + [p] * 8
+        lib.oracle_dispatch.restype = None
+        lib.oracle_combine.argtypes = [i64] * 4 + [p] * 6
+        lib.oracle_combine.restype = None
+        lib.oracle_ll_dispatch.argtypes = [i64] * 6 + [p] * 6
+        lib.oracle_ll_dispatch.restype = ctypes.c_int
+        lib.oracle_ll_combine.argtypes = [i64] * 6 + [p] * 4
+        lib.oracle_ll_combine.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def f32_to_bf16(f: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 bit patterns (round to nearest even)."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, dtype=np.uint16)
+    _load().oracle_f32_to_bf16(_ptr(f), _ptr(out), f.size)
+    return out
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Layout:
+    num_tokens_per_rank: np.ndarray  # int32 [R]
+    num_tokens_per_expert: np.ndarray  # int32 [E]
+    is_token_in_rank: np.ndarray  # uint8 [T, R]
+    rank_prefix_matrix: np.ndarray  # int32 [R]
+    channel_prefix_matrix: np.ndarray  # int32 [R, C]
+    recv_channel_prefix_matrix: np.ndarray  # int32 [R, C]
+    send_head: np.ndarray  # int32 [T, R]
+    recv_src_idx: np.ndarray  # int32 [N]
+
+    @property
+    def num_recv(self) -> int:
+        return int(self.recv_src_idx.shape[0])
+
+
+def layout(topk_idx: np.ndarray, E: int, R: int, C: int) -> Layout:
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    T, K = topk_idx.shape
+    cap = T * min(K, R)
+    ntpr = np.empty(R, np.int32)
+    ntpe = np.empty(E, np.int32)
+    itr = np.empty((T, R), np.uint8)
+    rpm = np.empty(R, np.int32)
+    cpm = np.empty((R, C), np.int32)
+    rcpm = np.empty((R, C), np.int32)
+    sh = np.empty((T, R), np.int32)
+    rsi = np.empty(max(cap, 1), np.int32)
+    n = _load().oracle_layout(T, K, E, R, C, _ptr(topk_idx), _ptr(ntpr), _ptr(ntpe), _ptr(itr),
+                              _ptr(rpm), _ptr(cpm), _ptr(rcpm), _ptr(sh), _ptr(rsi), cap)
+    if n < 0:
+        raise ValueError("oracle_layout rejected its arguments")
+    return Layout(ntpr, ntpe, itr, rpm, cpm, rcpm, sh, rsi[:n].copy())
+
+
+def dispatch(x: np.ndarray, topk_idx, topk_weights, E: int, R: int, lay: Layout,
+             with_topk: bool = True):
+    """Returns (recv_x, recv_topk_idx, recv_topk_weights); topk outputs are None
+    when ``with_topk`` is false (the handle-reuse dispatch)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    T, H = x.shape
+    N = lay.num_recv
+    recv_x = np.zeros((N, H), np.uint16)
+    rti = rtw = None
+    ti = tw = None
+    K = 1
+    if with_topk:
+        ti = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        K = ti.shape[1]
+        tw = np.ascontiguousarray(topk_weights, dtype=np.float32)
+        rti = np.empty((N, K), np.int64)
+        rtw = np.empty((N, K), np.float32)
+    _load().oracle_dispatch(T, H, K, E, R, _ptr(x), _ptr(ti), _ptr(tw),
+                            _ptr(lay.rank_prefix_matrix), _ptr(lay.send_head),
+                            _ptr(recv_x), _ptr(rti), _ptr(rtw))
+    return recv_x, rti, rtw
+
+
+def combine(y: np.ndarray, lay: Layout, recv_topk_weights=None, K: int = 0):
+    """Returns (out bf16 bits [T, H], combined_topk_weights [T, K] or None)."""
+    y = np.ascontiguousarray(y, dtype=np.uint16)
+    T, R = lay.send_head.shape
+    H = y.shape[1]
+    out = np.empty((T, H), np.uint16)
+    cw = None
+    rw = None
+    if recv_topk_weights is not None:
+        rw = np.ascontiguousarray(recv_topk_weights, dtype=np.float32)
+        K = rw.shape[1]
+        cw = np.empty((T, K), np.float32)
+    _load().oracle_combine(T, H, max(K, 1), R, _ptr(y), _ptr(rw), _ptr(lay.rank_prefix_matrix),
+                           _ptr(lay.send_head), _ptr(out), _ptr(cw))
+    return out, cw
+
+
+def ll_dispatch(x: np.ndarray, topk_idx: np.ndarray, E: int, R: int, num_slots: int,
+                with_buf: bool = True):
+    """Returns (buf [E/R, R, slots, H] bits or None, counts [E/R, R],
+    src_info [E/R, R, slots], topk_slot [T, K])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    ti = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    T, K = ti.shape
+    H = x.shape[1]
+    epr = E // R
+    buf = np.zeros((epr, R, num_slots, H), np.uint16) if with_buf else None
+    counts = np.empty((epr, R), np.int32)
+    src = np.empty((epr, R, num_slots), np.int32)
+    ts = np.empty((T, K), np.int32)
+    rc = _load().oracle_ll_dispatch(T, H, K, E, R, num_slots, _ptr(x), _ptr(ti), _ptr(buf),
+                                    _ptr(counts), _ptr(src), _ptr(ts))
+    if rc != 0:
+        raise ValueError("oracle_ll_dispatch rejected its arguments")
+    return buf, counts, src, ts
+
+
+def ll_combine(buf: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray, E: int, R: int):
+    buf = np.ascontiguousarray(buf, dtype=np.uint16)
+    epr, R2, num_slots, H = buf.shape
+    assert R2 == R and epr == E // R
+    ti = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    tw = np.ascontiguousarray(topk_weights, dtype=np.float32)
+    T, K = ti.shape
+    out = np.empty((T, H), np.uint16)
+    rc = _load().oracle_ll_combine(T, H, K, E, R, num_slots, _ptr(buf), _ptr(ti), _ptr(tw),
+                                   _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_ll_combine rejected its arguments")
+    return out

@@ -1,0 +1,88 @@
+"""The CPU oracle against its pins (no GPU needed)."""
+
+import pytest
+
+import pinlib
+from gen import config_inputs, generate, random_case
+
+
+def test_hand_worked_example():
+    pinlib.check_hand_example()
+
+
+def test_bruteforce_exhaustive_T3_K2_E4():
+    assert pinlib.check_bruteforce_exhaustive(T=3, K=2, E=4, Rs=(1, 2, 4)) == 5 ** 6 * 3 * 3
+
+
+def test_bruteforce_exhaustive_T2_K2_E6():
+    assert pinlib.check_bruteforce_exhaustive(T=2, K=2, E=6, Rs=(1, 2, 3, 6)) == 7 ** 4 * 4 * 3
+
+
+def test_bruteforce_exhaustive_T5_K1_E4():
+    pinlib.check_bruteforce_exhaustive(T=5, K=1, E=4, Rs=(1, 2, 4))
+
+
+def test_bruteforce_dispatch_combine():
+    pinlib.check_bruteforce_dispatch_combine(seed=0, cases=300)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_layout_invariants_full_configs(cfg):
+    pinlib.check_layout_invariants(config_inputs(cfg, with_x=False))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_layout_invariants_random(seed):
+    inp = random_case(seed, 257, 8, 24, 5, 6, 7, mask=0.2, dup=0.3)
+    pinlib.check_layout_invariants(inp)
+
+
+def test_special_cases():
+    pinlib.check_special_cases()
+
+
+@pytest.mark.parametrize("cfg", [0, 3])
+def test_dispatch_identity_combine_configs(cfg):
+    pinlib.check_identity_combine(config_inputs(cfg))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_dispatch_identity_combine_config_routing_small_rows(cfg):
+    """The full routing of the large configs with short rows (routing does not
+    depend on the row length)."""
+    inp = config_inputs(cfg, with_x=False)
+    small = generate(inp.T, 64, inp.E, inp.K, inp.R, inp.C, seed=99)
+    inp.x = small.x
+    inp.H = 64
+    pinlib.check_identity_combine(inp)
+
+
+def test_identity_combine_with_duplicates_and_masks():
+    pinlib.check_identity_combine(random_case(5, 300, 40, 16, 6, 4, 3, mask=0.25, dup=0.4))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_combine_fp64_bound(seed):
+    pinlib.check_combine_fp64(seed)
+
+
+def test_ll_config3():
+    pinlib.check_ll(config_inputs(3))
+
+
+def test_ll_random_with_masks_dups_and_overflow():
+    inp = random_case(3, 40, 16, 8, 4, 2, 1, mask=0.2, dup=0.5, slots=12)
+    pinlib.check_ll(inp)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_ll_combine_fp64_bound(seed):
+    pinlib.check_ll_fp64(seed)
+
+
+def test_bf16_edges():
+    pinlib.check_bf16_edges()
+
+
+def test_bf16_all_fp32_patterns():
+    pinlib.check_bf16_patterns(step=1)
