@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the expert-parallel hot path on one MI355X.
+
+One step = one pass of every hot-path operation over one batch of synthetic
+input, all on torch's current stream, through the C ABI:
+
+  training-scale batch (T=4096, H=7168, E=256, K=8, R=64 ranks, C=10 channels)
+    1. layout            ep_get_dispatch_layout   -> handle
+    2. dispatch          ep_dispatch(handle, x, topk_idx, topk_weights)   rows + top-k outputs
+    3. cached dispatch   ep_dispatch(handle, x2)                          rows only
+    4. combine           ep_combine(handle, y = rows of 2, weights of 2)
+    5. handle free
+  low-latency decode batch (T=128, H=7168, E=256, K=8, R=32, 128 slots)
+    6. LL dispatch       ep_ll_dispatch
+    7. LL combine        ep_ll_combine(packed rows of 6)
+
+Inputs are generated and copied to HBM before timing.  Device buffers are
+sized for the worst case (T*min(K,R) rows), so no step synchronizes the host.
+``value`` is whole-job throughput: the algorithmic bytes of all seven
+operations divided by the wall time of the timed steps.  Per-operation times
+come from HIP events recorded on the launch stream around each call; each of
+the timed calls launches exactly one kernel except the layout (three).
+
+Algorithmic bytes (what the method must move; x read once, only the N copied
+rows' positions read):
+  dispatch        (T+N)*H*2 + N*4 + T*K*12 + N*K*12
+  cached dispatch (T+N)*H*2 + N*4
+  combine         (N+T)*H*2 + N*4 + N*K*4 + T*K*4
+  layout          T*K*8 + T*R*5 + N*4
+  LL dispatch     T*H*2 + M*H*2 + T*K*12 + M*4      (M valid (token, slot) pairs)
+  LL combine      M*H*2 + T*H*2 + T*K*16
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch & combine HBM GB/s (% of peak) at T=4096,H=7168,K=8,R=64; layout Mtok/s"
+HBM_PEAK_GBS = 8000.0
+TRAIN = dict(T=4096, H=7168, E=256, K=8, R=64, C=10)
+DECODE = dict(T=128, H=7168, E=256, K=8, R=32, slots=128)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU work budget of the oracle baseline leg (0 = skip)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_sha(name: str) -> str:
+    path = os.path.join(ROOT, "combine_get_dispatch_05_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_file: str, kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    ent = data.get(kernel)
+    if not ent or ent.get("source_sha") != kernel_source_sha(kernel_file):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the hot path on one GPU only (the R ranks are logical "
+              "partitions of one GPU's HBM); --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_get_dispatch_05_amd as epm
+    from combine_get_dispatch_05_amd import abi
+    from gen import config_inputs, random_rows
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    L = abi.lib()
+    dev = torch.device("cuda", 0)
+
+    def to_dev(a, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return t.view(dtype) if dtype is not None else t
+
+    # ---------------------------------------------------------------- inputs
+    tr = config_inputs(1)
+    assert (tr.T, tr.H, tr.E, tr.K, tr.R, tr.C) == tuple(TRAIN[k] for k in "THEKRC")
+    T, H, E, K, R, C = tr.T, tr.H, tr.E, tr.K, tr.R, tr.C
+    x = to_dev(tr.x.view(np.int16), torch.bfloat16)
+    x2 = to_dev(random_rows(T, H, 0, tag=11).view(np.int16), torch.bfloat16)
+    topk = to_dev(tr.topk_idx)
+    w = to_dev(tr.topk_weights)
+    d = abi.dims(T, H, K, E, R, C)
+    cap = int(L.ep_max_recv_rows(ctypes.byref(d)))
+    recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    recv_x2 = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    rti = torch.empty((cap, K), dtype=torch.int64, device=dev)
+    rtw = torch.empty((cap, K), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    cw = torch.empty((T, K), dtype=torch.float32, device=dev)
+
+    dc = config_inputs(3)
+    dd = abi.dims(dc.T, dc.H, dc.K, dc.E, dc.R, 1)
+    S = dc.slots
+    epr = dc.E // dc.R
+    lx = to_dev(dc.x.view(np.int16), torch.bfloat16)
+    ltopk = to_dev(dc.topk_idx)
+    lw = to_dev(dc.topk_weights)
+    packed = torch.empty((epr, dc.R, S, dc.H), dtype=torch.bfloat16, device=dev)
+    lcount = torch.empty((epr, dc.R), dtype=torch.int32, device=dev)
+    lsrc = torch.empty((epr, dc.R, S), dtype=torch.int32, device=dev)
+    lslot = torch.empty((dc.T, dc.K), dtype=torch.int32, device=dev)
+    lout = torch.empty((dc.T, dc.H), dtype=torch.bfloat16, device=dev)
+
+    P = abi.ptr
+    ops = ["layout", "dispatch", "dispatch_cached", "combine", "ll_dispatch", "ll_combine"]
+
+    def step(events=None):
+        s = abi.current_stream()
+
+        def mark(i):
+            if events is not None:
+                events[i].record()
+
+        h = ctypes.c_void_p()
+        mark(0)
+        abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, ctypes.byref(h), s),
+                  "layout")
+        mark(1)
+        abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), ctypes.byref(h), P(recv_x),
+                                P(rti), P(rtw), cap, None, s), "dispatch")
+        mark(2)
+        abi.check(L.ep_dispatch(ctypes.byref(d), P(x2), None, None, ctypes.byref(h), P(recv_x2),
+                                None, None, cap, None, s), "cached dispatch")
+        mark(3)
+        abi.check(L.ep_combine(h, H, P(recv_x), cap, P(rtw), P(out), P(cw), s), "combine")
+        mark(4)
+        L.ep_handle_free(h)
+        abi.check(L.ep_ll_dispatch(ctypes.byref(dd), S, P(lx), P(ltopk), P(packed), P(lcount),
+                                   P(lsrc), P(lslot), s), "ll dispatch")
+        mark(5)
+        abi.check(L.ep_ll_combine(ctypes.byref(dd), S, P(packed), P(ltopk), P(lw), P(lslot),
+                                  P(lout), s), "ll combine")
+        mark(6)
+
+    # N and M for the byte counts
+    step()
+    torch.cuda.synchronize()
+    h = ctypes.c_void_p()
+    abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, ctypes.byref(h),
+                                       abi.current_stream()), "layout")
+    n = ctypes.c_int64()
+    abi.check(L.ep_handle_num_recv(h, ctypes.byref(n)), "num_recv")
+    L.ep_handle_free(h)
+    N = int(n.value)
+    M = int((dc.topk_idx >= 0).sum())
+
+    by = {
+        "layout": T * K * 8 + T * R * 5 + N * 4,
+        "dispatch": (T + N) * H * 2 + N * 4 + T * K * 12 + N * K * 12,
+        "dispatch_cached": (T + N) * H * 2 + N * 4,
+        "combine": (N + T) * H * 2 + N * 4 + N * K * 4 + T * K * 4,
+        "ll_dispatch": dc.T * dc.H * 2 + M * dc.H * 2 + dc.T * dc.K * 12 + M * 4,
+        "ll_combine": M * dc.H * 2 + dc.T * dc.H * 2 + dc.T * dc.K * 16,
+    }
+    step_bytes = sum(by.values())
+
+    # ---------------------------------------------------------------- timing
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_op_ms = {op: [] for op in ops}
+    for e in ev:
+        for j, op in enumerate(ops):
+            per_op_ms[op].append(e[j].elapsed_time(e[j + 1]))
+    avg_us = {op: 1e3 * float(np.mean(v)) for op, v in per_op_ms.items()}
+    med_us = {op: 1e3 * float(np.median(v)) for op, v in per_op_ms.items()}
+    min_us = {op: 1e3 * float(np.min(v)) for op, v in per_op_ms.items()}
+
+    ms_per_step = 1e3 * wall / args.steps
+    value = step_bytes / (wall / args.steps) / 1e9
+
+    op_report = {}
+    for op in ops:
+        gbs = by[op] / (avg_us[op] * 1e-6) / 1e9
+        op_report[op] = {"avg_us": round(avg_us[op], 2), "median_us": round(med_us[op], 2),
+                         "min_us": round(min_us[op], 2), "bytes": by[op], "gbs": round(gbs, 1),
+                         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    op_report["layout"]["mtok_s"] = round(T / (avg_us["layout"] * 1e-6) / 1e6, 2)
+    op_report["layout"]["kernels"] = 3
+
+    # dominant kernel: the single-kernel operation with the largest time share
+    kern = {"dispatch": ("dispatch.hip", "dispatch_pack_kernel"),
+            "dispatch_cached": ("dispatch.hip", "dispatch_pack_kernel"),
+            "combine": ("combine.hip", "combine_kernel")}
+    dom = max(kern, key=lambda op: avg_us[op])
+    achieved = by[dom] / (avg_us[dom] * 1e-6) / 1e9
+    traffic = load_traffic(kern[dom][0], f"{dom}:{kern[dom][1]}")
+    roofline = {"bound": "hbm", "kernel": f"{kern[dom][1]} ({dom})",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    # ---------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline and args.cpu_seconds > 0:
+        cpu = cpu_baseline(tr, dc, x2_bits=random_rows(T, H, 0, tag=11), budget=args.cpu_seconds,
+                           step_bytes=step_bytes)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "training-scale EP layout+dispatch+cached dispatch+combine "
+                        "(T=4096,H=7168,E=256,K=8,R=64,C=10, uniform distinct top-8) + "
+                        "low-latency decode dispatch+combine (T=128,H=7168,E=256,K=8,R=32,"
+                        "128 slots), one GPU",
+            "T": T, "H": H, "E": E, "K": K, "R": R, "C": C, "N": N,
+            "ll": {"T": dc.T, "R": dc.R, "slots": S, "M": M},
+            "step_bytes": step_bytes,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ops": op_report,
+    }
+    print(json.dumps(rec))
+
+
+def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int):
+    """The oracle, as it stands, on the same rows of the same workload:
+    whole passes (layout, dispatch, cached dispatch, combine, LL dispatch,
+    LL combine) until ``budget`` seconds of CPU work are spent."""
+    import oracle
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        lay = oracle.layout(tr.topk_idx, tr.E, tr.R, tr.C)
+        rx, rti, rtw = oracle.dispatch(tr.x, tr.topk_idx, tr.topk_weights, tr.E, tr.R, lay)
+        oracle.dispatch(x2_bits, None, None, tr.E, tr.R, lay, with_topk=False)
+        oracle.combine(rx, lay, rtw)
+        buf, _, _, _ = oracle.ll_dispatch(dc.x, dc.topk_idx, dc.E, dc.R, dc.slots)
+        oracle.ll_combine(buf, dc.topk_idx, dc.topk_weights, dc.E, dc.R)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget:
+            break
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(step_bytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} whole passes of the benchmark step (same workload, same rows) "
+                      f"in {el:.1f} s, single-threaded C oracle",
+            "host_cpu": model or platform.processor(), "host_nproc": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

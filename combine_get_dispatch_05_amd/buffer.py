@@ -1,0 +1,277 @@
+"""PyTorch-facing façade over libep.so with the call shapes of the pages' Buffer.
+
+"DeepEP Buffer Class API for Expert Parallel Communication" describes a
+``Buffer`` with ``get_dispatch_layout``, ``dispatch`` (6 results),
+``combine`` (3 results), ``low_latency_dispatch`` (5 results),
+``low_latency_combine`` (3 results) and ``destroy``.  This class keeps those
+names and result arities so callers can switch; the slots that carried a CUDA
+event or receive hook hold ``None`` (work is ordered on torch's current
+stream instead).  The R ranks are logical partitions of this GPU's memory.
+
+Only argument marshalling happens here: every step runs in the HIP kernels
+behind the C ABI.  Tensors must live on the current CUDA (HIP) device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import abi
+
+
+def _need(t: torch.Tensor, dtype, name: str, ndim: int):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class Layout:
+    """Device copies of a dispatch layout ("What the Handle Contains")."""
+
+    num_tokens_per_rank: torch.Tensor  # int32 [R]
+    num_tokens_per_expert: torch.Tensor  # int32 [E]
+    is_token_in_rank: torch.Tensor  # bool [T, R]
+    rank_prefix_matrix: torch.Tensor  # int32 [R]
+    channel_prefix_matrix: torch.Tensor  # int32 [R, C]
+    recv_channel_prefix_matrix: torch.Tensor  # int32 [R, C]
+    send_head: torch.Tensor  # int32 [T, R]
+    recv_src_idx: torch.Tensor  # int32 [N]
+
+
+class Handle:
+    """Opaque dispatch layout owned by the library (freed on ``free()`` or
+    garbage collection, ordered after the work already enqueued)."""
+
+    def __init__(self, raw: int, d: abi.Dims, device: torch.device):
+        self._raw = raw
+        self.dims = d
+        self.device = device
+
+    @property
+    def raw(self) -> ctypes.c_void_p:
+        if not self._raw:
+            raise ValueError("handle already freed")
+        return ctypes.c_void_p(self._raw)
+
+    @property
+    def num_recv(self) -> int:
+        """N, the number of packed rows (reads it back once)."""
+        n = ctypes.c_int64(0)
+        abi.check(abi.lib().ep_handle_num_recv(self.raw, ctypes.byref(n)), "ep_handle_num_recv")
+        return int(n.value)
+
+    @property
+    def nbytes(self) -> int:
+        return int(abi.lib().ep_handle_nbytes(self.raw))
+
+    def layout(self) -> Layout:
+        d = self.dims
+        T, R, E, C = d.num_tokens, d.num_ranks, d.num_experts, d.num_channels
+        n = self.num_recv
+        i32 = dict(dtype=torch.int32, device=self.device)
+        lay = Layout(torch.empty(R, **i32), torch.empty(E, **i32),
+                     torch.empty((T, R), dtype=torch.uint8, device=self.device),
+                     torch.empty(R, **i32), torch.empty((R, C), **i32), torch.empty((R, C), **i32),
+                     torch.empty((T, R), **i32), torch.empty(max(n, 1), **i32))
+        out = abi.LayoutOut(lay.num_tokens_per_rank.data_ptr(), lay.num_tokens_per_expert.data_ptr(),
+                            lay.is_token_in_rank.data_ptr(), lay.rank_prefix_matrix.data_ptr(),
+                            lay.channel_prefix_matrix.data_ptr(),
+                            lay.recv_channel_prefix_matrix.data_ptr(), lay.send_head.data_ptr(),
+                            lay.recv_src_idx.data_ptr(), n)
+        abi.check(abi.lib().ep_handle_copy_layout(self.raw, ctypes.byref(out), abi.current_stream()),
+                  "ep_handle_copy_layout")
+        lay.is_token_in_rank = lay.is_token_in_rank.view(torch.bool)
+        lay.recv_src_idx = lay.recv_src_idx[:n]
+        return lay
+
+    def free(self) -> None:
+        if self._raw:
+            abi.lib().ep_handle_free(ctypes.c_void_p(self._raw))
+            self._raw = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+@dataclass
+class LowLatencyHandle:
+    """What low_latency_combine needs to find each (token, slot)'s cell."""
+
+    src_info: torch.Tensor  # int32 [E/R, R, slots]
+    topk_slot: torch.Tensor  # int32 [T, K]
+    num_slots: int
+    num_experts: int
+    hidden: int
+
+
+class Buffer:
+    """Expert-parallel layout / dispatch / combine over R logical ranks of one GPU."""
+
+    def __init__(self, num_ranks: int, num_experts: int, num_channels: int = 1):
+        if num_experts % num_ranks:
+            raise ValueError("num_experts must be a multiple of num_ranks")
+        self.num_ranks = int(num_ranks)
+        self.num_experts = int(num_experts)
+        self.num_channels = int(num_channels)
+        self.destroyed = False
+
+    @property
+    def num_local_experts(self) -> int:
+        return self.num_experts // self.num_ranks
+
+    def _dims(self, T: int, H: int, K: int) -> abi.Dims:
+        return abi.dims(T, H, K, self.num_experts, self.num_ranks, self.num_channels)
+
+    # -------------------------------------------------------------- layout
+    def get_dispatch_layout(self, topk_idx: torch.Tensor, keep_handle: bool = False):
+        """Returns (num_tokens_per_rank [R], num_tokens_per_expert [E],
+        is_token_in_rank [T, R] bool, handle or None).  A kept handle can be
+        passed to one ``dispatch`` together with the same ``topk_idx``."""
+        _need(topk_idx, torch.int64, "topk_idx", 2)
+        T, K = topk_idx.shape
+        d = self._dims(T, 8, K)
+        dev = topk_idx.device
+        ntpr = torch.empty(self.num_ranks, dtype=torch.int32, device=dev)
+        ntpe = torch.empty(self.num_experts, dtype=torch.int32, device=dev)
+        itr = torch.empty((T, self.num_ranks), dtype=torch.uint8, device=dev)
+        out = abi.LayoutOut(ntpr.data_ptr(), ntpe.data_ptr(), itr.data_ptr(), None, None, None,
+                            None, None, 0)
+        raw = ctypes.c_void_p()
+        abi.check(abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk_idx),
+                                                   ctypes.byref(out),
+                                                   ctypes.byref(raw) if keep_handle else None,
+                                                   abi.current_stream()),
+                  "ep_get_dispatch_layout")
+        h = Handle(raw.value, d, dev) if keep_handle else None
+        return ntpr, ntpe, itr.view(torch.bool), h
+
+    # ------------------------------------------------------------ dispatch
+    def dispatch(self, x: torch.Tensor, topk_idx: Optional[torch.Tensor] = None,
+                 topk_weights: Optional[torch.Tensor] = None, handle: Optional[Handle] = None):
+        """Returns (recv_x [N, H], recv_topk_idx [N, K] or None,
+        recv_topk_weights [N, K] or None, num_recv_tokens_per_expert [R, E/R],
+        handle, None).  Without a handle the layout is computed and N is read
+        back (one host sync); with a handle from an earlier dispatch only the
+        rows are packed and topk arguments are refused."""
+        _need(x, torch.bfloat16, "x", 2)
+        T, H = x.shape
+        if handle is None and topk_idx is None:
+            raise ValueError("dispatch without a handle needs topk_idx")
+        if topk_idx is not None:
+            _need(topk_idx, torch.int64, "topk_idx", 2)
+            if topk_idx.shape[0] != T:
+                raise ValueError("topk_idx and x disagree on the number of tokens")
+        if topk_weights is not None:
+            _need(topk_weights, torch.float32, "topk_weights", 2)
+        K = topk_idx.shape[1] if topk_idx is not None else handle.dims.num_topk
+        d = self._dims(T, H, K)
+        dev = x.device
+        raw = ctypes.c_void_p(handle.raw.value if handle is not None else None)
+        if handle is not None and handle.dims.num_tokens != T:
+            raise ValueError("handle was made for another number of tokens")
+        cap = handle.num_recv if handle is not None else int(abi.lib().ep_max_recv_rows(ctypes.byref(d)))
+        recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+        rti = torch.empty((cap, K), dtype=torch.int64, device=dev) if topk_idx is not None else None
+        rtw = torch.empty((cap, K), dtype=torch.float32, device=dev) if topk_weights is not None else None
+        n = ctypes.c_int64(-1)
+        abi.check(abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), abi.ptr(topk_idx),
+                                        abi.ptr(topk_weights), ctypes.byref(raw), abi.ptr(recv_x),
+                                        abi.ptr(rti), abi.ptr(rtw), cap, ctypes.byref(n),
+                                        abi.current_stream()),
+                  "ep_dispatch")
+        if handle is None:
+            handle = Handle(raw.value, d, dev)
+        N = int(n.value)
+        lay_counts = None
+        if topk_idx is not None:
+            lay_counts = self._expert_counts(handle)
+        return (recv_x[:N], rti[:N] if rti is not None else None,
+                rtw[:N] if rtw is not None else None, lay_counts, handle, None)
+
+    def _expert_counts(self, handle: Handle) -> torch.Tensor:
+        ntpe = torch.empty(self.num_experts, dtype=torch.int32, device=handle.device)
+        out = abi.LayoutOut(None, ntpe.data_ptr(), None, None, None, None, None, None, 0)
+        abi.check(abi.lib().ep_handle_copy_layout(handle.raw, ctypes.byref(out),
+                                                  abi.current_stream()),
+                  "ep_handle_copy_layout")
+        return ntpe.view(self.num_ranks, self.num_local_experts)
+
+    # ------------------------------------------------------------- combine
+    def combine(self, x: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None):
+        """Returns (combined_x [T, H] bf16, combined_topk_weights [T, K] or
+        None, None): the ascending-rank fp32 sum of each token's rows."""
+        _need(x, torch.bfloat16, "x", 2)
+        if topk_weights is not None:
+            _need(topk_weights, torch.float32, "topk_weights", 2)
+        d = handle.dims
+        T, H = d.num_tokens, x.shape[1]
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+        cw = None
+        if topk_weights is not None:
+            cw = torch.empty((T, d.num_topk), dtype=torch.float32, device=x.device)
+        abi.check(abi.lib().ep_combine(handle.raw, H, abi.ptr(x), x.shape[0], abi.ptr(topk_weights),
+                                       abi.ptr(out), abi.ptr(cw), abi.current_stream()),
+                  "ep_combine")
+        return out, cw, None
+
+    # --------------------------------------------------------- low latency
+    def low_latency_dispatch(self, x: torch.Tensor, topk_idx: torch.Tensor,
+                             num_max_dispatch_tokens_per_rank: int,
+                             num_experts: Optional[int] = None):
+        """Returns (packed_x [E/R, R, slots, H], packed_count [E/R, R],
+        handle, None, None).  Unused packed cells are left as allocated."""
+        if num_experts is not None and num_experts != self.num_experts:
+            raise ValueError("num_experts differs from the buffer's")
+        _need(x, torch.bfloat16, "x", 2)
+        _need(topk_idx, torch.int64, "topk_idx", 2)
+        T, H = x.shape
+        K = topk_idx.shape[1]
+        S = int(num_max_dispatch_tokens_per_rank)
+        d = self._dims(T, H, K)
+        dev = x.device
+        epr, R = self.num_local_experts, self.num_ranks
+        packed = torch.empty((epr, R, S, H), dtype=torch.bfloat16, device=dev)
+        count = torch.empty((epr, R), dtype=torch.int32, device=dev)
+        src = torch.empty((epr, R, S), dtype=torch.int32, device=dev)
+        slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+        abi.check(abi.lib().ep_ll_dispatch(ctypes.byref(d), S, abi.ptr(x), abi.ptr(topk_idx),
+                                           abi.ptr(packed), abi.ptr(count), abi.ptr(src),
+                                           abi.ptr(slot), abi.current_stream()),
+                  "ep_ll_dispatch")
+        return packed, count, LowLatencyHandle(src, slot, S, self.num_experts, H), None, None
+
+    def low_latency_combine(self, x: torch.Tensor, topk_idx: torch.Tensor,
+                            topk_weights: torch.Tensor, handle: LowLatencyHandle):
+        """x has packed_x's layout [E/R, R, slots, H].  Returns (combined_x
+        [T, H] bf16, None, None)."""
+        _need(x, torch.bfloat16, "x", 4)
+        _need(topk_idx, torch.int64, "topk_idx", 2)
+        _need(topk_weights, torch.float32, "topk_weights", 2)
+        T, K = topk_idx.shape
+        H = x.shape[3]
+        d = self._dims(T, H, K)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+        abi.check(abi.lib().ep_ll_combine(ctypes.byref(d), handle.num_slots, abi.ptr(x),
+                                          abi.ptr(topk_idx), abi.ptr(topk_weights),
+                                          abi.ptr(handle.topk_slot), abi.ptr(out),
+                                          abi.current_stream()),
+                  "ep_ll_combine")
+        return out, None, None
+
+    def destroy(self) -> None:
+        """Return pooled device memory of the current device."""
+        abi.check(abi.lib().ep_pool_trim(), "ep_pool_trim")
+        self.destroyed = True

@@ -1,0 +1,599 @@
+// ep_api.hip -- host runtime and C ABI of libep.so (declared in include/ep.h).
+//
+// Owns argument validation ("Memory Alignment and Validation" of the DeepEP-Lib
+// "Core Implementation" page: int4-multiple rows, aligned buffers), the
+// dispatch handle ("What the Handle Contains" of "How DeepEP Optimizes Handle
+// Reuse for Repeated Dispatches"), and a stream-ordered per-device pool of
+// handle arenas so that creating a handle per step does not call hipMalloc
+// after the first step.  Every kernel launch is enqueued on the caller's
+// stream; the host only waits where the ABI says so (reading N back when a
+// caller asks for it or when a buffer is smaller than the worst case).
+
+#include <atomic>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "ep_internal.h"
+
+using namespace ep;
+
+namespace {
+
+thread_local std::string g_last_hip;
+
+int hip_fail(hipError_t e)
+{
+    g_last_hip = hipGetErrorString(e);
+    return EP_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ pool
+
+struct Arena {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;  // recorded when the arena was returned
+    bool pending = false;
+};
+
+struct DevicePool {
+    std::mutex mu;
+    std::multimap<size_t, Arena> free_list;
+};
+
+// Pools live until the process ends (never destroyed, so no HIP call runs
+// from a static destructor after the runtime has gone).
+DevicePool &pool_for(int dev)
+{
+    static std::mutex mu;
+    static std::map<int, DevicePool *> pools;
+    std::lock_guard<std::mutex> g(mu);
+    DevicePool *&p = pools[dev];
+    if (p == nullptr)
+        p = new DevicePool();
+    return *p;
+}
+
+size_t round_arena(size_t b)
+{
+    const size_t g = size_t(64) << 10;
+    return b == 0 ? g : (b + g - 1) / g * g;
+}
+
+int trim_pool(DevicePool &P)
+{
+    std::multimap<size_t, Arena> drop;
+    {
+        std::lock_guard<std::mutex> g(P.mu);
+        drop.swap(P.free_list);
+    }
+    int rc = EP_OK;
+    for (auto &kv : drop) {
+        Arena &a = kv.second;
+        if (a.pending) {
+            hipError_t e = hipEventSynchronize(a.done);
+            if (e != hipSuccess)
+                rc = hip_fail(e);
+        }
+        hipEventDestroy(a.done);
+        hipFree(a.ptr);
+    }
+    return rc;
+}
+
+int arena_get(int dev, size_t bytes, hipStream_t stream, Arena *out)
+{
+    bytes = round_arena(bytes);
+    DevicePool &P = pool_for(dev);
+    bool found = false;
+    {
+        std::lock_guard<std::mutex> g(P.mu);
+        auto it = P.free_list.lower_bound(bytes);
+        if (it != P.free_list.end() && it->first <= 2 * bytes) {
+            *out = it->second;
+            P.free_list.erase(it);
+            found = true;
+        }
+    }
+    if (found) {
+        if (out->pending) {
+            hipError_t e = hipStreamWaitEvent(stream, out->done, 0);
+            if (e != hipSuccess) {
+                std::lock_guard<std::mutex> g(P.mu);
+                P.free_list.emplace(out->bytes, *out);
+                return hip_fail(e);
+            }
+        }
+        return EP_OK;
+    }
+    void *p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e == hipErrorOutOfMemory) {
+        (void)hipGetLastError();
+        trim_pool(P);
+        e = hipMalloc(&p, bytes);
+    }
+    if (e == hipErrorOutOfMemory) {
+        (void)hipGetLastError();
+        return EP_ERR_NOMEM;
+    }
+    if (e != hipSuccess)
+        return hip_fail(e);
+    hipEvent_t ev = nullptr;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        hipFree(p);
+        return hip_fail(e);
+    }
+    out->ptr = p;
+    out->bytes = bytes;
+    out->done = ev;
+    out->pending = false;
+    return EP_OK;
+}
+
+void arena_put(int dev, Arena a, hipStream_t stream)
+{
+    hipError_t e = hipEventRecord(a.done, stream);
+    a.pending = e == hipSuccess;
+    if (e != hipSuccess) {
+        // Cannot order the reuse after the pending work: wait for it here.
+        (void)hipGetLastError();
+        hipStreamSynchronize(stream);
+    }
+    DevicePool &P = pool_for(dev);
+    std::lock_guard<std::mutex> g(P.mu);
+    P.free_list.emplace(a.bytes, a);
+}
+
+// ------------------------------------------------------------ validation
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_dims(const ep_dims *d)
+{
+    if (d == nullptr)
+        return EP_ERR_INVALID;
+    if (d->num_tokens < 0 || d->num_tokens > kMaxTokens)
+        return EP_ERR_INVALID;
+    if (d->hidden <= 0 || d->hidden > kMaxHidden)
+        return EP_ERR_INVALID;
+    if (d->hidden % 8 != 0)
+        return EP_ERR_ALIGN;  // a row must be whole 16-byte vectors
+    if (d->num_topk < 1 || d->num_topk > kMaxTopk)
+        return EP_ERR_INVALID;
+    if (d->num_ranks < 1 || d->num_ranks > kMaxRanks)
+        return EP_ERR_INVALID;
+    if (d->num_experts < d->num_ranks || d->num_experts > kMaxExperts ||
+        d->num_experts % d->num_ranks != 0)
+        return EP_ERR_INVALID;
+    if (d->num_channels < 1 || d->num_channels > kMaxChannels)
+        return EP_ERR_INVALID;
+    return EP_OK;
+}
+
+int64_t max_rows(const ep_dims &d)
+{
+    const int64_t km = d.num_topk < d.num_ranks ? d.num_topk : d.num_ranks;
+    return int64_t(d.num_tokens) * km;
+}
+
+bool same_layout_dims(const ep_dims &a, const ep_dims &b)
+{
+    return a.num_tokens == b.num_tokens && a.num_topk == b.num_topk &&
+           a.num_experts == b.num_experts && a.num_ranks == b.num_ranks &&
+           a.num_channels == b.num_channels;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- handle
+
+struct ep_handle {
+    ep_dims dims;
+    LayoutShape shape;
+    int device = 0;
+    Arena arena;
+    LayoutBufs bufs;
+    std::atomic<int64_t> num_recv{-1};  // N on the host once read back
+    std::atomic<bool> dispatched{false};
+    std::atomic<hipStream_t> last_stream{nullptr};
+};
+
+namespace {
+
+int create_handle(const ep_dims &d, const int64_t *topk_idx, hipStream_t stream, ep_handle **out)
+{
+    ep_handle *h = new (std::nothrow) ep_handle();
+    if (h == nullptr)
+        return EP_ERR_NOMEM;
+    h->dims = d;
+    h->shape = layout_shape(d);
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e);
+    }
+    size_t off[14];
+    const size_t bytes = layout_arena_bytes(h->shape, off);
+    int rc = arena_get(h->device, bytes, stream, &h->arena);
+    if (rc != EP_OK) {
+        delete h;
+        return rc;
+    }
+    h->bufs = layout_bufs_at(h->arena.ptr, off);
+    e = launch_layout(h->shape, topk_idx, h->bufs, stream);
+    h->last_stream = stream;
+    if (e != hipSuccess) {
+        ep_handle_free(h);
+        return hip_fail(e);
+    }
+    *out = h;
+    return EP_OK;
+}
+
+int read_num_recv(ep_handle *h, hipStream_t stream, int64_t *n)
+{
+    int64_t v = h->num_recv.load();
+    if (v < 0) {
+        hipError_t e = hipMemcpyAsync(&v, h->bufs.num_recv, sizeof(int64_t), hipMemcpyDeviceToHost,
+                                      stream);
+        if (e == hipSuccess)
+            e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        h->num_recv.store(v);
+    }
+    *n = v;
+    return EP_OK;
+}
+
+// Is a buffer of `cap` rows large enough?  Reads N only when cap is below
+// the worst case.
+int check_capacity(ep_handle *h, int64_t cap, hipStream_t stream)
+{
+    if (cap >= max_rows(h->dims))
+        return EP_OK;
+    int64_t n = 0;
+    int rc = read_num_recv(h, stream, &n);
+    if (rc != EP_OK)
+        return rc;
+    return n <= cap ? EP_OK : EP_ERR_CAPACITY;
+}
+
+int copy_layout(ep_handle *h, const ep_layout_out *o, hipStream_t stream)
+{
+    const int64_t T = h->dims.num_tokens, R = h->dims.num_ranks, E = h->dims.num_experts;
+    const int64_t C = h->dims.num_channels;
+    const void *ptrs[8] = {o->num_tokens_per_rank,   o->num_tokens_per_expert,
+                           o->is_token_in_rank,      o->rank_prefix_matrix,
+                           o->channel_prefix_matrix, o->recv_channel_prefix_matrix,
+                           o->send_head,             o->recv_src_idx};
+    for (int i = 0; i < 8; ++i)
+        if (ptrs[i] != nullptr && i != 2 && !aligned(ptrs[i], 4))
+            return EP_ERR_ALIGN;
+    int64_t src_rows = max_rows(h->dims);
+    if (o->recv_src_idx != nullptr) {
+        if (o->recv_src_cap < 0)
+            return EP_ERR_INVALID;
+        if (o->recv_src_cap < src_rows) {
+            int64_t n = 0;
+            int rc = read_num_recv(h, stream, &n);
+            if (rc != EP_OK)
+                return rc;
+            if (n > o->recv_src_cap)
+                return EP_ERR_CAPACITY;
+            src_rows = n;
+        }
+    }
+    struct Item {
+        void *dst;
+        const void *src;
+        size_t bytes;
+    } items[8] = {
+        {o->num_tokens_per_rank, h->bufs.num_tokens_per_rank, size_t(R) * 4},
+        {o->num_tokens_per_expert, h->bufs.num_tokens_per_expert, size_t(E) * 4},
+        {o->is_token_in_rank, h->bufs.is_token_in_rank, size_t(T * R)},
+        {o->rank_prefix_matrix, h->bufs.rank_prefix_matrix, size_t(R) * 4},
+        {o->channel_prefix_matrix, h->bufs.channel_prefix_matrix, size_t(R * C) * 4},
+        {o->recv_channel_prefix_matrix, h->bufs.recv_channel_prefix_matrix, size_t(R * C) * 4},
+        {o->send_head, h->bufs.send_head, size_t(T * R) * 4},
+        {o->recv_src_idx, h->bufs.recv_src_idx, size_t(src_rows) * 4},
+    };
+    for (const Item &it : items) {
+        if (it.dst == nullptr || it.bytes == 0)
+            continue;
+        hipError_t e = hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess)
+            return hip_fail(e);
+    }
+    h->last_stream = stream;
+    return EP_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------- ABI
+
+extern "C" {
+
+int64_t ep_max_recv_rows(const ep_dims *dims)
+{
+    if (check_dims(dims) != EP_OK)
+        return -1;
+    return max_rows(*dims);
+}
+
+int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, ep_layout_out *out,
+                           ep_handle **handle_out, ep_stream_t stream_)
+{
+    try {
+        int rc = check_dims(dims);
+        if (rc != EP_OK)
+            return rc;
+        if (dims->num_tokens > 0 && topk_idx == nullptr)
+            return EP_ERR_INVALID;
+        if (!aligned(topk_idx, 8))
+            return EP_ERR_ALIGN;
+        if (out == nullptr && handle_out == nullptr)
+            return EP_ERR_INVALID;
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        ep_handle *h = nullptr;
+        rc = create_handle(*dims, topk_idx, stream, &h);
+        if (rc != EP_OK)
+            return rc;
+        if (out != nullptr)
+            rc = copy_layout(h, out, stream);
+        if (handle_out != nullptr)
+            *handle_out = h;
+        else
+            ep_handle_free(h);
+        return rc;
+    } catch (const std::bad_alloc &) {
+        return EP_ERR_NOMEM;
+    } catch (...) {
+        return EP_ERR_INVALID;
+    }
+}
+
+int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
+                const float *topk_weights, ep_handle **handle, void *recv_x,
+                int64_t *recv_topk_idx, float *recv_topk_weights, int64_t recv_cap,
+                int64_t *num_recv, ep_stream_t stream_)
+{
+    try {
+        int rc = check_dims(dims);
+        if (rc != EP_OK)
+            return rc;
+        if (handle == nullptr)
+            return EP_ERR_INVALID;
+        const bool rows = dims->num_tokens > 0;
+        if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 8) ||
+            !aligned(recv_topk_idx, 8) || !aligned(topk_weights, 4) ||
+            !aligned(recv_topk_weights, 4))
+            return EP_ERR_ALIGN;
+        if (recv_x != nullptr && x == nullptr && rows)
+            return EP_ERR_INVALID;
+        if (recv_topk_idx != nullptr && topk_idx == nullptr)
+            return EP_ERR_INVALID;
+        if (recv_topk_weights != nullptr && (topk_weights == nullptr || topk_idx == nullptr))
+            return EP_ERR_INVALID;
+        if (recv_cap < 0)
+            return EP_ERR_INVALID;
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+        ep_handle *h = *handle;
+        const bool fresh = h == nullptr;
+        if (fresh) {
+            if (topk_idx == nullptr && rows)
+                return EP_ERR_INVALID;
+        } else {
+            if (!same_layout_dims(h->dims, *dims))
+                return EP_ERR_HANDLE;
+            // A handle returned by a dispatch is the cached fast path: the
+            // layout is known, so new routing is refused.
+            if (h->dispatched.load() && (topk_idx != nullptr || topk_weights != nullptr))
+                return EP_ERR_INVALID;
+        }
+        if (fresh) {
+            rc = create_handle(*dims, topk_idx, stream, &h);
+            if (rc != EP_OK)
+                return rc;
+            *handle = h;
+        }
+        const bool pack = recv_x != nullptr || recv_topk_idx != nullptr || recv_topk_weights != nullptr;
+        if (pack) {
+            rc = check_capacity(h, recv_cap, stream);
+            if (rc != EP_OK)
+                return rc;
+            hipError_t e = launch_dispatch(h->shape, dims->hidden, x, h->bufs, topk_idx,
+                                           topk_weights, recv_x, recv_topk_idx,
+                                           recv_topk_weights, stream);
+            if (e != hipSuccess)
+                return hip_fail(e);
+            h->dispatched = true;
+        }
+        h->last_stream = stream;
+        if (num_recv != nullptr) {
+            rc = read_num_recv(h, stream, num_recv);
+            if (rc != EP_OK)
+                return rc;
+        }
+        return EP_OK;
+    } catch (const std::bad_alloc &) {
+        return EP_ERR_NOMEM;
+    } catch (...) {
+        return EP_ERR_INVALID;
+    }
+}
+
+int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
+               const float *recv_topk_weights, void *out, float *combined_topk_weights,
+               ep_stream_t stream_)
+{
+    try {
+        if (h == nullptr)
+            return EP_ERR_HANDLE;
+        if (hidden <= 0 || hidden > kMaxHidden)
+            return EP_ERR_INVALID;
+        if (hidden % 8 != 0)
+            return EP_ERR_ALIGN;
+        if (!aligned(y, 16) || !aligned(out, 16) || !aligned(recv_topk_weights, 4) ||
+            !aligned(combined_topk_weights, 4))
+            return EP_ERR_ALIGN;
+        const bool rows = h->dims.num_tokens > 0;
+        if (rows && (out == nullptr || y == nullptr))
+            return EP_ERR_INVALID;
+        if (combined_topk_weights != nullptr && recv_topk_weights == nullptr)
+            return EP_ERR_INVALID;
+        if (y_rows < 0)
+            return EP_ERR_INVALID;
+        hipStream_t stream = static_cast<hipStream_t>(stream_);
+        int rc = check_capacity(h, y_rows, stream);
+        if (rc != EP_OK)
+            return rc;
+        hipError_t e = launch_combine(h->shape, hidden, y, h->bufs, recv_topk_weights, out,
+                                      combined_topk_weights, stream);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        h->last_stream = stream;
+        return EP_OK;
+    } catch (...) {
+        return EP_ERR_INVALID;
+    }
+}
+
+int ep_ll_dispatch(const ep_dims *dims, int32_t num_slots, const void *x,
+                   const int64_t *topk_idx, void *packed_x, int32_t *packed_count,
+                   int32_t *src_info, int32_t *topk_slot, ep_stream_t stream_)
+{
+    if (dims == nullptr)
+        return EP_ERR_INVALID;
+    ep_dims d = *dims;
+    d.num_channels = 1;  // channels do not apply to the low-latency path
+    int rc = check_dims(&d);
+    if (rc != EP_OK)
+        return rc;
+    if (num_slots < 1 || num_slots > kMaxLLSlots)
+        return EP_ERR_INVALID;
+    if (d.num_tokens > num_slots)
+        return EP_ERR_CAPACITY;
+    if (packed_count == nullptr || src_info == nullptr)
+        return EP_ERR_INVALID;
+    if (d.num_tokens > 0 && (topk_idx == nullptr || topk_slot == nullptr))
+        return EP_ERR_INVALID;
+    if (packed_x != nullptr && x == nullptr && d.num_tokens > 0)
+        return EP_ERR_INVALID;
+    if (!aligned(x, 16) || !aligned(packed_x, 16) || !aligned(topk_idx, 8) ||
+        !aligned(packed_count, 4) || !aligned(src_info, 4) || !aligned(topk_slot, 4))
+        return EP_ERR_ALIGN;
+    hipError_t e = launch_ll_dispatch(d, num_slots, x, topk_idx, packed_x, packed_count, src_info,
+                                      topk_slot, static_cast<hipStream_t>(stream_));
+    return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
+int ep_ll_combine(const ep_dims *dims, int32_t num_slots, const void *packed_y,
+                  const int64_t *topk_idx, const float *topk_weights,
+                  const int32_t *topk_slot, void *out, ep_stream_t stream_)
+{
+    if (dims == nullptr)
+        return EP_ERR_INVALID;
+    ep_dims d = *dims;
+    d.num_channels = 1;
+    int rc = check_dims(&d);
+    if (rc != EP_OK)
+        return rc;
+    if (num_slots < 1 || num_slots > kMaxLLSlots)
+        return EP_ERR_INVALID;
+    if (d.num_tokens > num_slots)
+        return EP_ERR_CAPACITY;
+    if (d.num_tokens > 0 && (packed_y == nullptr || topk_idx == nullptr ||
+                             topk_weights == nullptr || topk_slot == nullptr || out == nullptr))
+        return EP_ERR_INVALID;
+    if (!aligned(packed_y, 16) || !aligned(out, 16) || !aligned(topk_idx, 8) ||
+        !aligned(topk_weights, 4) || !aligned(topk_slot, 4))
+        return EP_ERR_ALIGN;
+    hipError_t e = launch_ll_combine(d, num_slots, packed_y, topk_idx, topk_weights, topk_slot,
+                                     out, static_cast<hipStream_t>(stream_));
+    return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
+int ep_handle_copy_layout(ep_handle *h, ep_layout_out *out, ep_stream_t stream)
+{
+    if (h == nullptr)
+        return EP_ERR_HANDLE;
+    if (out == nullptr)
+        return EP_ERR_INVALID;
+    try {
+        return copy_layout(h, out, static_cast<hipStream_t>(stream));
+    } catch (...) {
+        return EP_ERR_INVALID;
+    }
+}
+
+int ep_handle_num_recv(ep_handle *h, int64_t *num_recv)
+{
+    if (h == nullptr)
+        return EP_ERR_HANDLE;
+    if (num_recv == nullptr)
+        return EP_ERR_INVALID;
+    return read_num_recv(h, h->last_stream.load(), num_recv);
+}
+
+int ep_handle_dims(const ep_handle *h, ep_dims *dims)
+{
+    if (h == nullptr)
+        return EP_ERR_HANDLE;
+    if (dims == nullptr)
+        return EP_ERR_INVALID;
+    *dims = h->dims;
+    return EP_OK;
+}
+
+size_t ep_handle_nbytes(const ep_handle *h) { return h == nullptr ? 0 : h->arena.bytes; }
+
+void ep_handle_free(ep_handle *h)
+{
+    if (h == nullptr)
+        return;
+    int cur = 0;
+    const bool switch_dev = hipGetDevice(&cur) == hipSuccess && cur != h->device;
+    if (switch_dev)
+        hipSetDevice(h->device);
+    arena_put(h->device, h->arena, h->last_stream.load());
+    if (switch_dev)
+        hipSetDevice(cur);
+    delete h;
+}
+
+int ep_pool_trim(void)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    return trim_pool(pool_for(dev));
+}
+
+const char *ep_status_str(int status)
+{
+    switch (status) {
+    case EP_OK: return "ok";
+    case EP_ERR_INVALID: return "invalid argument";
+    case EP_ERR_ALIGN: return "alignment rule broken (16-byte rows and pointers)";
+    case EP_ERR_CAPACITY: return "output buffer has too few rows";
+    case EP_ERR_HANDLE: return "handle missing or does not match the dims";
+    case EP_ERR_HIP: return "HIP runtime error";
+    case EP_ERR_NOMEM: return "out of memory";
+    default: return "unknown status";
+    }
+}
+
+const char *ep_last_hip_error(void) { return g_last_hip.c_str(); }
+
+int ep_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

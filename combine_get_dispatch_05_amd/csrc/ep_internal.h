@@ -1,0 +1,101 @@
+// ep_internal.h -- declarations shared by the gfx950 kernels and the host
+// runtime of libep.so.  Not part of the public ABI (that is include/ep.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ep.h"
+
+namespace ep {
+
+// 16-byte vector: the unit of every token-row load and store (rows are whole
+// int4 vectors, as the runtime's alignment rule requires).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kMaxRanks = 512;     // NW <= 8 64-bit rank-mask words
+constexpr int kMaxTopk = 64;
+constexpr int kMaxExperts = 8192;  // per-block expert histogram lives in LDS
+constexpr int kMaxChannels = 4096;
+constexpr int kMaxLLSlots = 4096;  // LL slot list lives in LDS
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+constexpr int kMaxHidden = 1 << 20;
+
+// Device pointers of one layout (all inside a handle's arena).
+struct LayoutBufs {
+    int32_t *num_tokens_per_rank;        // [R]
+    int32_t *num_tokens_per_expert;      // [E]
+    uint8_t *is_token_in_rank;           // [T][R]
+    int32_t *rank_prefix_matrix;         // [R]
+    int32_t *channel_prefix_matrix;      // [R][C]
+    int32_t *recv_channel_prefix_matrix; // [R][C]
+    int32_t *send_head;                  // [T][R]
+    int32_t *recv_src_idx;               // [T*Kmax]
+    int32_t *dst_row;                    // [T][Kmax] packed rows of t, ascending rank, -1 padded
+    int32_t *dst_rank;                   // [T][Kmax] their ranks
+    uint64_t *wave_mask;                 // [nW][R] ballot of "token hits r" per 64-token wave
+    int32_t *wave_count;                 // [R][nW] per-wave counts, then exclusive bases
+    int32_t *blk_ecount;                 // [nB][E] per-block expert counts
+    int64_t *num_recv;                   // [1] N
+};
+
+struct LayoutShape {
+    int T, K, E, R, C, epr, kmax, nW, nB;
+};
+
+LayoutShape layout_shape(const ep_dims &d);
+// Byte offsets of every LayoutBufs field inside one arena; returns the total.
+size_t layout_arena_bytes(const LayoutShape &s, size_t off[14]);
+LayoutBufs layout_bufs_at(void *base, const size_t off[14]);
+
+hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const LayoutBufs &b,
+                         hipStream_t stream);
+
+hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, const LayoutBufs &b,
+                           const int64_t *topk_idx, const float *topk_weights, void *recv_x,
+                           int64_t *recv_topk_idx, float *recv_topk_weights, hipStream_t stream);
+
+hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const LayoutBufs &b,
+                          const float *recv_topk_weights, void *out,
+                          float *combined_topk_weights, hipStream_t stream);
+
+hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
+                              const int64_t *topk_idx, void *packed_x, int32_t *packed_count,
+                              int32_t *src_info, int32_t *topk_slot, hipStream_t stream);
+
+hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed_y,
+                             const int64_t *topk_idx, const float *topk_weights,
+                             const int32_t *topk_slot, void *out, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 round to nearest, ties to even: add just under half of the
+// dropped 16-bit fraction, plus one when the kept lsb is odd, then truncate.
+// A mantissa carry correctly bumps the exponent.  NaN is kept quiet.
+__device__ __forceinline__ uint32_t bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint64_t lanemask_lt()
+{
+    const unsigned lane = __lane_id();
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+}  // namespace ep

@@ -12,4 +12,5 @@ from .inputs import (  # noqa: F401
     config_inputs,
     generate,
     random_case,
+    random_rows,
 )

@@ -141,6 +141,13 @@ def generate(T: int, H: int, E: int, K: int, R: int, C: int, *, routing: str = "
                   slots=slots, name=name, extra=extra)
 
 
+def random_rows(n: int, h: int, seed: int, tag: int = 7) -> np.ndarray:
+    """Standard-normal bf16 rows (uint16 bit patterns, truncated like ``x``),
+    used as stand-in expert outputs for combine."""
+    f = _rng(seed, 1000 + tag).standard_normal((n, h), dtype=np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 def config_inputs(cfg_id: int, seed: int = 0, with_x: bool = True) -> Inputs:
     c = dict(CONFIGS[cfg_id])
     name = c.pop("name")

@@ -1,0 +1,251 @@
+/*
+ * ep.h -- C ABI of the MI355X (gfx950) expert-parallel layout / dispatch /
+ * combine library (libep.so).
+ *
+ * The operations follow these pages:
+ *   [P1] "DeepEP Buffer Class API for Expert Parallel Communication:
+ *        Architecture and Usage": "Configuration and Layout Helpers"
+ *        (get_dispatch_layout), "Dispatch Operation", "Combine Operation",
+ *        "IB-GDA Kernels" (low_latency_dispatch / low_latency_combine),
+ *        "Explicit Resource Cleanup" (destroy) and the FAQ on the handle.
+ *   [P3] DeepEP-Lib "Core Implementation" (C++ runtime): "Memory Alignment
+ *        and Validation" (int4-multiple rows, buffer alignment).
+ *   [P4] "How DeepEP Optimizes Handle Reuse for Repeated Dispatches": "What
+ *        the Handle Contains", "Fast Path Dispatch with Handle Reuse",
+ *        "Performance Contract and Constraints".
+ *
+ * The R destination ranks are logical partitions of this GPU's memory: a
+ * "segment" is a contiguous range of rows of one caller buffer.  Nothing here
+ * talks to another GPU.
+ *
+ * Conventions for every entry point
+ *   - Memory: every array argument is a DEVICE pointer owned by the caller,
+ *     except the ones documented as host pointers.  The library never frees
+ *     caller memory.  The handle is the only library-owned memory.
+ *   - Streams: `stream` is a hipStream_t (NULL = the legacy default stream).
+ *     All device work is enqueued on it, in order; no call synchronizes the
+ *     host unless its documentation says so.
+ *   - Layouts are dense row-major.  bf16 tensors are 16-bit words.  topk_idx
+ *     is int64 with -1 for a masked slot; weights are fp32.
+ *   - Expert e belongs to rank e / (E/R) as local expert e % (E/R).
+ *   - Alignment ([P3]): token-row pointers (x, recv_x, y, out, packed_x,
+ *     packed_y) must be 16-byte aligned and hidden*2 must be a multiple of 16
+ *     (rows are whole int4 vectors); int64 arrays 8-byte, others 4-byte
+ *     aligned.  Violations return EP_ERR_ALIGN before any work is enqueued.
+ *   - Expert ids outside [-1, E) are invalid input.  The kernels ignore such
+ *     slots (treat them as masked) so that no access leaves its buffer.
+ *   - Errors: every int-returning call returns an ep_status.  On any error no
+ *     work has been enqueued and no output pointer argument was written,
+ *     except as noted.  Host-side errors never throw across the ABI.
+ *   - Concurrency: calls may run on different streams concurrently as long
+ *     as they do not write the same caller memory.  One handle may be read by
+ *     several calls at once; it must not be freed while they are in flight
+ *     on other streams than its last one (ep_handle_free orders the free
+ *     after the last call that used the handle).
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *ep_stream_t; /* a hipStream_t */
+
+typedef enum ep_status {
+    EP_OK = 0,
+    EP_ERR_INVALID = 1,  /* bad dimension, NULL where required, forbidden argument mix */
+    EP_ERR_ALIGN = 2,    /* pointer or row-size alignment rule broken */
+    EP_ERR_CAPACITY = 3, /* caller buffer has fewer rows than the result needs */
+    EP_ERR_HANDLE = 4,   /* handle does not match the dims, or NULL handle */
+    EP_ERR_HIP = 5,      /* a HIP runtime call failed (see ep_last_hip_error) */
+    EP_ERR_NOMEM = 6     /* device or host allocation failed */
+} ep_status;
+
+/* Problem sizes.  Limits: 0 <= num_tokens <= 2^24; hidden > 0, hidden % 8 == 0,
+ * hidden <= 2^20; 1 <= num_topk <= 64; 1 <= num_ranks <= 512;
+ * num_experts % num_ranks == 0, num_experts <= 8192; num_channels >= 1,
+ * num_channels <= 2^20. */
+typedef struct ep_dims {
+    int32_t num_tokens;   /* T */
+    int32_t hidden;       /* H, bf16 elements per token row */
+    int32_t num_topk;     /* K */
+    int32_t num_experts;  /* E */
+    int32_t num_ranks;    /* R */
+    int32_t num_channels; /* C: channels are ceil(T/C)-token contiguous ranges */
+} ep_dims;
+
+/* Opaque, library-owned dispatch layout ("handle" of [P4] "What the Handle
+ * Contains"): rank_prefix_matrix, channel_prefix_matrix,
+ * recv_channel_prefix_matrix, recv_src_idx, is_token_in_rank, send_head, the
+ * per-rank and per-expert counts, the dims, and per-token destination-row
+ * lists.  Immutable once created; freed by ep_handle_free. */
+typedef struct ep_handle ep_handle;
+
+/* Caller-owned device outputs of the layout.  Any field may be NULL (not
+ * wanted).  Shapes:
+ *   num_tokens_per_rank        int32 [R]    tokens that go to rank r
+ *   num_tokens_per_expert      int32 [E]    (token, slot) pairs naming e
+ *   is_token_in_rank           uint8 [T][R] 1 iff t goes to r
+ *   rank_prefix_matrix         int32 [R]    inclusive prefix of num_tokens_per_rank;
+ *                                           segment r starts at row [r-1] (0 for r = 0),
+ *                                           N = [R-1] rows in total
+ *   channel_prefix_matrix      int32 [R][C] tokens of rank r before the end of channel c
+ *   recv_channel_prefix_matrix int32 [R][C] tokens of rank r before the start of channel c
+ *   send_head                  int32 [T][R] row of t inside segment r, -1 if none
+ *   recv_src_idx               int32 [recv_src_cap] source token of packed row i, i < N
+ */
+typedef struct ep_layout_out {
+    int32_t *num_tokens_per_rank;
+    int32_t *num_tokens_per_expert;
+    uint8_t *is_token_in_rank;
+    int32_t *rank_prefix_matrix;
+    int32_t *channel_prefix_matrix;
+    int32_t *recv_channel_prefix_matrix;
+    int32_t *send_head;
+    int32_t *recv_src_idx;
+    int64_t recv_src_cap; /* rows available in recv_src_idx */
+} ep_layout_out;
+
+/* Largest possible row count N of a dispatch: T * min(K, R). */
+int64_t ep_max_recv_rows(const ep_dims *dims);
+
+/*
+ * [P1] "Configuration and Layout Helpers": compute the token-to-rank layout
+ * of topk_idx [T][K] on the GPU, before any token data moves.
+ *
+ * out (nullable): fields that are non-NULL receive copies of the layout.  If
+ *   out->recv_src_idx is non-NULL and recv_src_cap < ep_max_recv_rows(), the
+ *   call synchronizes the stream to learn N and returns EP_ERR_CAPACITY if
+ *   N > recv_src_cap (then no output in `out` is written; the handle, if
+ *   asked for, is still created and returned).
+ * handle_out (nullable): receives a new handle holding the layout.  Such a
+ *   handle may be given to one ep_dispatch together with the same topk_idx
+ *   (the "pre-computed layout" of [P1] "Dispatch Operation").
+ * No host synchronization unless noted above.
+ */
+int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, ep_layout_out *out,
+                           ep_handle **handle_out, ep_stream_t stream);
+
+/*
+ * [P1] "Dispatch Operation" and [P4] "Fast Path Dispatch with Handle Reuse":
+ * pack token rows x [T][H] (bf16) into R contiguous per-rank segments of
+ * recv_x [recv_cap][H] in token order: row S[r] + send_head[t][r] receives
+ * x[t] for every rank r that t goes to.
+ *
+ *   *handle == NULL       fresh dispatch: topk_idx is required; the layout is
+ *                         computed and a new handle is stored in *handle.
+ *   handle from ep_get_dispatch_layout and not yet used by a dispatch:
+ *                         the layout is reused; topk_idx / topk_weights may
+ *                         be given and must be the table the layout came from.
+ *   handle returned by an earlier dispatch (cached fast path):
+ *                         topk_idx and topk_weights must be NULL
+ *                         (EP_ERR_INVALID otherwise); only rows are packed.
+ *
+ * recv_topk_idx [recv_cap][K] int64 (nullable, needs topk_idx): slot k of
+ *   packed row (t, r) holds e - r*(E/R) when slot k of t is valid and its
+ *   expert e lives on r, else -1.
+ * recv_topk_weights [recv_cap][K] fp32 (nullable, needs topk_weights): the
+ *   slot's weight in the same case, else 0.
+ * recv_x (nullable): NULL skips the row copy (layout / size query only).
+ * recv_cap: rows available in recv_x / recv_topk_*.  If it is below N the
+ *   call returns EP_ERR_CAPACITY (a fresh handle is still returned in
+ *   *handle).  When recv_cap >= ep_max_recv_rows() no host synchronization
+ *   is needed to check it.
+ * num_recv (HOST pointer, nullable): receives N; asking for it synchronizes
+ *   the stream once per handle (later calls use the cached value).
+ * dims must equal the handle's dims except hidden, which may differ.
+ */
+int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
+                const float *topk_weights, ep_handle **handle, void *recv_x,
+                int64_t *recv_topk_idx, float *recv_topk_weights, int64_t recv_cap,
+                int64_t *num_recv, ep_stream_t stream);
+
+/*
+ * [P1] "Combine Operation": addition-based reduction of the packed rows
+ * y [y_rows][hidden] (bf16, same segment layout as the dispatch that made
+ * handle) back to token order:
+ *   out[t] = bf16_rne( sum over ranks r ascending that t went to of
+ *                      fp32(y[S[r] + send_head[t][r]]) ),  fp32 accumulation
+ *   starting at +0; a token that went nowhere gets +0.
+ * recv_topk_weights [y_rows][K] fp32 (nullable) and combined_topk_weights
+ * [T][K] fp32 (nullable, needs the former): the same ascending-rank fp32 sum
+ * of the per-row weights (the reduced weights combine returns).
+ * y_rows below N returns EP_ERR_CAPACITY (checked without synchronizing
+ * when y_rows >= ep_max_recv_rows(), else N is read once per handle).
+ */
+int ep_combine(ep_handle *handle, int32_t hidden, const void *y, int64_t y_rows,
+               const float *recv_topk_weights, void *out, float *combined_topk_weights,
+               ep_stream_t stream);
+
+/*
+ * [P1] "IB-GDA Kernels", low_latency_dispatch: stream every valid (token,
+ * slot) pair straight into its expert's receive area.  With epr = E/R:
+ *   packed_x  [epr][R][num_slots][H] bf16: cell (le, r, s) gets x[t] for the
+ *             pair (t, k) naming expert r*epr + le whose slot is s
+ *   packed_count [epr][R] int32: pairs routed to each expert
+ *   src_info  [epr][R][num_slots] int32: source token of each used cell, -1
+ *             for unused cells
+ *   topk_slot [T][K] int32: slot s of pair (t, k), -1 when masked or dropped
+ * Slots follow (token, slot) order.  Requires T <= num_slots
+ * (EP_ERR_CAPACITY); pairs past num_slots (possible only when a token names
+ * one expert twice) are dropped and still counted.  Unused packed_x cells
+ * are not written.  packed_x may be NULL (metadata only).  No host sync.
+ */
+int ep_ll_dispatch(const ep_dims *dims, int32_t num_slots, const void *x,
+                   const int64_t *topk_idx, void *packed_x, int32_t *packed_count,
+                   int32_t *src_info, int32_t *topk_slot, ep_stream_t stream);
+
+/*
+ * [P1] "IB-GDA Kernels", low_latency_combine: for every token,
+ *   out[t] = bf16_rne(acc),  acc = fma(topk_weights[t][k], fp32(cell(t, k)), acc)
+ * over k ascending, valid non-dropped slots only, from acc = +0, where cell
+ * (t, k) is the packed_y row [le][r][topk_slot[t][k]] of the slot's expert.
+ * packed_y has packed_x's layout; topk_slot comes from ep_ll_dispatch.
+ * No host sync.
+ */
+int ep_ll_combine(const ep_dims *dims, int32_t num_slots, const void *packed_y,
+                  const int64_t *topk_idx, const float *topk_weights,
+                  const int32_t *topk_slot, void *out, ep_stream_t stream);
+
+/* Copy the handle's layout into caller buffers (fields may be NULL); same
+ * shapes and capacity rule as ep_get_dispatch_layout. */
+int ep_handle_copy_layout(ep_handle *handle, ep_layout_out *out, ep_stream_t stream);
+
+/* N of the handle.  Synchronizes the handle's last stream the first time. */
+int ep_handle_num_recv(ep_handle *handle, int64_t *num_recv);
+
+/* The handle's dims (host copy). */
+int ep_handle_dims(const ep_handle *handle, ep_dims *dims);
+
+/* Device bytes the handle holds (the print_memory_usage of the pages' V2.5
+ * buffer base class). */
+size_t ep_handle_nbytes(const ep_handle *handle);
+
+/* [P1] "Explicit Resource Cleanup": release a handle.  NULL is a no-op.  The
+ * memory returns to the library's per-device pool, ordered after all work
+ * enqueued so far on the handle's last stream; it is never reused before
+ * that work completes. */
+void ep_handle_free(ep_handle *handle);
+
+/* Release every pooled device allocation of the calling thread's current
+ * device (waits for their pending work).  Returns an ep_status. */
+int ep_pool_trim(void);
+
+/* Static text of a status code. */
+const char *ep_status_str(int status);
+
+/* Text of the last HIP error seen by this thread (empty if none). */
+const char *ep_last_hip_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int ep_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -1,0 +1,294 @@
+"""HIP path against the CPU oracle, element by element, through the C ABI.
+
+Layout, dispatch (fresh and handle-reuse) and the low-latency metadata must be
+bit-exact; combine within 1 bf16 ulp (and, since both sides run the same
+ascending-rank fp32 sums, exactly equal in practice).  Runs on all five
+workloads at full size, and on randomized ragged cases that cross every
+tile/chunk boundary of the kernels (T not a multiple of 64/256, R above 64,
+row lengths that are not a multiple of the block's vector count, repeated
+experts inside a token, masked slots, empty inputs).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gen import config_inputs, random_case, random_rows
+from gpu_util import assert_bf16_close, dev, dev_bf16, host, host_bits
+
+pytestmark = pytest.mark.gpu
+
+import combine_get_dispatch_05_amd as epm  # noqa: E402  (fails loudly when libep.so is missing)
+from combine_get_dispatch_05_amd import abi  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu-test] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+LAYOUT_FIELDS = ["num_tokens_per_rank", "num_tokens_per_expert", "rank_prefix_matrix",
+                 "channel_prefix_matrix", "recv_channel_prefix_matrix", "send_head",
+                 "recv_src_idx"]
+
+
+def compare_layout(lay, ora):
+    for name in LAYOUT_FIELDS:
+        np.testing.assert_array_equal(host(getattr(lay, name)), getattr(ora, name), err_msg=name)
+    np.testing.assert_array_equal(host(lay.is_token_in_rank).astype(np.uint8),
+                                  ora.is_token_in_rank, err_msg="is_token_in_rank")
+
+
+def f32_bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def run_normal_path(inp, seed=0):
+    """Fresh dispatch, handle-reuse dispatch and combine against the oracle."""
+    E, R, C = inp.E, inp.R, inp.C
+    ora = oracle.layout(inp.topk_idx, E, R, C)
+    buf = epm.Buffer(R, E, C)
+    x = dev_bf16(inp.x)
+    topk = dev(inp.topk_idx)
+    w = dev(inp.topk_weights)
+
+    # layout alone
+    ntpr, ntpe, itr, _ = buf.get_dispatch_layout(topk)
+    np.testing.assert_array_equal(host(ntpr), ora.num_tokens_per_rank)
+    np.testing.assert_array_equal(host(ntpe), ora.num_tokens_per_expert)
+    np.testing.assert_array_equal(host(itr).astype(np.uint8), ora.is_token_in_rank)
+
+    # fresh dispatch
+    recv_x, rti, rtw, counts, h, ev = buf.dispatch(x, topk, w)
+    assert ev is None
+    assert h.num_recv == ora.num_recv
+    o_rx, o_rti, o_rtw = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, E, R, ora)
+    np.testing.assert_array_equal(host_bits(recv_x), o_rx)
+    np.testing.assert_array_equal(host(rti), o_rti)
+    np.testing.assert_array_equal(f32_bits(host(rtw)), f32_bits(o_rtw))
+    np.testing.assert_array_equal(host(counts).reshape(-1), ora.num_tokens_per_expert)
+    compare_layout(h.layout(), ora)
+
+    # handle-reuse dispatch of new rows
+    x2 = random_rows(inp.T, inp.H, seed, tag=11)
+    recv_x2, rti2, rtw2, counts2, h2, _ = buf.dispatch(dev_bf16(x2), handle=h)
+    assert h2 is h and rti2 is None and rtw2 is None and counts2 is None
+    o_rx2, _, _ = oracle.dispatch(x2, None, None, E, R, ora, with_topk=False)
+    np.testing.assert_array_equal(host_bits(recv_x2), o_rx2)
+
+    # combine random expert outputs with the dispatched weights
+    y = random_rows(ora.num_recv, inp.H, seed, tag=12)
+    out, cw, _ = buf.combine(dev_bf16(y), h, rtw)
+    o_out, o_cw = oracle.combine(y, ora, o_rtw)
+    assert_bf16_close(host_bits(out), o_out, what="combine")
+    np.testing.assert_array_equal(f32_bits(host(cw)), f32_bits(o_cw))
+
+    # identity combine of the dispatched rows
+    out_id, _, _ = buf.combine(recv_x, h)
+    o_id, _ = oracle.combine(o_rx, ora)
+    assert_bf16_close(host_bits(out_id), o_id, what="identity combine")
+    h.free()
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 4])
+def test_normal_path_configs(cfg):
+    run_normal_path(config_inputs(cfg))
+
+
+def test_layout_config3():
+    inp = config_inputs(3, with_x=False)
+    ora = oracle.layout(inp.topk_idx, inp.E, inp.R, inp.C)
+    buf = epm.Buffer(inp.R, inp.E, inp.C)
+    _, _, _, h = buf.get_dispatch_layout(dev(inp.topk_idx), keep_handle=True)
+    compare_layout(h.layout(), ora)
+
+
+RANDOM_CASES = [
+    # T, H, E, K, R, C, mask, dup
+    (0, 64, 8, 2, 4, 3, 0.0, 0.0),
+    (1, 8, 4, 1, 1, 1, 0.0, 0.0),
+    (63, 24, 12, 3, 3, 5, 0.2, 0.3),
+    (65, 40, 64, 9, 64, 2, 0.1, 0.2),
+    (200, 2056, 130, 5, 65, 200, 0.1, 0.1),
+    (257, 16384, 512, 8, 512, 7, 0.05, 0.0),
+    (1000, 7168, 288, 8, 144, 20, 0.05, 0.1),
+    (4097, 136, 256, 16, 32, 13, 0.3, 0.2),
+    (300, 512, 64, 64, 8, 3, 0.1, 0.1),
+    (129, 1024, 448, 8, 448, 4096, 0.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: "T%d_H%d_E%d_K%d_R%d_C%d" % c[:6])
+def test_normal_path_random(case):
+    T, H, E, K, R, C, mask, dup = case
+    run_normal_path(random_case(7 + T, T, H, E, K, R, C, mask=mask, dup=dup), seed=T)
+
+
+def run_ll(inp, seed=0):
+    E, R, S = inp.E, inp.R, inp.slots
+    T, K = inp.topk_idx.shape
+    o_buf, o_cnt, o_src, o_slot = oracle.ll_dispatch(inp.x, inp.topk_idx, E, R, S)
+    buf = epm.Buffer(R, E)
+    x = dev_bf16(inp.x)
+    topk = dev(inp.topk_idx)
+    packed, count, hdl, ev, hook = buf.low_latency_dispatch(x, topk, S, E)
+    assert ev is None and hook is None
+    np.testing.assert_array_equal(host(count), o_cnt)
+    np.testing.assert_array_equal(host(hdl.src_info), o_src)
+    np.testing.assert_array_equal(host(hdl.topk_slot), o_slot)
+    used = np.minimum(o_cnt, S)
+    pk = host_bits(packed)
+    epr = E // R
+    for le in range(epr):
+        for r in range(R):
+            u = int(used[le, r])
+            np.testing.assert_array_equal(pk[le, r, :u], o_buf[le, r, :u])
+    # weighted combine of identity experts and of random expert outputs
+    w = dev(inp.topk_weights)
+    out, _, _ = buf.low_latency_combine(packed, topk, w, hdl)
+    assert_bf16_close(host_bits(out), oracle.ll_combine(o_buf, inp.topk_idx, inp.topk_weights, E, R),
+                      what="ll combine (identity)")
+    y = random_rows(epr * R * S, inp.H, seed, tag=13).reshape(epr, R, S, inp.H)
+    out2, _, _ = buf.low_latency_combine(dev_bf16(y), topk, w, hdl)
+    assert_bf16_close(host_bits(out2), oracle.ll_combine(y, inp.topk_idx, inp.topk_weights, E, R),
+                      what="ll combine (random)")
+
+
+def test_ll_config3():
+    run_ll(config_inputs(3))
+
+
+LL_CASES = [
+    # T, H, E, K, R, slots, mask, dup
+    (0, 64, 8, 2, 2, 4, 0.0, 0.0),
+    (1, 8, 4, 1, 2, 1, 0.0, 0.0),
+    (37, 136, 16, 4, 4, 40, 0.2, 0.5),
+    (200, 2048, 64, 6, 8, 256, 0.1, 0.0),
+    (64, 7168, 288, 8, 144, 64, 0.05, 0.0),
+    (300, 16384, 32, 8, 32, 300, 0.0, 0.3),
+]
+
+
+@pytest.mark.parametrize("case", LL_CASES, ids=lambda c: "T%d_H%d_E%d_K%d_R%d_S%d" % c[:6])
+def test_ll_random(case):
+    T, H, E, K, R, S, mask, dup = case
+    run_ll(random_case(3 + T, T, H, E, K, R, 1, mask=mask, dup=dup, slots=S), seed=T)
+
+
+# ----------------------------------------------------------- boundary / errors
+
+
+def test_errors_and_reuse_contract():
+    inp = config_inputs(0)
+    buf = epm.Buffer(inp.R, inp.E, inp.C)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+    _, _, _, _, h, _ = buf.dispatch(x, topk, w)
+    # a handle from a dispatch refuses new routing
+    with pytest.raises(abi.EpError) as ei:
+        buf.dispatch(x, topk, w, handle=h)
+    assert ei.value.code == abi.EP_ERR_INVALID
+    # a handle for other dims is refused
+    d = abi.dims(inp.T, inp.H, inp.K, inp.E, inp.R, inp.C + 1)
+    raw = ctypes.c_void_p(h.raw.value)
+    rx = torch.empty((4096, inp.H), dtype=torch.bfloat16, device="cuda")
+    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, ctypes.byref(raw),
+                               abi.ptr(rx), None, None, 4096, None, abi.current_stream())
+    assert rc == abi.EP_ERR_HANDLE
+    # too few rows: refused, nothing written
+    n = h.num_recv
+    small = torch.full((n - 1, inp.H), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    d = abi.dims(inp.T, inp.H, inp.K, inp.E, inp.R, inp.C)
+    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, ctypes.byref(raw),
+                               abi.ptr(small), None, None, n - 1, None, abi.current_stream())
+    assert rc == abi.EP_ERR_CAPACITY
+    assert bool((small.view(torch.int16) == 7).all())
+    out = torch.empty((inp.T, inp.H), dtype=torch.bfloat16, device="cuda")
+    rc = abi.lib().ep_combine(h.raw, inp.H, abi.ptr(small), n - 1, None, abi.ptr(out), None,
+                              abi.current_stream())
+    assert rc == abi.EP_ERR_CAPACITY
+    # misaligned row pointer
+    off = torch.empty((n + 1, inp.H), dtype=torch.bfloat16, device="cuda")
+    bad = ctypes.c_void_p(off.data_ptr() + 2)
+    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, ctypes.byref(raw), bad,
+                               None, None, n, None, abi.current_stream())
+    assert rc == abi.EP_ERR_ALIGN
+    h.free()
+
+
+def test_layout_handle_accepts_its_topk_once():
+    inp = config_inputs(0)
+    buf = epm.Buffer(inp.R, inp.E, inp.C)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+    _, _, _, h = buf.get_dispatch_layout(topk, keep_handle=True)
+    rx, rti, rtw, _, h2, _ = buf.dispatch(x, topk, w, handle=h)
+    ora = oracle.layout(inp.topk_idx, inp.E, inp.R, inp.C)
+    o_rx, o_rti, o_rtw = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, inp.E, inp.R, ora)
+    np.testing.assert_array_equal(host_bits(rx), o_rx)
+    np.testing.assert_array_equal(host(rti), o_rti)
+    with pytest.raises(abi.EpError):
+        buf.dispatch(x, topk, w, handle=h)
+
+
+def test_layout_capacity_out():
+    inp = config_inputs(0)
+    d = abi.dims(inp.T, 8, inp.K, inp.E, inp.R, inp.C)
+    topk = dev(inp.topk_idx)
+    ora = oracle.layout(inp.topk_idx, inp.E, inp.R, inp.C)
+    n = ora.num_recv
+    src = torch.full((n - 1,), -5, dtype=torch.int32, device="cuda")
+    o = abi.LayoutOut(None, None, None, None, None, None, None, src.data_ptr(), n - 1)
+    rc = abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk), ctypes.byref(o), None,
+                                          abi.current_stream())
+    assert rc == abi.EP_ERR_CAPACITY
+    assert bool((src == -5).all())
+    src = torch.full((n,), -5, dtype=torch.int32, device="cuda")
+    o = abi.LayoutOut(None, None, None, None, None, None, None, src.data_ptr(), n)
+    rc = abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk), ctypes.byref(o), None,
+                                          abi.current_stream())
+    assert rc == abi.EP_OK
+    np.testing.assert_array_equal(host(src), ora.recv_src_idx)
+
+
+def test_guard_bands_and_determinism():
+    """Rows outside [0, N) of the packed buffer, and the bytes around the
+    combine output, stay untouched; two runs give identical bytes."""
+    inp = random_case(21, 777, 264, 96, 6, 24, 5, mask=0.1, dup=0.1)
+    E, R, C, H = inp.E, inp.R, inp.C, inp.H
+    buf = epm.Buffer(R, E, C)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+    d = abi.dims(inp.T, H, inp.K, E, R, C)
+    cap = int(abi.lib().ep_max_recv_rows(ctypes.byref(d)))
+    G = 3
+    results = []
+    for _ in range(2):
+        big = torch.full((cap + 2 * G, H), 0x7FC1, dtype=torch.int16, device="cuda")
+        recv = big[G:G + cap].view(torch.bfloat16)
+        raw = ctypes.c_void_p()
+        n = ctypes.c_int64()
+        rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), abi.ptr(topk), abi.ptr(w),
+                                   ctypes.byref(raw), abi.ptr(recv), None, None, cap,
+                                   ctypes.byref(n), abi.current_stream())
+        assert rc == abi.EP_OK
+        N = int(n.value)
+        b = host(big)
+        assert np.all(b[:G] == 0x7FC1) and np.all(b[G + N:] == 0x7FC1)
+        obig = torch.full((inp.T + 2 * G, H), 0x7FC1, dtype=torch.int16, device="cuda")
+        out = obig[G:G + inp.T].view(torch.bfloat16)
+        rc = abi.lib().ep_combine(raw, H, abi.ptr(recv), cap, None, abi.ptr(out), None,
+                                  abi.current_stream())
+        assert rc == abi.EP_OK
+        ob = host(obig)
+        assert np.all(ob[:G] == 0x7FC1) and np.all(ob[G + inp.T:] == 0x7FC1)
+        results.append((b[G:G + N].copy(), ob[G:G + inp.T].copy()))
+        abi.lib().ep_handle_free(raw)
+    assert np.array_equal(results[0][0], results[1][0])
+    assert np.array_equal(results[0][1], results[1][1])
