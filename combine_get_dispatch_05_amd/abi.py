@@ -27,7 +27,7 @@ EXPORTS = (
     "ep_max_recv_rows", "ep_get_dispatch_layout", "ep_dispatch", "ep_combine",
     "ep_ll_dispatch", "ep_ll_combine", "ep_handle_copy_layout", "ep_handle_num_recv",
     "ep_handle_dims", "ep_handle_nbytes", "ep_handle_free", "ep_pool_trim", "ep_status_str",
-    "ep_last_hip_error", "ep_version",
+    "ep_last_hip_error", "ep_version", "ep_set_tuning", "ep_tuning_list",
 )
 
 
@@ -60,7 +60,7 @@ class EpError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m combine_get_dispatch_05_amd.build` (or __graft_entry__.build())")
+                          "`python combine_get_dispatch_05_amd/build.py` (or __graft_entry__.build())")
     # torch ships its own HIP runtime.  Loading torch first makes libep.so
     # bind to that same runtime instance (its DT_NEEDED soname then matches
     # the already loaded copy), so the streams and device pointers torch hands
@@ -87,6 +87,12 @@ def _load():
         "ep_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "ep_last_hip_error": (ctypes.c_char_p, []),
         "ep_version": (ctypes.c_int, []),
+        "ep_set_tuning": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int]),
+        "ep_tuning_list": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_int),
+                                          ctypes.POINTER(ctypes.c_int),
+                                          ctypes.POINTER(ctypes.c_int)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -121,6 +127,23 @@ def ptr(t):
 def current_stream():
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def tunings(op: str) -> list:
+    """All compiled-in launch shapes of ``op`` ("dispatch" or "combine")."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    n = _lib.ep_tuning_list(op.encode(), -1, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    out = []
+    for i in range(max(n, 0)):
+        _lib.ep_tuning_list(op.encode(), i, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+        out.append((a.value, b.value, c.value))
+    return out
+
+
+def set_tuning(op: str, *shape: int) -> None:
+    """Override the launch shape of ``op`` (no arguments: back to default)."""
+    vals = list(shape) + [-1] * (3 - len(shape)) if shape else [-1, -1, -1]
+    check(_lib.ep_set_tuning(op.encode(), *vals), "ep_set_tuning")
 
 
 def version() -> tuple:

@@ -1,6 +1,8 @@
 """Build libep.so (the gfx950 HIP kernels and their C ABI) in-tree with hipcc.
 
-    python -m combine_get_dispatch_05_amd.build
+    python combine_get_dispatch_05_amd/build.py
+
+(run it as a script: importing the package loads libep.so, which this builds)
 
 Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
 parallel), then all objects are linked into ``combine_get_dispatch_05_amd/libep.so``.

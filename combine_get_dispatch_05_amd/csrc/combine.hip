@@ -4,15 +4,21 @@
 // "Combine Operation": the rows a token sent out come back and are reduced by
 // addition into that token's position, using the dispatch handle to find
 // them.  Here the rows of token t sit at S[r] + send_head[t][r] in one buffer;
-// the workgroup for t reads them in ascending rank order (the layout's
-// per-token row list is already in that order), adds them in fp32 registers
-// starting from +0, and writes one bf16 row rounded to nearest even.  The
-// optional weight reduction sums the per-row top-k weights the same way.
+// a group of G lanes (whole wavefronts) reads them in ascending rank order
+// (the layout's per-token row list is already in that order), adds them in
+// fp32 registers starting from +0, and writes one bf16 row rounded to
+// nearest even.  The optional weight reduction sums the per-row top-k
+// weights the same way.
 //
 // The sum order is fixed (rank ascending, one add per row per element), so the
-// result does not depend on launch geometry.  Two rows' loads are issued
-// before either is added so that each lane keeps 2*VPT 16-byte loads in
-// flight.
+// result does not depend on the launch shape.  U rows' loads are issued
+// before any of them is added, so each lane keeps U*VPT 16-byte loads in
+// flight; the row list is loaded once per wavefront and broadcast with
+// readlane (no LDS, no barrier).
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
 
 #include "ep_internal.h"
 
@@ -23,7 +29,7 @@ namespace {
 constexpr int kCombineBlock = 256;
 
 template <int VPT>
-__device__ __forceinline__ void add_rows(float (&acc)[VPT][8], const u32x4 (&v)[VPT])
+__device__ __forceinline__ void add_row(float (&acc)[VPT][8], const u32x4 (&v)[VPT])
 {
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -35,91 +41,174 @@ __device__ __forceinline__ void add_rows(float (&acc)[VPT][8], const u32x4 (&v)[
     }
 }
 
-template <int VPT>
-__global__ __launch_bounds__(kCombineBlock) void combine_kernel(
-    const u32x4 *__restrict__ y, int V, int K, int kmax, const int32_t *__restrict__ dst_row,
-    const float *__restrict__ recv_topk_weights, u32x4 *__restrict__ out,
-    float *__restrict__ combined_topk_weights)
+template <bool NTL>
+__device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
 {
-    __shared__ int32_t s_row[kMaxTopk];
-    const int tid = threadIdx.x;
-    const int64_t t = blockIdx.x;
-    if (tid < kmax)
-        s_row[tid] = dst_row[t * kmax + tid];
-    __syncthreads();
-    int nhit = 0;
-    while (nhit < kmax && s_row[nhit] >= 0)
-        ++nhit;
+    if (NTL)
+        return __builtin_nontemporal_load(p);
+    return *p;
+}
 
-    for (int base = 0; base < V; base += kCombineBlock * VPT) {
-        float acc[VPT][8];
-#pragma unroll
-        for (int i = 0; i < VPT; ++i)
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                acc[i][q] = 0.0f;
+// One group of G lanes reduces one token at a time; with a persistent grid
+// (fewer groups than tokens) each group walks tokens with a grid stride.
+// NTL: rows are loaded nontemporally (each is read exactly once).
+template <int G, int VPT, int U, bool NTL>
+__global__ __launch_bounds__(kCombineBlock) void combine_kernel(
+    const u32x4 *__restrict__ y, int T, int V, int K, int kmax,
+    const int32_t *__restrict__ dst_row, const float *__restrict__ recv_topk_weights,
+    u32x4 *__restrict__ out, float *__restrict__ combined_topk_weights)
+{
+    constexpr int kGroups = kCombineBlock / G;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int gt = threadIdx.x % G;
+    const int first = __builtin_amdgcn_readfirstlane(blockIdx.x * kGroups + threadIdx.x / G);
+    const int stride = gridDim.x * kGroups;
+    for (int t = first; t < T; t += stride) {
+        const int rowv = lane < kmax ? dst_row[int64_t(t) * kmax + lane] : -1;
+        const int nhit = __popcll(wave_ballot(rowv >= 0));
 
-        int j = 0;
-        for (; j + 1 < nhit; j += 2) {
-            const u32x4 *ya = y + int64_t(s_row[j]) * V;
-            const u32x4 *yb = y + int64_t(s_row[j + 1]) * V;
-            u32x4 a[VPT], c[VPT];
+        for (int base = 0; base < V; base += G * VPT) {
+            float acc[VPT][8];
+#pragma unroll
+            for (int i = 0; i < VPT; ++i)
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[i][q] = 0.0f;
+
+            for (int j = 0; j < nhit; j += U) {
+                u32x4 v[U][VPT];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool live = j + u < nhit;
+                    const int row = __builtin_amdgcn_readlane(rowv, live ? j + u : 0);
+                    const u32x4 *yr = y + int64_t(row) * V;
+#pragma unroll
+                    for (int i = 0; i < VPT; ++i) {
+                        const int idx = base + i * G + gt;
+                        v[u][i] = (live && idx < V) ? load_row_vec<NTL>(yr + idx)
+                                                    : u32x4{0, 0, 0, 0};
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (j + u < nhit)
+                        add_row<VPT>(acc, v[u]);
+            }
+
+            u32x4 *o = out + int64_t(t) * V;
 #pragma unroll
             for (int i = 0; i < VPT; ++i) {
-                const int idx = base + i * kCombineBlock + tid;
-                a[i] = idx < V ? ya[idx] : u32x4{0, 0, 0, 0};
-                c[i] = idx < V ? yb[idx] : u32x4{0, 0, 0, 0};
-            }
-            add_rows<VPT>(acc, a);
-            add_rows<VPT>(acc, c);
-        }
-        if (j < nhit) {
-            const u32x4 *ya = y + int64_t(s_row[j]) * V;
-            u32x4 a[VPT];
+                const int idx = base + i * G + gt;
+                if (idx < V) {
+                    u32x4 r;
 #pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int idx = base + i * kCombineBlock + tid;
-                a[i] = idx < V ? ya[idx] : u32x4{0, 0, 0, 0};
+                    for (int q = 0; q < 4; ++q)
+                        r[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
+                    __builtin_nontemporal_store(r, o + idx);
+                }
             }
-            add_rows<VPT>(acc, a);
         }
 
-        u32x4 *o = out + t * V;
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = base + i * kCombineBlock + tid;
-            if (idx < V) {
-                u32x4 r;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    r[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
-                __builtin_nontemporal_store(r, o + idx);
+        if (combined_topk_weights != nullptr) {
+            for (int k = gt; k < K; k += G) {
+                float w = 0.0f;
+                for (int j = 0; j < nhit; ++j) {
+                    const int64_t row = __builtin_amdgcn_readlane(rowv, j);
+                    w += recv_topk_weights[row * K + k];
+                }
+                combined_topk_weights[int64_t(t) * K + k] = w;
             }
-        }
-    }
-
-    if (combined_topk_weights != nullptr) {
-        for (int k = tid; k < K; k += kCombineBlock) {
-            float w = 0.0f;
-            for (int jj = 0; jj < nhit; ++jj)
-                w += recv_topk_weights[int64_t(s_row[jj]) * K + k];
-            combined_topk_weights[t * K + k] = w;
         }
     }
 }
 
-template <int VPT>
-hipError_t launch_vpt(const LayoutShape &s, int V, const void *y, const LayoutBufs &b,
-                      const float *recv_topk_weights, void *out, float *combined_topk_weights,
-                      hipStream_t stream)
+typedef void (*CombineFn)(const u32x4 *, int, int, int, int, const int32_t *, const float *,
+                          u32x4 *, float *);
+
+// A launch shape: G lanes per token, VPT vectors per lane, U rows in flight,
+// NTL nontemporal row loads, and P = persistent block count (0: one group per
+// token).  The tuning knob addresses shapes as (G, VPT, U*100 + NTL*10 + P/256)
+// so that one int carries the last three.
+struct CombineCfg {
+    int G, VPT, U, NTL, P;
+    CombineFn fn;
+};
+
+#define EP_COMBINE_CFG(G, VPT, U, NTL, P) {G, VPT, U, NTL, P, combine_kernel<G, VPT, U, NTL>}
+
+const CombineCfg kCombineCfgs[] = {
+    EP_COMBINE_CFG(256, 1, 2, 1, 0),    EP_COMBINE_CFG(256, 2, 2, 1, 0),
+    EP_COMBINE_CFG(256, 4, 2, 1, 0),    EP_COMBINE_CFG(256, 4, 4, 1, 0),
+    EP_COMBINE_CFG(256, 4, 2, 0, 0),    EP_COMBINE_CFG(128, 7, 1, 1, 0),
+    EP_COMBINE_CFG(128, 7, 2, 1, 0),    EP_COMBINE_CFG(128, 7, 2, 0, 0),
+    EP_COMBINE_CFG(128, 7, 4, 1, 0),    EP_COMBINE_CFG(128, 7, 2, 1, 1024),
+    EP_COMBINE_CFG(128, 8, 2, 1, 0),    EP_COMBINE_CFG(64, 14, 1, 1, 0),
+    EP_COMBINE_CFG(64, 14, 2, 1, 0),    EP_COMBINE_CFG(64, 7, 2, 1, 0),
+};
+
+int combine_code(const CombineCfg &c) { return c.U * 100 + c.NTL * 10 + c.P / 256; }
+
+std::atomic<int> g_over_g{-2}, g_over_v{-1}, g_over_u{-1};  // -2: env not read yet
+
+// Launch shape for rows of V vectors.  An override (ep_set_tuning, or the env
+// var EP_TUNE_COMBINE="G,VPT,U") wins; results never depend on it.
+// Otherwise: one chunk that covers the row exactly, one row in flight,
+// nontemporal row loads (measured best on the training-scale rows: the rows
+// are read once, and keeping them out of the caches leaves the caches to the
+// data that is reused).
+const CombineCfg &pick(int V)
 {
-    hipLaunchKernelGGL((combine_kernel<VPT>), dim3(s.T), dim3(kCombineBlock), 0, stream,
-                       static_cast<const u32x4 *>(y), V, s.K, s.kmax, b.dst_row,
-                       recv_topk_weights, static_cast<u32x4 *>(out), combined_topk_weights);
-    return hipGetLastError();
+    if (g_over_g.load() == -2) {
+        int g = -1, v = -1, u = -1;
+        if (const char *s = std::getenv("EP_TUNE_COMBINE"))
+            if (std::sscanf(s, "%d,%d,%d", &g, &v, &u) != 3)
+                g = v = u = -1;
+        g_over_v = v;
+        g_over_u = u;
+        g_over_g = g;
+    }
+    const int og = g_over_g.load(), ov = g_over_v.load(), ou = g_over_u.load();
+    for (const CombineCfg &c : kCombineCfgs)
+        if (c.G == og && c.VPT == ov && combine_code(c) == ou)
+            return c;
+    for (const CombineCfg &c : kCombineCfgs)
+        if (c.U == 1 && c.NTL == 1 && c.P == 0 && c.G * c.VPT == V && c.G >= 128)
+            return c;
+    if (V <= 256)
+        return kCombineCfgs[0];
+    if (V <= 512)
+        return kCombineCfgs[1];
+    return kCombineCfgs[2];
 }
 
 }  // namespace
+
+bool set_combine_tuning(int g, int vpt, int u)
+{
+    if (g == -1 && vpt == -1 && u == -1) {
+        g_over_v = -1;
+        g_over_u = -1;
+        g_over_g = -1;
+        return true;
+    }
+    for (const CombineCfg &c : kCombineCfgs)
+        if (c.G == g && c.VPT == vpt && combine_code(c) == u) {
+            g_over_v = vpt;
+            g_over_u = u;
+            g_over_g = g;
+            return true;
+        }
+    return false;
+}
+
+int combine_tuning_count() { return int(sizeof(kCombineCfgs) / sizeof(kCombineCfgs[0])); }
+
+void combine_tuning_at(int i, int *g, int *vpt, int *u)
+{
+    *g = kCombineCfgs[i].G;
+    *vpt = kCombineCfgs[i].VPT;
+    *u = combine_code(kCombineCfgs[i]);
+}
 
 hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const LayoutBufs &b,
                           const float *recv_topk_weights, void *out,
@@ -128,12 +217,15 @@ hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const
     if (s.T == 0)
         return hipSuccess;
     const int V = hidden / 8;
-    const int need = (V + kCombineBlock - 1) / kCombineBlock;
-    if (need <= 1)
-        return launch_vpt<1>(s, V, y, b, recv_topk_weights, out, combined_topk_weights, stream);
-    if (need <= 2)
-        return launch_vpt<2>(s, V, y, b, recv_topk_weights, out, combined_topk_weights, stream);
-    return launch_vpt<4>(s, V, y, b, recv_topk_weights, out, combined_topk_weights, stream);
+    const CombineCfg &c = pick(V);
+    const int per_block = kCombineBlock / c.G;
+    int blocks = (s.T + per_block - 1) / per_block;
+    if (c.P > 0 && c.P < blocks)
+        blocks = c.P;
+    hipLaunchKernelGGL(c.fn, dim3(blocks), dim3(kCombineBlock), 0, stream,
+                       static_cast<const u32x4 *>(y), s.T, V, s.K, s.kmax, b.dst_row,
+                       recv_topk_weights, static_cast<u32x4 *>(out), combined_topk_weights);
+    return hipGetLastError();
 }
 
 }  // namespace ep

@@ -36,6 +36,7 @@ struct Arena {
     void *ptr = nullptr;
     size_t bytes = 0;
     hipEvent_t done = nullptr;  // recorded when the arena was returned
+    hipStream_t freed_on = nullptr;
     bool pending = false;
 };
 
@@ -99,7 +100,9 @@ int arena_get(int dev, size_t bytes, hipStream_t stream, Arena *out)
         }
     }
     if (found) {
-        if (out->pending) {
+        // Work on the stream that returned the arena is already ordered
+        // before this call; only another stream has to wait for it.
+        if (out->pending && out->freed_on != stream) {
             hipError_t e = hipStreamWaitEvent(stream, out->done, 0);
             if (e != hipSuccess) {
                 std::lock_guard<std::mutex> g(P.mu);
@@ -139,6 +142,7 @@ void arena_put(int dev, Arena a, hipStream_t stream)
 {
     hipError_t e = hipEventRecord(a.done, stream);
     a.pending = e == hipSuccess;
+    a.freed_on = stream;
     if (e != hipSuccess) {
         // Cannot order the reuse after the pending work: wait for it here.
         (void)hipGetLastError();
@@ -217,7 +221,7 @@ int create_handle(const ep_dims &d, const int64_t *topk_idx, hipStream_t stream,
         delete h;
         return hip_fail(e);
     }
-    size_t off[14];
+    size_t off[kArenaFields];
     const size_t bytes = layout_arena_bytes(h->shape, off);
     int rc = arena_get(h->device, bytes, stream, &h->arena);
     if (rc != EP_OK) {
@@ -576,6 +580,36 @@ int ep_pool_trim(void)
     if (e != hipSuccess)
         return hip_fail(e);
     return trim_pool(pool_for(dev));
+}
+
+int ep_set_tuning(const char *op, int a, int b, int c)
+{
+    if (op == nullptr)
+        return EP_ERR_INVALID;
+    if (std::strcmp(op, "dispatch") == 0)
+        return set_dispatch_tuning(a, b, c) ? EP_OK : EP_ERR_INVALID;
+    if (std::strcmp(op, "combine") == 0)
+        return set_combine_tuning(a, b, c) ? EP_OK : EP_ERR_INVALID;
+    return EP_ERR_INVALID;
+}
+
+int ep_tuning_list(const char *op, int index, int *a, int *b, int *c)
+{
+    if (op == nullptr || a == nullptr || b == nullptr || c == nullptr)
+        return -1;
+    if (std::strcmp(op, "dispatch") == 0) {
+        const int n = dispatch_tuning_count();
+        if (index >= 0 && index < n)
+            dispatch_tuning_at(index, a, b, c);
+        return n;
+    }
+    if (std::strcmp(op, "combine") == 0) {
+        const int n = combine_tuning_count();
+        if (index >= 0 && index < n)
+            combine_tuning_at(index, a, b, c);
+        return n;
+    }
+    return -1;
 }
 
 const char *ep_status_str(int status)

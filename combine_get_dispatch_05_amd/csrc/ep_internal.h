@@ -24,6 +24,7 @@ constexpr int64_t kMaxTokens = int64_t(1) << 24;
 constexpr int kMaxHidden = 1 << 20;
 
 // Device pointers of one layout (all inside a handle's arena).
+constexpr int kArenaFields = 15;
 struct LayoutBufs {
     int32_t *num_tokens_per_rank;        // [R]
     int32_t *num_tokens_per_expert;      // [E]
@@ -36,8 +37,9 @@ struct LayoutBufs {
     int32_t *dst_row;                    // [T][Kmax] packed rows of t, ascending rank, -1 padded
     int32_t *dst_rank;                   // [T][Kmax] their ranks
     uint64_t *wave_mask;                 // [nW][R] ballot of "token hits r" per 64-token wave
-    int32_t *wave_count;                 // [R][nW] per-wave counts, then exclusive bases
-    int32_t *blk_ecount;                 // [nB][E] per-block expert counts
+    int32_t *wave_base;                  // [nW][R] hits of r in earlier waves of the same block
+    int32_t *blk_count;                  // [nB][R] block totals (exclusive bases after a scan kernel)
+    int32_t *blk_ecount;                 // [nB][E] per-block expert counts (512-token blocks)
     int64_t *num_recv;                   // [1] N
 };
 
@@ -47,8 +49,8 @@ struct LayoutShape {
 
 LayoutShape layout_shape(const ep_dims &d);
 // Byte offsets of every LayoutBufs field inside one arena; returns the total.
-size_t layout_arena_bytes(const LayoutShape &s, size_t off[14]);
-LayoutBufs layout_bufs_at(void *base, const size_t off[14]);
+size_t layout_arena_bytes(const LayoutShape &s, size_t off[kArenaFields]);
+LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields]);
 
 hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const LayoutBufs &b,
                          hipStream_t stream);
@@ -68,6 +70,15 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
 hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed_y,
                              const int64_t *topk_idx, const float *topk_weights,
                              const int32_t *topk_slot, void *out, hipStream_t stream);
+
+// Launch-shape overrides (never change results).  (-1, ...) restores the
+// default choice.  Return false for a shape that is not compiled in.
+bool set_dispatch_tuning(int g, int vpt, int code);
+bool set_combine_tuning(int g, int vpt, int u);
+int dispatch_tuning_count();
+void dispatch_tuning_at(int i, int *g, int *vpt, int *code);
+int combine_tuning_count();
+void combine_tuning_at(int i, int *g, int *vpt, int *u);
 
 // ---------------------------------------------------------------- device helpers
 

@@ -9,20 +9,22 @@
 // channel_prefix_matrix, recv_channel_prefix_matrix, recv_src_idx,
 // is_token_in_rank, send_head).
 //
-// Three launches, all stream-ordered:
-//   count: one wavefront per 64 tokens.  Each lane builds its token's rank
-//          bitmask; one ballot per rank gives the wave's 64-bit membership
-//          mask for that rank, whose popcount is the wave's count.  Expert
-//          counts go to an LDS-privatised histogram per block.
-//   scan:  one block.  Per rank, an exclusive scan of the wave counts (one
-//          wavefront per rank); a block scan of the rank totals gives
-//          rank_prefix_matrix; expert totals; the channel entries that end at
-//          the last token.
-//   pos:   one wavefront per 64 tokens again.  Lanes take ranks and walk the
-//          wave's tokens, so every [T][R] row (send_head, is_token_in_rank)
-//          is written by contiguous lanes; then lanes take tokens and emit
-//          each token's destination rows in ascending rank order, the list
-//          the pack and reduce kernels read.
+// Two launches, stream-ordered (three for more than 16K tokens):
+//   count: each lane builds its token's rank bitmask; one ballot per rank
+//          gives a 64-token wave's membership mask for that rank, whose
+//          popcount is the wave's count; 512-token blocks turn those into
+//          within-block offsets in LDS and publish per-rank block totals.
+//          Expert counts go to an LDS-privatised histogram per block.
+//   (scan: for many blocks, one block turns the block totals into bases.)
+//   pos:   one 64-token tile per block.  It sums the block totals it needs
+//          (one batch of independent loads), so no block ever waits for
+//          another; every (token, rank) cell's position is a tile base plus
+//          a popcount, computed flat across the block so that [T][R] rows
+//          (send_head, is_token_in_rank) are written by contiguous lanes; one
+//          wave then emits each token's destination rows in ascending rank
+//          order, the list the pack and reduce kernels read.  Block 0 writes
+//          the totals (counts, rank_prefix_matrix, channel entries at the
+//          last token).
 // Positions come from ballots and scans, never from atomics, so every output
 // is deterministic and segments are in token order.
 
@@ -32,7 +34,7 @@ namespace ep {
 
 namespace {
 
-constexpr int kLayoutBlock = 256;  // 4 wavefronts = 256 tokens per block
+constexpr int kCountBlock = 512;  // 8 wavefronts = 512 tokens per count block
 
 template <int NW>
 __device__ __forceinline__ void token_rank_mask(const int64_t *__restrict__ row, int K, int E,
@@ -53,19 +55,38 @@ __device__ __forceinline__ void token_rank_mask(const int64_t *__restrict__ row,
     }
 }
 
-template <int NW>
-__global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(
-    const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int epr, int nW,
-    uint64_t *__restrict__ wave_mask, int32_t *__restrict__ wave_count,
-    int32_t *__restrict__ blk_ecount)
+__device__ __forceinline__ int wave_inclusive_scan(int v)
 {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(v, o, kWave);
+        if (lane >= o)
+            v += n;
+    }
+    return v;
+}
+
+// Count.  Every block (512 tokens = 8 waves): one ballot per rank gives each
+// wave's membership mask of that rank; the block turns the 8 waves'
+// popcounts into within-block offsets (LDS) and publishes masks, offsets,
+// its per-rank totals and its LDS expert histogram.
+template <int NW>
+__global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
+    const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int epr, int nW,
+    uint64_t *__restrict__ wave_mask, int32_t *__restrict__ wave_base,
+    int32_t *__restrict__ blk_count, int32_t *__restrict__ blk_ecount)
+{
+    constexpr int kWaves = kCountBlock / kWave;
     extern __shared__ int32_t s_ecount[];  // [E]
+    __shared__ int32_t s_wcnt[kWaves][kMaxRanks];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wg = blockIdx.x * (kLayoutBlock / kWave) + (tid >> 6);
-    const int64_t t = int64_t(blockIdx.x) * kLayoutBlock + tid;
+    const int wid = tid >> 6;
+    const int wg = blockIdx.x * kWaves + wid;
+    const int64_t t = int64_t(blockIdx.x) * kCountBlock + tid;
 
-    for (int i = tid; i < E; i += kLayoutBlock)
+    for (int i = tid; i < E; i += kCountBlock)
         s_ecount[i] = 0;
     __syncthreads();
 
@@ -83,189 +104,269 @@ __global__ __launch_bounds__(kLayoutBlock) void layout_count_kernel(
         }
     }
 
-    if (wg < nW) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            uint64_t mine = 0;
-            for (int b = 0; b < kWave; ++b) {
-                const int r = w * kWave + b;
-                if (r >= R)
-                    break;
-                const uint64_t bal = wave_ballot((m[w] >> b) & 1ull);
-                if (lane == b)
-                    mine = bal;
-            }
-            const int r = w * kWave + lane;
-            if (r < R) {
+    for (int w = 0; w < NW; ++w) {
+        uint64_t mine = 0;
+        for (int b = 0; b < kWave; ++b) {
+            const int r = w * kWave + b;
+            if (r >= R)
+                break;
+            const uint64_t bal = wave_ballot((m[w] >> b) & 1ull);
+            if (lane == b)
+                mine = bal;
+        }
+        const int r = w * kWave + lane;
+        if (r < R) {
+            if (wg < nW)
                 wave_mask[size_t(wg) * R + r] = mine;
-                wave_count[size_t(r) * nW + wg] = __popcll(mine);
-            }
+            s_wcnt[wid][r] = __popcll(mine);
         }
     }
-
     __syncthreads();
-    for (int i = tid; i < E; i += kLayoutBlock)
+
+    for (int r = tid; r < R; r += kCountBlock) {
+        int acc = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int c = s_wcnt[w][r];
+            const int g = blockIdx.x * kWaves + w;
+            if (g < nW)
+                wave_base[size_t(g) * R + r] = acc;
+            acc += c;
+        }
+        blk_count[size_t(blockIdx.x) * R + r] = acc;
+    }
+    for (int i = tid; i < E; i += kCountBlock)
         blk_ecount[size_t(blockIdx.x) * E + i] = s_ecount[i];
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v)
+constexpr int kPosBlock = 256;
+constexpr int kSelfScanBlocks = 32;  // up to this many count blocks, pos blocks scan for themselves
+constexpr int kBatch = 8;
+
+// Block-wide exclusive scan of v over ranks (R <= 2 * kPosBlock): each thread
+// holds two consecutive ranks.  Writes S[r] into s_seg and returns N.
+__device__ __forceinline__ int rank_exclusive_scan(const int32_t *s_tot, int32_t *s_seg, int R,
+                                                   int32_t *s_wsum)
 {
-    const int lane = threadIdx.x & (kWave - 1);
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid >> 6;
+    const int r0 = 2 * tid;
+    const int a = r0 < R ? s_tot[r0] : 0;
+    const int b = r0 + 1 < R ? s_tot[r0 + 1] : 0;
+    const int incl = wave_inclusive_scan(a + b);
+    if (lane == kWave - 1)
+        s_wsum[wid] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(v, o, kWave);
-        if (lane >= o)
-            v += n;
+    for (int w = 0; w < kPosBlock / kWave; ++w) {
+        before += w < wid ? s_wsum[w] : 0;
+        total += s_wsum[w];
     }
-    return v;
+    const int ex = before + incl - (a + b);
+    if (r0 < R)
+        s_seg[r0] = ex;
+    if (r0 + 1 < R)
+        s_seg[r0 + 1] = ex + a;
+    return total;
 }
 
-constexpr int kScanBlock = 1024;
+// Totals only the layout as a whole knows: per-rank and per-expert counts,
+// rank_prefix_matrix, N, and the channel entries at the last token.
+__device__ void write_totals(int T, int E, int R, int C, int nB, const int32_t *s_tot,
+                             const int32_t *s_seg, const int32_t *__restrict__ blk_ecount,
+                             int32_t *__restrict__ num_tokens_per_rank,
+                             int32_t *__restrict__ num_tokens_per_expert,
+                             int32_t *__restrict__ rank_prefix_matrix,
+                             int32_t *__restrict__ channel_prefix_matrix,
+                             int32_t *__restrict__ recv_channel_prefix_matrix,
+                             int64_t *__restrict__ num_recv, int N, int nthreads)
+{
+    const int tid = threadIdx.x;
+    for (int r = tid; r < R; r += nthreads) {
+        num_tokens_per_rank[r] = s_tot[r];
+        rank_prefix_matrix[r] = s_seg[r] + s_tot[r];
+        recv_channel_prefix_matrix[size_t(r) * C] = 0;
+    }
+    if (tid == 0)
+        *num_recv = N;
+    for (int e = tid; e < E; e += nthreads) {
+        int sum = 0;
+        for (int b0 = 0; b0 < nB; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                c[i] = b0 + i < nB ? blk_ecount[size_t(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                sum += c[i];
+        }
+        num_tokens_per_expert[e] = sum;
+    }
+    const int per = T > 0 ? (T + C - 1) / C : 1;
+    const int c0 = T > 0 ? (T + per - 1) / per - 1 : 0;  // first c with end(c) == T
+    const int ntail = C - c0;
+    for (int i = tid; i < R * ntail; i += nthreads) {
+        const int r = i / ntail;
+        const int c = c0 + i % ntail;
+        channel_prefix_matrix[size_t(r) * C + c] = s_tot[r];
+        if (c + 1 < C)
+            recv_channel_prefix_matrix[size_t(r) * C + c + 1] = s_tot[r];
+    }
+}
 
-__global__ __launch_bounds__(kScanBlock) void layout_scan_kernel(
-    int T, int E, int R, int C, int nW, int nB, int32_t *__restrict__ wave_count,
+// Scan for large token counts (more than kSelfScanBlocks count blocks): one
+// block turns the block totals into exclusive bases in place and writes the
+// totals.  Also the whole layout of an empty token range.
+__global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
+    int T, int E, int R, int C, int nB, int32_t *__restrict__ blk_count,
     const int32_t *__restrict__ blk_ecount, int32_t *__restrict__ num_tokens_per_rank,
     int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ rank_prefix_matrix,
     int32_t *__restrict__ channel_prefix_matrix, int32_t *__restrict__ recv_channel_prefix_matrix,
     int64_t *__restrict__ num_recv)
 {
     __shared__ int32_t s_tot[kMaxRanks];
-    __shared__ int32_t s_wsum[kScanBlock / kWave];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wid = tid >> 6;
-    constexpr int kWaves = kScanBlock / kWave;
-
-    // Per rank: exclusive scan of the wave counts over waves, in place.
-    for (int r = wid; r < R; r += kWaves) {
-        int32_t *row = wave_count + size_t(r) * nW;
+    __shared__ int32_t s_seg[kMaxRanks];
+    __shared__ int32_t s_wsum[kPosBlock / kWave];
+    for (int r = threadIdx.x; r < R; r += kPosBlock) {
         int carry = 0;
-        for (int base = 0; base < nW; base += kWave) {
-            const int i = base + lane;
-            const int v = i < nW ? row[i] : 0;
-            const int incl = wave_inclusive_scan(v);
-            if (i < nW)
-                row[i] = carry + incl - v;
-            carry += __shfl(incl, kWave - 1, kWave);
+        for (int b0 = 0; b0 < nB; b0 += kBatch) {
+            int c[kBatch];
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                c[i] = b0 + i < nB ? blk_count[size_t(b0 + i) * R + r] : 0;
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i) {
+                if (b0 + i < nB)
+                    blk_count[size_t(b0 + i) * R + r] = carry;
+                carry += c[i];
+            }
         }
-        if (lane == 0)
-            s_tot[r] = carry;
+        s_tot[r] = T > 0 ? carry : 0;
     }
     __syncthreads();
-
-    // Rank totals and their inclusive prefix (R <= 512 < block size).
-    const int v = tid < R ? s_tot[tid] : 0;
-    const int incl = wave_inclusive_scan(v);
-    if (lane == kWave - 1)
-        s_wsum[wid] = incl;
+    const int N = rank_exclusive_scan(s_tot, s_seg, R, s_wsum);
     __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wid; ++w)
-        before += s_wsum[w];
-    if (tid < R) {
-        num_tokens_per_rank[tid] = v;
-        rank_prefix_matrix[tid] = before + incl;
-        if (tid == R - 1)
-            *num_recv = before + incl;
-    }
-
-    // Expert totals over the count blocks.
-    for (int e = tid; e < E; e += kScanBlock) {
-        int s = 0;
-        for (int b = 0; b < nB; ++b)
-            s += blk_ecount[size_t(b) * E + e];
-        num_tokens_per_expert[e] = s;
-    }
-
-    // Channels ending at the last token hold the rank totals; channel 0 of the
-    // exclusive matrix is 0.  The other entries sit on token boundaries and
-    // are written by the position kernel.
-    const int per = T > 0 ? (T + C - 1) / C : 1;
-    const int c0 = T > 0 ? (T + per - 1) / per - 1 : 0;  // first c with end(c) == T
-    const int ntail = C - c0;
-    for (int i = tid; i < R * ntail; i += kScanBlock) {
-        const int r = i / ntail;
-        const int c = c0 + i % ntail;
-        const int tot = s_tot[r];
-        channel_prefix_matrix[size_t(r) * C + c] = tot;
-        if (c + 1 < C)
-            recv_channel_prefix_matrix[size_t(r) * C + c + 1] = tot;
-    }
-    for (int r = tid; r < R; r += kScanBlock)
-        recv_channel_prefix_matrix[size_t(r) * C] = 0;
+    write_totals(T, E, R, C, T > 0 ? nB : 0, s_tot, s_seg, blk_ecount, num_tokens_per_rank,
+                 num_tokens_per_expert, rank_prefix_matrix, channel_prefix_matrix,
+                 recv_channel_prefix_matrix, num_recv, N, kPosBlock);
 }
 
-template <int NW>
-__global__ __launch_bounds__(kLayoutBlock) void layout_pos_kernel(
+// Positions of one 64-token tile.  With kSelfScan the block first sums the
+// count blocks' per-rank totals itself (all loads of a batch issued before
+// any add): those before its own block give its bases, all of them give the
+// segment starts S[r]; block 0 also writes the totals.  Otherwise the bases
+// were made by layout_scan_kernel.
+//
+// The (token, rank) cells of the tile are then spread flat over the block:
+// each cell's position is its tile base plus a popcount of the rank's
+// membership mask below the token, so there is no loop-carried dependence,
+// and consecutive lanes write consecutive entries of every [T][R] row
+// (send_head, is_token_in_rank).  Finally the first wave takes the tokens and
+// emits each token's destination rows in ascending rank order, the list the
+// pack and reduce kernels read.
+template <int NW, bool kSelfScan>
+__global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int C, int epr, int kmax,
-    int nW, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
-    const int32_t *__restrict__ rank_prefix_matrix, uint8_t *__restrict__ is_token_in_rank,
-    int32_t *__restrict__ send_head, int32_t *__restrict__ recv_src_idx,
-    int32_t *__restrict__ dst_row, int32_t *__restrict__ dst_rank,
-    int32_t *__restrict__ channel_prefix_matrix, int32_t *__restrict__ recv_channel_prefix_matrix)
+    int nB, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
+    const int32_t *__restrict__ blk_count, const int32_t *__restrict__ blk_ecount,
+    uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
+    int32_t *__restrict__ recv_src_idx, int32_t *__restrict__ dst_row,
+    int32_t *__restrict__ dst_rank, int32_t *__restrict__ num_tokens_per_rank,
+    int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ rank_prefix_matrix,
+    int32_t *__restrict__ channel_prefix_matrix, int32_t *__restrict__ recv_channel_prefix_matrix,
+    int64_t *__restrict__ num_recv)
 {
-    constexpr int kWavesPerBlock = kLayoutBlock / kWave;
-    __shared__ uint64_t s_mask[kWavesPerBlock][NW * kWave];
-    __shared__ int32_t s_row0[kWavesPerBlock][NW * kWave];  // S[r] + wave base of r
+    __shared__ uint64_t s_mask[NW * kWave];
+    __shared__ int32_t s_seg[NW * kWave];  // S[r]
+    __shared__ int32_t s_off[NW * kWave];  // position of this tile's first hit inside segment r
+    __shared__ int32_t s_tot[NW * kWave];
+    __shared__ int32_t s_wsum[kPosBlock / kWave];
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wib = tid >> 6;
-    const int wg = blockIdx.x * kWavesPerBlock + wib;
-    const bool wave_live = wg < nW;
+    const int wg = blockIdx.x;
+    const int blk = wg / (kCountBlock / kWave);
     const int64_t t0 = int64_t(wg) * kWave;
+    const int ntok = int(T - t0 < kWave ? T - t0 : kWave);
 
-    if (wave_live) {
-        for (int r = lane; r < R; r += kWave) {
-            s_mask[wib][r] = wave_mask[size_t(wg) * R + r];
-            const int seg = r > 0 ? rank_prefix_matrix[r - 1] : 0;
-            s_row0[wib][r] = seg + wave_base[size_t(r) * nW + wg];
+    uint64_t m[NW];
+    if (tid < ntok)
+        token_rank_mask<NW>(topk_idx + (t0 + tid) * K, K, E, epr, m);
+    for (int r = tid; r < R; r += kPosBlock) {
+        s_mask[r] = wave_mask[size_t(wg) * R + r];
+        int before = 0, tot = 0;
+        if (kSelfScan) {
+            for (int b0 = 0; b0 < nB; b0 += kBatch) {
+                int c[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    c[i] = b0 + i < nB ? blk_count[size_t(b0 + i) * R + r] : 0;
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    before += b0 + i < blk ? c[i] : 0;
+                    tot += c[i];
+                }
+            }
+            s_tot[r] = tot;
+        } else {
+            before = blk_count[size_t(blk) * R + r];
         }
+        s_off[r] = before + wave_base[size_t(wg) * R + r];
     }
     __syncthreads();
-    if (!wave_live)
-        return;
+    if (kSelfScan) {
+        const int N = rank_exclusive_scan(s_tot, s_seg, R, s_wsum);
+        __syncthreads();
+        if (blockIdx.x == 0)
+            write_totals(T, E, R, C, nB, s_tot, s_seg, blk_ecount, num_tokens_per_rank,
+                         num_tokens_per_expert, rank_prefix_matrix, channel_prefix_matrix,
+                         recv_channel_prefix_matrix, num_recv, N, kPosBlock);
+    } else {
+        for (int r = tid; r < R; r += kPosBlock)
+            s_seg[r] = r > 0 ? rank_prefix_matrix[r - 1] : 0;
+        __syncthreads();
+    }
 
-    // Lanes = ranks: walk the wave's tokens in order.
-    const int ntok = int(T - t0 < kWave ? T - t0 : kWave);
+    // Flat walk over the tile's cells, (token, rank) row-major.
+    const int cells = ntok * R;
+    const int dt = kPosBlock / R, dr = kPosBlock % R;
+    int tl = tid / R, r = tid % R;
+    for (int i = tid; i < cells; i += kPosBlock) {
+        const uint64_t b = s_mask[r];
+        const bool hit = (b >> tl) & 1ull;
+        const int pos = s_off[r] + __popcll(b & ((1ull << tl) - 1ull));
+        const int64_t t = t0 + tl;
+        send_head[size_t(t) * R + r] = hit ? pos : -1;
+        is_token_in_rank[size_t(t) * R + r] = hit ? 1 : 0;
+        if (hit)
+            recv_src_idx[s_seg[r] + pos] = int32_t(t);
+        tl += dt;
+        r += dr;
+        if (r >= R) {
+            r -= R;
+            ++tl;
+        }
+    }
+
+    // Channel ends inside the tile: hits of rank r before the boundary token.
     const int per = (T + C - 1) / C;
-    int64_t first_boundary = ((t0 + per - 1) / per) * per;  // smallest multiple of per >= t0
-    if (first_boundary == 0)
-        first_boundary = per;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int r = w * kWave + lane;
-        const bool act = r < R;
-        const uint64_t b = act ? s_mask[wib][r] : 0;
-        const int row0 = act ? s_row0[wib][r] : 0;
-        const int seg = act ? (r > 0 ? rank_prefix_matrix[r - 1] : 0) : 0;
-        int pos = row0 - seg;  // position inside segment r of the next hit
-        int64_t boundary = first_boundary;
-        for (int tl = 0; tl < ntok; ++tl) {
-            const int64_t t = t0 + tl;
-            const bool hit = (b >> tl) & 1ull;
-            if (t == boundary) {  // end of channel t/per - 1, which is < T
-                if (act) {
-                    const int64_t c = t / per - 1;
-                    channel_prefix_matrix[size_t(r) * C + c] = pos;
-                    recv_channel_prefix_matrix[size_t(r) * C + c + 1] = pos;
-                }
-                boundary += per;
-            }
-            if (act) {
-                send_head[size_t(t) * R + r] = hit ? pos : -1;
-                is_token_in_rank[size_t(t) * R + r] = hit ? 1 : 0;
-                if (hit)
-                    recv_src_idx[seg + pos] = int32_t(t);
-            }
-            pos += hit ? 1 : 0;
+    int64_t boundary = ((t0 + per - 1) / per) * per;  // smallest multiple of per >= t0
+    if (boundary == 0)
+        boundary = per;
+    for (; boundary < t0 + ntok; boundary += per) {
+        const int bl = int(boundary - t0);
+        const int64_t c = boundary / per - 1;
+        for (int rr = tid; rr < R; rr += kPosBlock) {
+            const int cnt = s_off[rr] + __popcll(s_mask[rr] & ((1ull << bl) - 1ull));
+            channel_prefix_matrix[size_t(rr) * C + c] = cnt;
+            recv_channel_prefix_matrix[size_t(rr) * C + c + 1] = cnt;
         }
     }
 
     // Lanes = tokens: each token's destination rows, ascending rank.
-    const int64_t t = t0 + lane;
-    if (t < T) {
-        uint64_t m[NW];
-        token_rank_mask<NW>(topk_idx + t * K, K, E, epr, m);
+    if (tid < ntok) {
+        const int64_t t = t0 + tid;
         const uint64_t below = lanemask_lt();
         int j = 0;
 #pragma unroll
@@ -274,10 +375,9 @@ __global__ __launch_bounds__(kLayoutBlock) void layout_pos_kernel(
             while (mm) {
                 const int bit = __ffsll((unsigned long long)mm) - 1;
                 mm &= mm - 1;
-                const int r = w * kWave + bit;
-                const int row = s_row0[wib][r] + __popcll(s_mask[wib][r] & below);
-                dst_row[size_t(t) * kmax + j] = row;
-                dst_rank[size_t(t) * kmax + j] = r;
+                const int rr = w * kWave + bit;
+                dst_row[size_t(t) * kmax + j] = s_seg[rr] + s_off[rr] + __popcll(s_mask[rr] & below);
+                dst_rank[size_t(t) * kmax + j] = rr;
                 ++j;
             }
         }
@@ -292,22 +392,24 @@ template <int NW>
 hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx, const LayoutBufs &b,
                             hipStream_t stream)
 {
-    if (s.T > 0) {
-        hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(s.nB), dim3(kLayoutBlock),
+    if (s.T > 0)
+        hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(s.nB), dim3(kCountBlock),
                            size_t(s.E) * sizeof(int32_t), stream, topk_idx, s.T, s.K, s.E, s.R,
-                           s.epr, s.nW, b.wave_mask, b.wave_count, b.blk_ecount);
-    }
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kScanBlock), 0, stream, s.T, s.E, s.R,
-                       s.C, s.nW, s.nB, b.wave_count, b.blk_ecount, b.num_tokens_per_rank,
-                       b.num_tokens_per_expert, b.rank_prefix_matrix, b.channel_prefix_matrix,
-                       b.recv_channel_prefix_matrix, b.num_recv);
-    if (s.T > 0) {
-        hipLaunchKernelGGL(layout_pos_kernel<NW>, dim3(s.nB), dim3(kLayoutBlock), 0, stream,
-                           topk_idx, s.T, s.K, s.E, s.R, s.C, s.epr, s.kmax, s.nW, b.wave_mask,
-                           b.wave_count, b.rank_prefix_matrix, b.is_token_in_rank, b.send_head,
-                           b.recv_src_idx, b.dst_row, b.dst_rank, b.channel_prefix_matrix,
-                           b.recv_channel_prefix_matrix);
-    }
+                           s.epr, s.nW, b.wave_mask, b.wave_base, b.blk_count, b.blk_ecount);
+    const bool self_scan = s.T > 0 && s.nB <= kSelfScanBlocks;
+    if (!self_scan)
+        hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kPosBlock), 0, stream, s.T, s.E, s.R,
+                           s.C, s.nB, b.blk_count, b.blk_ecount, b.num_tokens_per_rank,
+                           b.num_tokens_per_expert, b.rank_prefix_matrix, b.channel_prefix_matrix,
+                           b.recv_channel_prefix_matrix, b.num_recv);
+    auto pos_kernel = self_scan ? layout_pos_kernel<NW, true> : layout_pos_kernel<NW, false>;
+    if (s.T > 0)
+        hipLaunchKernelGGL(pos_kernel, dim3(s.nW), dim3(kPosBlock), 0, stream, topk_idx, s.T, s.K, s.E, s.R,
+                           s.C, s.epr, s.kmax, s.nB, b.wave_mask, b.wave_base, b.blk_count,
+                           b.blk_ecount, b.is_token_in_rank, b.send_head, b.recv_src_idx,
+                           b.dst_row, b.dst_rank, b.num_tokens_per_rank, b.num_tokens_per_expert,
+                           b.rank_prefix_matrix, b.channel_prefix_matrix,
+                           b.recv_channel_prefix_matrix, b.num_recv);
     return hipGetLastError();
 }
 
@@ -324,27 +426,27 @@ LayoutShape layout_shape(const ep_dims &d)
     s.epr = s.E / s.R;
     s.kmax = s.K < s.R ? s.K : s.R;
     s.nW = (s.T + kWave - 1) / kWave;
-    s.nB = (s.T + kLayoutBlock - 1) / kLayoutBlock;
+    s.nB = s.T > 0 ? (s.T + kCountBlock - 1) / kCountBlock : 1;
     return s;
 }
 
-size_t layout_arena_bytes(const LayoutShape &s, size_t off[14])
+size_t layout_arena_bytes(const LayoutShape &s, size_t off[kArenaFields])
 {
     const size_t T = size_t(s.T), R = size_t(s.R), E = size_t(s.E), C = size_t(s.C);
     const size_t km = size_t(s.kmax), nW = size_t(s.nW), nB = size_t(s.nB);
-    const size_t sizes[14] = {
-        R * 4,       E * 4,      T * R,       R * 4,       R * C * 4,   R * C * 4,  T * R * 4,
-        T * km * 4,  T * km * 4, T * km * 4,  nW * R * 8,  R * nW * 4,  nB * E * 4, 8,
+    const size_t sizes[kArenaFields] = {
+        R * 4,      E * 4,      T * R,      R * 4,      R * C * 4,  R * C * 4,  T * R * 4,
+        T * km * 4, T * km * 4, T * km * 4, nW * R * 8, nW * R * 4, nB * R * 4, nB * E * 4, 8,
     };
     size_t cur = 0;
-    for (int i = 0; i < 14; ++i) {
+    for (int i = 0; i < kArenaFields; ++i) {
         off[i] = cur;
         cur += (sizes[i] + 255) & ~size_t(255);
     }
     return cur;
 }
 
-LayoutBufs layout_bufs_at(void *base, const size_t off[14])
+LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields])
 {
     char *p = static_cast<char *>(base);
     LayoutBufs b;
@@ -359,9 +461,10 @@ LayoutBufs layout_bufs_at(void *base, const size_t off[14])
     b.dst_row = reinterpret_cast<int32_t *>(p + off[8]);
     b.dst_rank = reinterpret_cast<int32_t *>(p + off[9]);
     b.wave_mask = reinterpret_cast<uint64_t *>(p + off[10]);
-    b.wave_count = reinterpret_cast<int32_t *>(p + off[11]);
-    b.blk_ecount = reinterpret_cast<int32_t *>(p + off[12]);
-    b.num_recv = reinterpret_cast<int64_t *>(p + off[13]);
+    b.wave_base = reinterpret_cast<int32_t *>(p + off[11]);
+    b.blk_count = reinterpret_cast<int32_t *>(p + off[12]);
+    b.blk_ecount = reinterpret_cast<int32_t *>(p + off[13]);
+    b.num_recv = reinterpret_cast<int64_t *>(p + off[14]);
     return b;
 }
 

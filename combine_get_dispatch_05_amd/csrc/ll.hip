@@ -7,9 +7,9 @@
 // the tokens' positions, weighted by the top-k weights.
 //
 // Dispatch is one fused launch with one workgroup per expert: the workgroup
-// scans the [T][K] table in (token, slot) order, turns "names my expert" into
-// slots with a ballot + block prefix (so slots follow token order), records
-// the token of each slot, and then copies those token rows into the expert's
+// scans the [T][K] table, turns "names my expert" into slots with one
+// block-wide prefix scan (so slots follow (token, slot) order), records the
+// token of each slot, and then copies those token rows into the expert's
 // area [le][r][slot][:] with every lane issuing independent 16-byte loads and
 // stores.  No layout pass, no second launch, no host sync.
 //
@@ -26,14 +26,33 @@ namespace {
 constexpr int kLLBlock = 256;
 constexpr int kLLWaves = kLLBlock / kWave;
 
+__device__ __forceinline__ int ll_wave_inclusive_scan(int v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(v, o, kWave);
+        if (lane >= o)
+            v += n;
+    }
+    return v;
+}
+
+// One workgroup per expert.  Each thread owns a contiguous chunk of the
+// flattened [T][K] table (held in registers when it is short), counts the
+// pairs naming its expert, and one block-wide exclusive scan of those counts
+// gives every thread the first slot of its chunk, so slots follow (token,
+// slot) order.  The rows are then copied with the (row, vector) pairs spread
+// flat over the block, kUnroll independent 16-byte loads in flight per lane.
 __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
     const u32x4 *__restrict__ x, int T, int V, int K, int E, int R, int epr, int S,
     const int64_t *__restrict__ topk_idx, u32x4 *__restrict__ packed_x,
     int32_t *__restrict__ packed_count, int32_t *__restrict__ src_info,
     int32_t *__restrict__ topk_slot)
 {
+    constexpr int kHold = 8;
     __shared__ int32_t s_tok[kMaxLLSlots];
-    __shared__ int32_t s_wcnt[kLLWaves];
+    __shared__ int32_t s_wsum[kLLWaves];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
@@ -42,65 +61,89 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
     const int r = e / epr;
     const int64_t cell0 = (int64_t(le) * R + r) * S;
     const int TK = T * K;
+    const int chunk = (TK + kLLBlock - 1) / kLLBlock;
+    const int i0 = tid * chunk;
+    const int i1 = i0 + chunk < TK ? i0 + chunk : TK;
+    const bool held = chunk <= kHold;
 
-    int running = 0;
-    for (int base = 0; base < TK; base += kLLBlock) {
-        const int i = base + tid;
-        const int64_t v = i < TK ? topk_idx[i] : -1;
-        const bool match = v == e;
-        if (e == 0 && i < TK && !(v >= 0 && v < E))
-            topk_slot[i] = -1;  // masked or invalid slots: workgroup 0 marks them
-        const uint64_t bal = wave_ballot(match);
-        if (lane == 0)
-            s_wcnt[wid] = __popcll(bal);
-        __syncthreads();
-        int before = 0, total = 0;
+    int64_t v[kHold];
+    int mine = 0;
+    if (held) {
 #pragma unroll
-        for (int w = 0; w < kLLWaves; ++w) {
-            const int c = s_wcnt[w];
-            before += w < wid ? c : 0;
-            total += c;
+        for (int q = 0; q < kHold; ++q) {
+            v[q] = i0 + q < i1 ? topk_idx[i0 + q] : -1;
+            mine += v[q] == e ? 1 : 0;
         }
-        if (match) {
-            const int s = running + before + __popcll(bal & lanemask_lt());
-            const int tok = i / K;
+    } else {
+        for (int i = i0; i < i1; ++i)
+            mine += topk_idx[i] == e ? 1 : 0;
+    }
+
+    const int incl = ll_wave_inclusive_scan(mine);
+    if (lane == kWave - 1)
+        s_wsum[wid] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kLLWaves; ++w) {
+        const int c = s_wsum[w];
+        before += w < wid ? c : 0;
+        total += c;
+    }
+    int s = before + incl - mine;  // first slot of this thread's chunk
+
+    auto place = [&](int i, int64_t val) {
+        if (val == e) {
             if (s < S) {
                 topk_slot[i] = s;
-                src_info[cell0 + s] = tok;
-                s_tok[s] = tok;
+                src_info[cell0 + s] = i / K;
+                s_tok[s] = i / K;
             } else {
                 topk_slot[i] = -1;
             }
+            ++s;
+        } else if (e == 0 && !(val >= 0 && val < E)) {
+            topk_slot[i] = -1;  // masked or invalid slots: workgroup 0 marks them
         }
-        running += total;
-        __syncthreads();
+    };
+    if (held) {
+#pragma unroll
+        for (int q = 0; q < kHold; ++q)
+            if (i0 + q < i1)
+                place(i0 + q, v[q]);
+    } else {
+        for (int i = i0; i < i1; ++i)
+            place(i, topk_idx[i]);
     }
+
     if (tid == 0)
-        packed_count[int64_t(le) * R + r] = running;
-    const int used = running < S ? running : S;
-    for (int s = used + tid; s < S; s += kLLBlock)
-        src_info[cell0 + s] = -1;
+        packed_count[int64_t(le) * R + r] = total;
+    const int used = total < S ? total : S;
+    for (int q = used + tid; q < S; q += kLLBlock)
+        src_info[cell0 + q] = -1;
+    __syncthreads();
 
     if (packed_x != nullptr) {
-        constexpr int kUnroll = 4;
-        for (int s = 0; s < used; ++s) {
-            const u32x4 *src = x + int64_t(s_tok[s]) * V;
-            u32x4 *dst = packed_x + (cell0 + s) * V;
-            for (int b0 = 0; b0 < V; b0 += kLLBlock * kUnroll) {
-                u32x4 v[kUnroll];
+        constexpr int kUnroll = 8;
+        const int n = used * V;
+        for (int p0 = 0; p0 < n; p0 += kLLBlock * kUnroll) {
+            u32x4 buf[kUnroll];
+            int64_t dst[kUnroll];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int idx = b0 + u * kLLBlock + tid;
-                    if (idx < V)
-                        v[u] = src[idx];
-                }
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int idx = b0 + u * kLLBlock + tid;
-                    if (idx < V)
-                        dst[idx] = v[u];
+            for (int u = 0; u < kUnroll; ++u) {
+                const int p = p0 + u * kLLBlock + tid;
+                dst[u] = -1;
+                if (p < n) {
+                    const int row = p / V;
+                    const int col = p - row * V;
+                    buf[u] = x[int64_t(s_tok[row]) * V + col];
+                    dst[u] = (cell0 + row) * V + col;
                 }
             }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                if (dst[u] >= 0)
+                    packed_x[dst[u]] = buf[u];
         }
     }
 }
@@ -132,7 +175,7 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_kernel(
         for (int q = 0; q < 8; ++q)
             acc[i][q] = 0.0f;
 
-    constexpr int kGroup = 4;
+    constexpr int kGroup = 8;
     for (int k0 = 0; k0 < K; k0 += kGroup) {
         u32x4 v[kGroup][VPT];
 #pragma unroll

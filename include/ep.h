@@ -235,6 +235,22 @@ void ep_handle_free(ep_handle *handle);
  * device (waits for their pending work).  Returns an ep_status. */
 int ep_pool_trim(void);
 
+/* Launch-shape override for the pack ("dispatch") or the reduce ("combine")
+ * kernels, process-wide, for every later call.  Results never depend on it.
+ * a = lanes per token G, b = 16-byte vectors per lane VPT, c = a code for
+ * the rest: dispatch NTS*10 + P/256, combine U*100 + NTL*10 + P/256, where
+ * NTS/NTL = nontemporal stores/loads, U = rows in flight and P = persistent
+ * block count (0 = one lane group per token).  ep_tuning_list enumerates the
+ * compiled-in shapes.  a = b = c = -1 restores the default choice; a shape
+ * that is not compiled in returns EP_ERR_INVALID.  The env vars
+ * EP_TUNE_DISPATCH="G,VPT,c" and EP_TUNE_COMBINE="G,VPT,c" set the initial
+ * override. */
+int ep_set_tuning(const char *op, int a, int b, int c);
+
+/* Enumerate the compiled-in shapes of `op`: writes shape `index` (if in
+ * range) to a, b, c and returns how many there are (-1 for an unknown op). */
+int ep_tuning_list(const char *op, int index, int *a, int *b, int *c);
+
 /* Static text of a status code. */
 const char *ep_status_str(int status);
 

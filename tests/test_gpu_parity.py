@@ -292,3 +292,39 @@ def test_guard_bands_and_determinism():
         abi.lib().ep_handle_free(raw)
     assert np.array_equal(results[0][0], results[1][0])
     assert np.array_equal(results[0][1], results[1][1])
+
+
+@pytest.mark.parametrize("H", [7168, 2056, 64])
+def test_every_launch_shape(H):
+    """Every compiled-in pack and reduce launch shape gives the oracle's bytes
+    (shapes change only how work is split, never the result)."""
+    inp = random_case(99, 301, H, 64, 8, 16, 5, mask=0.1, dup=0.1)
+    E, R, C = inp.E, inp.R, inp.C
+    ora = oracle.layout(inp.topk_idx, E, R, C)
+    o_rx, o_rti, o_rtw = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, E, R, ora)
+    y = random_rows(ora.num_recv, H, 5, tag=12)
+    o_out, o_cw = oracle.combine(y, ora, o_rtw)
+    buf = epm.Buffer(R, E, C)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+    yd = dev_bf16(y)
+    try:
+        for shape in abi.tunings("dispatch"):
+            abi.set_tuning("dispatch", *shape)
+            rx, rti, rtw, _, h, _ = buf.dispatch(x, topk, w)
+            np.testing.assert_array_equal(host_bits(rx), o_rx, err_msg=str(shape))
+            np.testing.assert_array_equal(host(rti), o_rti, err_msg=str(shape))
+            np.testing.assert_array_equal(f32_bits(host(rtw)), f32_bits(o_rtw), err_msg=str(shape))
+            rx2, _, _, _, _, _ = buf.dispatch(x, handle=h)
+            np.testing.assert_array_equal(host_bits(rx2), o_rx, err_msg=str(shape))
+            h.free()
+        abi.set_tuning("dispatch")
+        _, _, _, _, h, _ = buf.dispatch(x, topk, w)
+        for shape in abi.tunings("combine"):
+            abi.set_tuning("combine", *shape)
+            out, cw, _ = buf.combine(yd, h, dev(o_rtw))
+            assert_bf16_close(host_bits(out), o_out, what=f"combine {shape}")
+            np.testing.assert_array_equal(f32_bits(host(cw)), f32_bits(o_cw), err_msg=str(shape))
+        h.free()
+    finally:
+        abi.set_tuning("dispatch")
+        abi.set_tuning("combine")
