@@ -16,7 +16,8 @@ input, all on torch's current stream, through the C ABI:
 
 Inputs are generated and copied to HBM before timing; successive steps use
 four copies of the token batches in turn (470 MB, more than the last-level
-cache), so each dispatch reads its rows from HBM.  Device buffers are sized
+cache), so each dispatch reads its rows from HBM, and two copies of each
+packed-row buffer, so no dispatch overwrites rows still dirty in a cache.  Device buffers are sized
 for the worst case (T*min(K,R) rows), so no step synchronizes the host.
 ``value`` is whole-job throughput: the algorithmic bytes of all operations
 divided by the wall time of the timed steps.  Inside the timed steps HIP
@@ -129,8 +130,10 @@ def main():
     w = to_dev(tr.topk_weights)
     d = abi.dims(T, H, K, E, R, C)
     cap = int(L.ep_max_recv_rows(ctypes.byref(d)))
-    recv_x = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
-    recv_x2 = torch.empty((cap, H), dtype=torch.bfloat16, device=dev)
+    # Two packed-row buffers per dispatch, used in turn, so a dispatch never
+    # overwrites rows that the previous step may still hold dirty in a cache.
+    recv_xs = [torch.empty((cap, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    recv_x2s = [torch.empty((cap, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
     rti = torch.empty((cap, K), dtype=torch.int64, device=dev)
     rtw = torch.empty((cap, K), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -158,6 +161,8 @@ def main():
         s = abi.current_stream()
         x = xs[counter[0] % NBUF]
         x2 = x2s[counter[0] % NBUF]
+        recv_x = recv_xs[counter[0] % 2]
+        recv_x2 = recv_x2s[counter[0] % 2]
         counter[0] += 1
 
         def mark(i):

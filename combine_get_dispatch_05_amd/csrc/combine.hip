@@ -49,12 +49,15 @@ __device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
     return *p;
 }
 
-// One group of G lanes reduces one token at a time; with a persistent grid
-// (fewer groups than tokens) each group walks tokens with a grid stride.
-// NTL: rows are loaded nontemporally (each is read exactly once).
+// A group of G lanes reduces one slice of one token's row at a time: the
+// row's chunks of G*VPT vectors are dealt round-robin to S groups (S = 1: one
+// group per token).  With a persistent grid (fewer groups than token slices)
+// each group walks them with a grid stride.  NTL: rows are loaded
+// nontemporally (each is read exactly once).  The slice-0 group reduces the
+// weights.
 template <int G, int VPT, int U, bool NTL>
 __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
-    const u32x4 *__restrict__ y, int T, int V, int K, int kmax,
+    const u32x4 *__restrict__ y, int T, int V, int K, int kmax, int S,
     const int32_t *__restrict__ dst_row, const float *__restrict__ recv_topk_weights,
     u32x4 *__restrict__ out, float *__restrict__ combined_topk_weights)
 {
@@ -63,11 +66,13 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
     const int gt = threadIdx.x % G;
     const int first = __builtin_amdgcn_readfirstlane(blockIdx.x * kGroups + threadIdx.x / G);
     const int stride = gridDim.x * kGroups;
-    for (int t = first; t < T; t += stride) {
+    for (int ts = first; ts < T * S; ts += stride) {
+        const int t = ts / S;
+        const int slice = ts - t * S;
         const int rowv = lane < kmax ? dst_row[int64_t(t) * kmax + lane] : -1;
         const int nhit = __popcll(wave_ballot(rowv >= 0));
 
-        for (int base = 0; base < V; base += G * VPT) {
+        for (int base = slice * G * VPT; base < V; base += S * G * VPT) {
             float acc[VPT][8];
 #pragma unroll
             for (int i = 0; i < VPT; ++i)
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
             }
         }
 
-        if (combined_topk_weights != nullptr) {
+        if (combined_topk_weights != nullptr && slice == 0) {
             for (int k = gt; k < K; k += G) {
                 float w = 0.0f;
                 for (int j = 0; j < nhit; ++j) {
@@ -122,31 +127,35 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
     }
 }
 
-typedef void (*CombineFn)(const u32x4 *, int, int, int, int, const int32_t *, const float *,
-                          u32x4 *, float *);
+typedef void (*CombineFn)(const u32x4 *, int, int, int, int, int, const int32_t *,
+                          const float *, u32x4 *, float *);
 
-// A launch shape: G lanes per token, VPT vectors per lane, U rows in flight,
-// NTL nontemporal row loads, and P = persistent block count (0: one group per
-// token).  The tuning knob addresses shapes as (G, VPT, U*100 + NTL*10 + P/256)
-// so that one int carries the last three.
+// A launch shape: G lanes per group, VPT vectors per lane, S groups per token
+// (row slices), U rows in flight, NTL nontemporal row loads, and P =
+// persistent block count (0: one group per token slice).  The tuning knob
+// addresses shapes as (G, VPT, S*1000 + U*100 + NTL*10 + P/256).
 struct CombineCfg {
-    int G, VPT, U, NTL, P;
+    int G, VPT, S, U, NTL, P;
     CombineFn fn;
 };
 
-#define EP_COMBINE_CFG(G, VPT, U, NTL, P) {G, VPT, U, NTL, P, combine_kernel<G, VPT, U, NTL>}
+#define EP_COMBINE_CFG(G, VPT, S, U, NTL, P) {G, VPT, S, U, NTL, P, combine_kernel<G, VPT, U, NTL>}
 
 const CombineCfg kCombineCfgs[] = {
-    EP_COMBINE_CFG(256, 1, 2, 1, 0),    EP_COMBINE_CFG(256, 2, 2, 1, 0),
-    EP_COMBINE_CFG(256, 4, 2, 1, 0),    EP_COMBINE_CFG(256, 4, 4, 1, 0),
-    EP_COMBINE_CFG(256, 4, 2, 0, 0),    EP_COMBINE_CFG(128, 7, 1, 1, 0),
-    EP_COMBINE_CFG(128, 7, 2, 1, 0),    EP_COMBINE_CFG(128, 7, 2, 0, 0),
-    EP_COMBINE_CFG(128, 7, 4, 1, 0),    EP_COMBINE_CFG(128, 7, 2, 1, 1024),
-    EP_COMBINE_CFG(128, 8, 2, 1, 0),    EP_COMBINE_CFG(64, 14, 1, 1, 0),
-    EP_COMBINE_CFG(64, 14, 2, 1, 0),    EP_COMBINE_CFG(64, 7, 2, 1, 0),
+    EP_COMBINE_CFG(256, 1, 1, 2, 1, 0), EP_COMBINE_CFG(256, 2, 1, 2, 1, 0),
+    EP_COMBINE_CFG(256, 4, 1, 2, 1, 0), EP_COMBINE_CFG(256, 4, 1, 4, 1, 0),
+    EP_COMBINE_CFG(128, 7, 1, 1, 1, 0), EP_COMBINE_CFG(128, 7, 1, 1, 0, 0),
+    EP_COMBINE_CFG(128, 7, 1, 2, 1, 0), EP_COMBINE_CFG(128, 8, 1, 2, 1, 0),
+    EP_COMBINE_CFG(64, 14, 1, 1, 1, 0), EP_COMBINE_CFG(64, 7, 2, 1, 1, 0),
+    EP_COMBINE_CFG(64, 7, 2, 2, 1, 0),  EP_COMBINE_CFG(64, 4, 4, 2, 1, 0),
+    EP_COMBINE_CFG(64, 2, 7, 4, 1, 0),  EP_COMBINE_CFG(64, 2, 7, 8, 1, 0),
+    EP_COMBINE_CFG(64, 1, 14, 8, 1, 0),
 };
 
-int combine_code(const CombineCfg &c) { return c.U * 100 + c.NTL * 10 + c.P / 256; }
+int combine_code(const CombineCfg &c)
+{
+    return c.S * 1000 + c.U * 100 + c.NTL * 10 + c.P / 256;
+}
 
 std::atomic<int> g_over_g{-2}, g_over_v{-1}, g_over_u{-1};  // -2: env not read yet
 
@@ -172,7 +181,7 @@ const CombineCfg &pick(int V)
         if (c.G == og && c.VPT == ov && combine_code(c) == ou)
             return c;
     for (const CombineCfg &c : kCombineCfgs)
-        if (c.U == 1 && c.NTL == 1 && c.P == 0 && c.G * c.VPT == V && c.G >= 128)
+        if (c.S == 1 && c.U == 1 && c.NTL == 1 && c.P == 0 && c.G * c.VPT == V && c.G >= 128)
             return c;
     if (V <= 256)
         return kCombineCfgs[0];
@@ -219,11 +228,12 @@ hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const
     const int V = hidden / 8;
     const CombineCfg &c = pick(V);
     const int per_block = kCombineBlock / c.G;
-    int blocks = (s.T + per_block - 1) / per_block;
+    const int64_t groups = int64_t(s.T) * c.S;
+    int blocks = int((groups + per_block - 1) / per_block);
     if (c.P > 0 && c.P < blocks)
         blocks = c.P;
     hipLaunchKernelGGL(c.fn, dim3(blocks), dim3(kCombineBlock), 0, stream,
-                       static_cast<const u32x4 *>(y), s.T, V, s.K, s.kmax, b.dst_row,
+                       static_cast<const u32x4 *>(y), s.T, V, s.K, s.kmax, c.S, b.dst_row,
                        recv_topk_weights, static_cast<u32x4 *>(out), combined_topk_weights);
     return hipGetLastError();
 }

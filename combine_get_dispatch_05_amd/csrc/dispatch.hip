@@ -48,12 +48,15 @@ __device__ __forceinline__ u32x4 load_x_vec(const u32x4 *p)
     return *p;
 }
 
-// One group of G lanes packs one token at a time; with a persistent grid
-// (fewer groups than tokens) each group walks tokens with a grid stride.
-// NTS / NTL: packed rows are stored / token rows loaded nontemporally.
+// A group of G lanes packs one slice of one token's row at a time: the row's
+// chunks of G*VPT vectors are dealt round-robin to S groups (S = 1: one group
+// per token), so more, shorter-lived wavefronts share the stores.  With a
+// persistent grid (fewer groups than token slices) each group walks them with
+// a grid stride.  NTS / NTL: packed rows are stored / token rows loaded
+// nontemporally.  The slice-0 group writes the top-k outputs.
 template <int G, int VPT, bool NTS, bool NTL, bool kTopk>
 __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
-    const u32x4 *__restrict__ x, int T, int V, int K, int E, int epr, int kmax,
+    const u32x4 *__restrict__ x, int T, int V, int K, int E, int epr, int kmax, int S,
     const int32_t *__restrict__ dst_row, const int32_t *__restrict__ dst_rank,
     const int64_t *__restrict__ topk_idx, const float *__restrict__ topk_weights,
     u32x4 *__restrict__ recv_x, int64_t *__restrict__ recv_topk_idx,
@@ -64,13 +67,15 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
     const int gt = threadIdx.x % G;
     const int first = __builtin_amdgcn_readfirstlane(blockIdx.x * kGroups + threadIdx.x / G);
     const int stride = gridDim.x * kGroups;
-    for (int t = first; t < T; t += stride) {
+    for (int ts = first; ts < T * S; ts += stride) {
+        const int t = ts / S;
+        const int slice = ts - t * S;
         const u32x4 *src = x + int64_t(t) * V;
         const int rowv = lane < kmax ? dst_row[int64_t(t) * kmax + lane] : -1;
         const int nhit = __popcll(wave_ballot(rowv >= 0));  // rows are packed first
 
         if (recv_x != nullptr) {
-            for (int base = 0; base < V; base += G * VPT) {
+            for (int base = slice * G * VPT; base < V; base += S * G * VPT) {
                 u32x4 v[VPT];
 #pragma unroll
                 for (int i = 0; i < VPT; ++i) {
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
             }
         }
 
-        if (kTopk) {
+        if (kTopk && slice == 0) {
             const int rankv = lane < kmax ? dst_rank[int64_t(t) * kmax + lane] : -1;
             for (int k = gt; k < K; k += G) {
                 const int64_t e = topk_idx[int64_t(t) * K + k];
@@ -113,35 +118,38 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
     }
 }
 
-typedef void (*PackFn)(const u32x4 *, int, int, int, int, int, int, const int32_t *,
+typedef void (*PackFn)(const u32x4 *, int, int, int, int, int, int, int, const int32_t *,
                        const int32_t *, const int64_t *, const float *, u32x4 *, int64_t *,
                        float *);
 
-// A launch shape: G lanes per token, VPT vectors per lane, NTS / NTL
-// nontemporal stores / loads, P persistent block count (0: one group per
-// token).  The tuning knob addresses shapes as (G, VPT, NTL*100 + NTS*10 +
-// P/256).
+// A launch shape: G lanes per group, VPT vectors per lane, S groups per token
+// (row slices), NTS / NTL nontemporal stores / loads, P persistent block
+// count (0: one group per token slice).  The tuning knob addresses shapes as
+// (G, VPT, S*1000 + NTL*100 + NTS*10 + P/256).
 struct PackCfg {
-    int G, VPT, NTS, NTL, P;
+    int G, VPT, S, NTS, NTL, P;
     PackFn plain, topk;
 };
 
-#define EP_PACK_CFG(G, VPT, NTS, NTL, P)                                                   \
-    {G, VPT, NTS, NTL, P, dispatch_pack_kernel<G, VPT, NTS, NTL, false>,                   \
+#define EP_PACK_CFG(G, VPT, S, NTS, NTL, P)                                                \
+    {G, VPT, S, NTS, NTL, P, dispatch_pack_kernel<G, VPT, NTS, NTL, false>,                \
      dispatch_pack_kernel<G, VPT, NTS, NTL, true>}
 
 const PackCfg kPackCfgs[] = {
-    EP_PACK_CFG(256, 1, 1, 0, 0),    EP_PACK_CFG(256, 2, 1, 0, 0),
-    EP_PACK_CFG(256, 4, 1, 0, 0),    EP_PACK_CFG(256, 4, 1, 1, 0),
-    EP_PACK_CFG(128, 4, 1, 0, 0),    EP_PACK_CFG(128, 7, 1, 0, 0),
-    EP_PACK_CFG(128, 7, 1, 1, 0),    EP_PACK_CFG(128, 7, 0, 0, 0),
-    EP_PACK_CFG(128, 7, 0, 1, 0),    EP_PACK_CFG(128, 7, 1, 0, 1024),
-    EP_PACK_CFG(128, 8, 1, 0, 0),    EP_PACK_CFG(64, 8, 1, 0, 0),
-    EP_PACK_CFG(64, 14, 1, 0, 0),    EP_PACK_CFG(64, 14, 1, 1, 0),
-    EP_PACK_CFG(64, 16, 1, 0, 0),
+    EP_PACK_CFG(256, 1, 1, 1, 0, 0),  EP_PACK_CFG(256, 2, 1, 1, 0, 0),
+    EP_PACK_CFG(256, 4, 1, 1, 0, 0),  EP_PACK_CFG(128, 4, 1, 1, 0, 0),
+    EP_PACK_CFG(128, 7, 1, 1, 0, 0),  EP_PACK_CFG(128, 7, 1, 0, 0, 0),
+    EP_PACK_CFG(128, 7, 1, 1, 1, 0),  EP_PACK_CFG(128, 8, 1, 1, 0, 0),
+    EP_PACK_CFG(64, 14, 1, 1, 0, 0),  EP_PACK_CFG(64, 7, 2, 1, 0, 0),
+    EP_PACK_CFG(64, 4, 4, 1, 0, 0),   EP_PACK_CFG(64, 2, 7, 1, 0, 0),
+    EP_PACK_CFG(64, 1, 14, 1, 0, 0),  EP_PACK_CFG(64, 2, 7, 0, 0, 0),
+    EP_PACK_CFG(64, 2, 7, 1, 0, 1024),
 };
 
-int pack_code(const PackCfg &c) { return c.NTL * 100 + c.NTS * 10 + c.P / 256; }
+int pack_code(const PackCfg &c)
+{
+    return c.S * 1000 + c.NTL * 100 + c.NTS * 10 + c.P / 256;
+}
 
 std::atomic<int> g_over_g{-2}, g_over_v{-1}, g_over_c{-1};  // -2: env not read yet
 
@@ -166,7 +174,7 @@ const PackCfg &pick(int V)
             return c;
     for (int G : {128, 256, 64})
         for (const PackCfg &c : kPackCfgs)
-            if (c.G == G && c.G * c.VPT == V && c.NTS == 1 && c.NTL == 0 && c.P == 0)
+            if (c.G == G && c.G * c.VPT == V && c.S == 1 && c.NTS == 1 && c.NTL == 0 && c.P == 0)
                 return c;
     if (V <= 256)
         return kPackCfgs[0];
@@ -214,11 +222,13 @@ hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, cons
     const PackCfg &c = pick(V);
     const bool topk = recv_topk_idx != nullptr || recv_topk_weights != nullptr;
     const int per_block = kPackBlock / c.G;
-    int blocks = (s.T + per_block - 1) / per_block;
+    const int64_t groups = int64_t(s.T) * c.S;
+    int blocks = int((groups + per_block - 1) / per_block);
     if (c.P > 0 && c.P < blocks)
         blocks = c.P;
     hipLaunchKernelGGL(topk ? c.topk : c.plain, dim3(blocks), dim3(kPackBlock), 0, stream,
-                       static_cast<const u32x4 *>(x), s.T, V, s.K, s.E, s.epr, s.kmax, b.dst_row,
+                       static_cast<const u32x4 *>(x), s.T, V, s.K, s.E, s.epr, s.kmax, c.S,
+                       b.dst_row,
                        b.dst_rank, topk_idx, topk_weights, static_cast<u32x4 *>(recv_x),
                        recv_topk_idx, recv_topk_weights);
     return hipGetLastError();

@@ -237,10 +237,11 @@ int ep_pool_trim(void);
 
 /* Launch-shape override for the pack ("dispatch") or the reduce ("combine")
  * kernels, process-wide, for every later call.  Results never depend on it.
- * a = lanes per token G, b = 16-byte vectors per lane VPT, c = a code for
- * the rest: dispatch NTS*10 + P/256, combine U*100 + NTL*10 + P/256, where
+ * a = lanes per group G, b = 16-byte vectors per lane VPT, c = a code for
+ * the rest: dispatch S*1000 + NTL*100 + NTS*10 + P/256, combine S*1000 +
+ * U*100 + NTL*10 + P/256, where S = lane groups per token (row slices),
  * NTS/NTL = nontemporal stores/loads, U = rows in flight and P = persistent
- * block count (0 = one lane group per token).  ep_tuning_list enumerates the
+ * block count (0 = one lane group per token slice).  ep_tuning_list enumerates the
  * compiled-in shapes.  a = b = c = -1 restores the default choice; a shape
  * that is not compiled in returns EP_ERR_INVALID.  The env vars
  * EP_TUNE_DISPATCH="G,VPT,c" and EP_TUNE_COMBINE="G,VPT,c" set the initial
