@@ -33,26 +33,40 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def _configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    p, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.oracle_f32_to_bf16.argtypes = [p, p, i64]
+    lib.oracle_f32_to_bf16.restype = None
+    lib.oracle_layout.argtypes = [i64] * 5 + [p] * 9 + [i64]
+    lib.oracle_layout.restype = i64
+    lib.oracle_dispatch.argtypes = [i64] * 5 + [p] * 8
+    lib.oracle_dispatch.restype = None
+    lib.oracle_combine.argtypes = [i64] * 4 + [p] * 8
+    lib.oracle_combine.restype = None
+    lib.oracle_ll_dispatch.argtypes = [i64] * 6 + [p] * 7
+    lib.oracle_ll_dispatch.restype = ctypes.c_int
+    lib.oracle_ll_combine.argtypes = [i64] * 6 + [p] * 6
+    lib.oracle_ll_combine.restype = ctypes.c_int
+    lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_e4m3_array.argtypes = [p, p, i64]
+    lib.oracle_f32_to_e4m3_array.restype = None
+    lib.oracle_ll_dispatch_fp8.argtypes = [i64] * 6 + [p] * 8
+    lib.oracle_ll_dispatch_fp8.restype = ctypes.c_int
+    lib.oracle_lb_reduce_grads.argtypes = [i64] * 3 + [p] * 3
+    lib.oracle_lb_reduce_grads.restype = None
+    lib.oracle_lb_prefetch_weights.argtypes = [i64] * 3 + [p] * 3
+    lib.oracle_lb_prefetch_weights.restype = None
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
-        p, i64 = ctypes.c_void_p, ctypes.c_int64
-        lib.oracle_f32_to_bf16.argtypes = [p, p, i64]
-        lib.oracle_f32_to_bf16.restype = None
-        lib.oracle_layout.argtypes = [i64] * 5 + [p] * 9 + [i64]
-        lib.oracle_layout.restype = i64
-        lib.oracle_dispatch.argtypes = [i64] * 5 + [p] * 8
-        lib.oracle_dispatch.restype = None
-        lib.oracle_combine.argtypes = [i64] * 4 + [p] * 6
-        lib.oracle_combine.restype = None
-        lib.oracle_ll_dispatch.argtypes = [i64] * 6 + [p] * 6
-        lib.oracle_ll_dispatch.restype = ctypes.c_int
-        lib.oracle_ll_combine.argtypes = [i64] * 6 + [p] * 4
-        lib.oracle_ll_combine.restype = ctypes.c_int
-        _lib = lib
+        _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
 
 
@@ -133,8 +147,10 @@ def dispatch(x: np.ndarray, topk_idx, topk_weights, E: int, R: int, lay: Layout,
     return recv_x, rti, rtw
 
 
-def combine(y: np.ndarray, lay: Layout, recv_topk_weights=None, K: int = 0):
-    """Returns (out bf16 bits [T, H], combined_topk_weights [T, K] or None)."""
+def combine(y: np.ndarray, lay: Layout, recv_topk_weights=None, K: int = 0, bias0=None,
+            bias1=None):
+    """Returns (out bf16 bits [T, H], combined_topk_weights [T, K] or None).
+    bias0 / bias1: optional bf16 bits [T, H] added after the rank sum."""
     y = np.ascontiguousarray(y, dtype=np.uint16)
     T, R = lay.send_head.shape
     H = y.shape[1]
@@ -145,15 +161,28 @@ def combine(y: np.ndarray, lay: Layout, recv_topk_weights=None, K: int = 0):
         rw = np.ascontiguousarray(recv_topk_weights, dtype=np.float32)
         K = rw.shape[1]
         cw = np.empty((T, K), np.float32)
+    b0 = None if bias0 is None else np.ascontiguousarray(bias0, dtype=np.uint16)
+    b1 = None if bias1 is None else np.ascontiguousarray(bias1, dtype=np.uint16)
+    for b in (b0, b1):
+        assert b is None or b.shape == (T, H)
     _load().oracle_combine(T, H, max(K, 1), R, _ptr(y), _ptr(rw), _ptr(lay.rank_prefix_matrix),
-                           _ptr(lay.send_head), _ptr(out), _ptr(cw))
+                           _ptr(lay.send_head), _ptr(b0), _ptr(b1), _ptr(out), _ptr(cw))
     return out, cw
 
 
+def _mask(rank_mask, R):
+    if rank_mask is None:
+        return None
+    m = np.ascontiguousarray(rank_mask, dtype=np.int32)
+    assert m.shape == (R,)
+    return m
+
+
 def ll_dispatch(x: np.ndarray, topk_idx: np.ndarray, E: int, R: int, num_slots: int,
-                with_buf: bool = True):
+                with_buf: bool = True, rank_mask=None):
     """Returns (buf [E/R, R, slots, H] bits or None, counts [E/R, R],
-    src_info [E/R, R, slots], topk_slot [T, K])."""
+    src_info [E/R, R, slots], topk_slot [T, K]).  rank_mask: int32 [R],
+    nonzero = masked rank."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     ti = np.ascontiguousarray(topk_idx, dtype=np.int64)
     T, K = ti.shape
@@ -163,14 +192,18 @@ def ll_dispatch(x: np.ndarray, topk_idx: np.ndarray, E: int, R: int, num_slots: 
     counts = np.empty((epr, R), np.int32)
     src = np.empty((epr, R, num_slots), np.int32)
     ts = np.empty((T, K), np.int32)
-    rc = _load().oracle_ll_dispatch(T, H, K, E, R, num_slots, _ptr(x), _ptr(ti), _ptr(buf),
-                                    _ptr(counts), _ptr(src), _ptr(ts))
+    m = _mask(rank_mask, R)
+    rc = _load().oracle_ll_dispatch(T, H, K, E, R, num_slots, _ptr(x), _ptr(ti), _ptr(m),
+                                    _ptr(buf), _ptr(counts), _ptr(src), _ptr(ts))
     if rc != 0:
         raise ValueError("oracle_ll_dispatch rejected its arguments")
     return buf, counts, src, ts
 
 
-def ll_combine(buf: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray, E: int, R: int):
+def ll_combine(buf: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray, E: int, R: int,
+               rank_mask=None, combine_mask=None):
+    """rank_mask: the mask the dispatch used (slots); combine_mask: ranks
+    masked at combine time (skipped)."""
     buf = np.ascontiguousarray(buf, dtype=np.uint16)
     epr, R2, num_slots, H = buf.shape
     assert R2 == R and epr == E // R
@@ -178,8 +211,67 @@ def ll_combine(buf: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray, 
     tw = np.ascontiguousarray(topk_weights, dtype=np.float32)
     T, K = ti.shape
     out = np.empty((T, H), np.uint16)
+    m = _mask(rank_mask, R)
+    cm = _mask(combine_mask, R)
     rc = _load().oracle_ll_combine(T, H, K, E, R, num_slots, _ptr(buf), _ptr(ti), _ptr(tw),
-                                   _ptr(out))
+                                   _ptr(m), _ptr(cm), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_ll_combine rejected its arguments")
     return out
+
+
+def e4m3_to_f32(code: int) -> float:
+    return float(_load().oracle_e4m3_to_f32(int(code)))
+
+
+def f32_to_e4m3(f: np.ndarray) -> np.ndarray:
+    """fp32 -> FP8 E4M3 codes, round to nearest even, saturating at +-448."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, dtype=np.uint8)
+    _load().oracle_f32_to_e4m3_array(_ptr(f), _ptr(out), f.size)
+    return out
+
+
+def ll_dispatch_fp8(x: np.ndarray, topk_idx: np.ndarray, E: int, R: int, num_slots: int,
+                    rank_mask=None):
+    """Returns (q [E/R, R, slots, H] uint8, scale [E/R, R, slots, H/128] fp32,
+    counts, src_info, topk_slot).  Unused cells of q / scale are zero."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    ti = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    T, K = ti.shape
+    H = x.shape[1]
+    epr = E // R
+    q = np.zeros((epr, R, num_slots, H), np.uint8)
+    sc = np.zeros((epr, R, num_slots, H // 128), np.float32)
+    counts = np.empty((epr, R), np.int32)
+    src = np.empty((epr, R, num_slots), np.int32)
+    ts = np.empty((T, K), np.int32)
+    m = _mask(rank_mask, R)
+    rc = _load().oracle_ll_dispatch_fp8(T, H, K, E, R, num_slots, _ptr(x), _ptr(ti), _ptr(m),
+                                        _ptr(q), _ptr(sc), _ptr(counts), _ptr(src), _ptr(ts))
+    if rc != 0:
+        raise ValueError("oracle_ll_dispatch_fp8 rejected its arguments")
+    return q, sc, counts, src, ts
+
+
+def lb_reduce_grads(redundant_grads: np.ndarray, expert_grads: np.ndarray,
+                    mapping: np.ndarray) -> np.ndarray:
+    """Returns new expert gradients (bf16 bits [E, P]); the input is not changed."""
+    rg = np.ascontiguousarray(redundant_grads, dtype=np.uint16)
+    eg = np.array(expert_grads, dtype=np.uint16, copy=True, order="C")
+    mp = np.ascontiguousarray(mapping, dtype=np.int64)
+    assert rg.shape == (len(mp), eg.shape[1])
+    _load().oracle_lb_reduce_grads(len(mp), eg.shape[0], eg.shape[1], _ptr(rg), _ptr(eg), _ptr(mp))
+    return eg
+
+
+def lb_prefetch_weights(expert_weights: np.ndarray, redundant_weights: np.ndarray,
+                        mapping: np.ndarray) -> np.ndarray:
+    """Returns new replica weights (bf16 bits [n_rep, P])."""
+    ew = np.ascontiguousarray(expert_weights, dtype=np.uint16)
+    rw = np.array(redundant_weights, dtype=np.uint16, copy=True, order="C")
+    mp = np.ascontiguousarray(mapping, dtype=np.int64)
+    assert rw.shape == (len(mp), ew.shape[1])
+    _load().oracle_lb_prefetch_weights(len(mp), ew.shape[0], ew.shape[1], _ptr(ew), _ptr(rw),
+                                       _ptr(mp))
+    return rw

@@ -17,6 +17,8 @@
  *   [P4] "How DeepEP Optimizes Handle Reuse for Repeated Dispatches",
  *        sections "What the Handle Contains" and "Fast Path Dispatch with
  *        Handle Reuse".
+ *   [P5] "Chapter 10, V2: buffers beyond EP" (bowenzhou.top), section 10.2
+ *        (lb_prefetch_weights / lb_reduce_grads with a redundancy mapping).
  * Where the pages leave a step open, the reading taken is stated next to the
  * code as "reading:".
  *
@@ -225,12 +227,16 @@ void oracle_dispatch(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R,
  *               f32(y[S[r] + send_head[t][r]][h]) )
  * The sum is sequential fp32 starting from +0 (reading: ascending rank order,
  * fp32 accumulation).  A token that hit no rank gets +0.
+ * Bias terms ([P1] "Combine Operation" names them without a formula):
+ * reading: bias0 then bias1, bf16 [T][H] each, nullable, added in fp32 after
+ * the rank sum and before the single rounding to bf16.
  * The optional weight output is the same reduction of recv_topk_weights,
  * kept in fp32 (the reduced weights the pages' combine returns).
  */
 void oracle_combine(int64_t T, int64_t H, int64_t K, int64_t R,
                     const uint16_t *y, const float *recv_topk_weights,
                     const int32_t *rank_prefix_matrix, const int32_t *send_head,
+                    const uint16_t *bias0, const uint16_t *bias1,
                     uint16_t *out, float *combined_topk_weights)
 {
     float *acc = (float *)malloc((size_t)(H > 0 ? H : 1) * sizeof(float));
@@ -245,6 +251,12 @@ void oracle_combine(int64_t T, int64_t H, int64_t K, int64_t R,
             for (int64_t h = 0; h < H; ++h)
                 acc[h] += bf16_to_f32(y[row * H + h]);
         }
+        if (bias0 != NULL)
+            for (int64_t h = 0; h < H; ++h)
+                acc[h] += bf16_to_f32(bias0[t * H + h]);
+        if (bias1 != NULL)
+            for (int64_t h = 0; h < H; ++h)
+                acc[h] += bf16_to_f32(bias1[t * H + h]);
         for (int64_t h = 0; h < H; ++h)
             out[t * H + h] = f32_to_bf16_rne(acc[h]);
 
@@ -267,18 +279,32 @@ void oracle_combine(int64_t T, int64_t H, int64_t K, int64_t R,
 
 /* ------------------------------------------------------------ low latency --- */
 
+/* Is pair (t, k) sent?  Its slot must be valid, and its expert's rank must
+ * not be masked.  [P1] "Dynamic Rank Masking": a masked rank (mask value 1)
+ * stops taking part without tearing the context down; reading: its pairs are
+ * treated exactly like masked slots (not sent, not counted, not combined).
+ * rank_mask may be NULL (no rank masked). */
+static int ll_live(int64_t e, int64_t E, int64_t epr, const int32_t *rank_mask)
+{
+    if (e < 0 || e >= E)
+        return 0;
+    if (rank_mask != NULL && rank_mask[e / epr] != 0)
+        return 0;
+    return 1;
+}
+
 /* Slot of (t, k) inside its expert's receive area: the number of earlier
- * (t', k') pairs, in (token, slot) order, that name the same expert.
+ * live (t', k') pairs, in (token, slot) order, that name the same expert.
  * Reading: the pages leave the order open; token order is taken. */
-static void ll_slots(int64_t T, int64_t K, int64_t E, const int64_t *topk_idx, int32_t *slot,
-                     int32_t *count)
+static void ll_slots(int64_t T, int64_t K, int64_t E, int64_t epr, const int32_t *rank_mask,
+                     const int64_t *topk_idx, int32_t *slot, int32_t *count)
 {
     for (int64_t e = 0; e < E; ++e)
         count[e] = 0;
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t k = 0; k < K; ++k) {
             int64_t e = topk_idx[t * K + k];
-            if (e < 0 || e >= E) {
+            if (!ll_live(e, E, epr, rank_mask)) {
                 slot[t * K + k] = -1;
                 continue;
             }
@@ -300,14 +326,14 @@ static void ll_slots(int64_t T, int64_t K, int64_t E, const int64_t *topk_idx, i
  * Returns 0, or -1 on invalid arguments.
  */
 int oracle_ll_dispatch(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R, int64_t num_slots,
-                       const uint16_t *x, const int64_t *topk_idx, uint16_t *buf,
-                       int32_t *counts, int32_t *src_info, int32_t *topk_slot)
+                       const uint16_t *x, const int64_t *topk_idx, const int32_t *rank_mask,
+                       uint16_t *buf, int32_t *counts, int32_t *src_info, int32_t *topk_slot)
 {
     if (E % R != 0 || num_slots < 1)
         return -1;
     int64_t epr = E / R;
     int32_t *cnt = (int32_t *)malloc((size_t)E * sizeof(int32_t));
-    ll_slots(T, K, E, topk_idx, topk_slot, cnt);
+    ll_slots(T, K, E, epr, rank_mask, topk_idx, topk_slot, cnt);
     for (int64_t i = 0; i < epr * R * num_slots; ++i)
         src_info[i] = -1;
     for (int64_t e = 0; e < E; ++e)
@@ -339,11 +365,14 @@ int oracle_ll_dispatch(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R, in
  *   out[t][h] = bf16_rne( acc ),  acc = fma(w[t][k], f32(buf[cell(t,k)][h]), acc)
  * over k ascending, valid in-capacity slots only, from acc = +0 (reading: the
  * pages give no order; ascending slot with a fused multiply-add is taken).
- * The slots are recomputed here from topk_idx by the definition above.
+ * The slots are recomputed here from topk_idx by the definition above, with
+ * the rank mask the dispatch used (rank_mask).  combine_mask (nullable) masks
+ * ranks at combine time: their pairs contribute nothing, whatever the
+ * dispatch did (a rank that failed after the dispatch).
  */
 int oracle_ll_combine(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R, int64_t num_slots,
                       const uint16_t *buf, const int64_t *topk_idx, const float *topk_weights,
-                      uint16_t *out)
+                      const int32_t *rank_mask, const int32_t *combine_mask, uint16_t *out)
 {
     if (E % R != 0 || num_slots < 1)
         return -1;
@@ -351,7 +380,7 @@ int oracle_ll_combine(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R, int
     int32_t *slot = (int32_t *)malloc((size_t)(T * K > 0 ? T * K : 1) * sizeof(int32_t));
     int32_t *cnt = (int32_t *)malloc((size_t)E * sizeof(int32_t));
     float *acc = (float *)malloc((size_t)(H > 0 ? H : 1) * sizeof(float));
-    ll_slots(T, K, E, topk_idx, slot, cnt);
+    ll_slots(T, K, E, epr, rank_mask, topk_idx, slot, cnt);
     for (int64_t t = 0; t < T; ++t) {
         for (int64_t h = 0; h < H; ++h)
             acc[h] = 0.0f;
@@ -359,6 +388,8 @@ int oracle_ll_combine(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R, int
             int64_t e = topk_idx[t * K + k];
             int64_t s = slot[t * K + k];
             if (e < 0 || s < 0 || s >= num_slots)
+                continue;
+            if (combine_mask != NULL && combine_mask[e / epr] != 0)
                 continue;
             float w = topk_weights[t * K + k];
             int64_t cell = ((e % epr) * R + e / epr) * num_slots + s;
@@ -372,4 +403,150 @@ int oracle_ll_combine(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R, int
     free(cnt);
     free(slot);
     return 0;
+}
+
+/* ------------------------------------------------------------------ FP8 --- */
+
+/* OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits, no infinities, 0x7F / 0xFF are NaN, largest finite 448 = 1.75 * 2^8,
+ * smallest normal 2^-6, subnormals m * 2^-9 (m = 1..7). */
+float oracle_e4m3_to_f32(uint8_t c)
+{
+    int sign = c >> 7, ex = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (ex == 15 && m == 7)
+        return NAN;
+    if (ex == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, ex - 7);
+    return (float)(sign ? -v : v);
+}
+
+/* Round to nearest, ties to even, saturating at +-448 (the finite range is
+ * what a scaled activation needs; there is no infinity to round to). */
+uint8_t oracle_f32_to_e4m3(float f)
+{
+    if (isnan(f))
+        return 0x7F;
+    uint8_t sign = signbit(f) ? 0x80 : 0;
+    double a = fabs((double)f);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        double q = rint(a * 512.0); /* units of 2^-9; 8 is the smallest normal */
+        return sign | (uint8_t)q;
+    }
+    int e;
+    double fr = frexp(a, &e); /* a = fr * 2^e, fr in [0.5, 1) */
+    e -= 1;                   /* a = (2 fr) * 2^e, 2 fr in [1, 2) */
+    double mi = rint((2.0 * fr - 1.0) * 8.0);
+    if (mi == 8.0) {
+        mi = 0.0;
+        e += 1;
+    }
+    int code = ((e + 7) << 3) | (int)mi;
+    if (code > 0x7E)
+        code = 0x7E;
+    return sign | (uint8_t)code;
+}
+
+void oracle_f32_to_e4m3_array(const float *in, uint8_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_e4m3(in[i]);
+}
+
+/*
+ * Low-latency dispatch with FP8 payload ([P1] "IB-GDA Kernels": FP8 when
+ * use_fp8 is set; the pages' code example sets it on the dispatch).  Slots,
+ * counts, src_info and topk_slot are those of oracle_ll_dispatch.  Each sent
+ * row is cut into blocks of 128 elements; per block (reading, the pages give
+ * no recipe):
+ *   amax  = max(max |x|, 1e-4)               (fp32)
+ *   sinv  = 448 / amax                        (fp32 division)
+ *   q[h]  = e4m3_rne_sat(x[h] * sinv)         (fp32 product, then rounding)
+ *   scale = amax / 448                        (fp32 division; x ~ q * scale)
+ * packed_q [E/R][R][slots][H] bytes, packed_scale [E/R][R][slots][H/128].
+ * Requires H % 128 == 0.  Returns 0, or -1 on invalid arguments.
+ */
+int oracle_ll_dispatch_fp8(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R,
+                           int64_t num_slots, const uint16_t *x, const int64_t *topk_idx,
+                           const int32_t *rank_mask, uint8_t *packed_q, float *packed_scale,
+                           int32_t *counts, int32_t *src_info, int32_t *topk_slot)
+{
+    if (H % 128 != 0)
+        return -1;
+    int rc = oracle_ll_dispatch(T, H, K, E, R, num_slots, x, topk_idx, rank_mask, NULL, counts,
+                                src_info, topk_slot);
+    if (rc != 0)
+        return rc;
+    int64_t epr = E / R, nb = H / 128;
+    for (int64_t cell = 0; cell < epr * R * num_slots; ++cell) {
+        int32_t t = src_info[cell];
+        if (t < 0)
+            continue;
+        for (int64_t b = 0; b < nb; ++b) {
+            float amax = 0.0f;
+            for (int64_t h = b * 128; h < (b + 1) * 128; ++h) {
+                float v = fabsf(bf16_to_f32(x[t * H + h]));
+                if (v > amax)
+                    amax = v;
+            }
+            if (amax < 1e-4f)
+                amax = 1e-4f;
+            float sinv = 448.0f / amax;
+            packed_scale[cell * nb + b] = amax / 448.0f;
+            for (int64_t h = b * 128; h < (b + 1) * 128; ++h)
+                packed_q[cell * H + h] = oracle_f32_to_e4m3(bf16_to_f32(x[t * H + h]) * sinv);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------- load balancing --- */
+
+/*
+ * [P5] 10.2: lb_reduce_grads folds the gradients of redundant expert
+ * replicas back into the experts they copy, following redundancy_mapping
+ * (replica j copies expert mapping[j]).  Reading: bf16 gradients, fp32
+ * accumulation starting from the expert's own gradient, replicas added in
+ * ascending j, one rounding to bf16; experts with no replica are untouched;
+ * mapping entries outside [0, E) are ignored.
+ *   expert_grads [E][P] (in/out), redundant_grads [n_rep][P].
+ */
+void oracle_lb_reduce_grads(int64_t n_rep, int64_t E, int64_t P, const uint16_t *redundant_grads,
+                            uint16_t *expert_grads, const int64_t *mapping)
+{
+    float *acc = (float *)malloc((size_t)(P > 0 ? P : 1) * sizeof(float));
+    for (int64_t e = 0; e < E; ++e) {
+        int any = 0;
+        for (int64_t j = 0; j < n_rep; ++j)
+            any |= mapping[j] == e;
+        if (!any)
+            continue;
+        for (int64_t p = 0; p < P; ++p)
+            acc[p] = bf16_to_f32(expert_grads[e * P + p]);
+        for (int64_t j = 0; j < n_rep; ++j)
+            if (mapping[j] == e)
+                for (int64_t p = 0; p < P; ++p)
+                    acc[p] += bf16_to_f32(redundant_grads[j * P + p]);
+        for (int64_t p = 0; p < P; ++p)
+            expert_grads[e * P + p] = f32_to_bf16_rne(acc[p]);
+    }
+    free(acc);
+}
+
+/* [P5] 10.2: lb_prefetch_weights copies each expert's weights into its
+ * replicas' slots before the expert computation: redundant[j] =
+ * expert[mapping[j]]; replicas with an invalid mapping entry are untouched. */
+void oracle_lb_prefetch_weights(int64_t n_rep, int64_t E, int64_t P, const uint16_t *expert_weights,
+                                uint16_t *redundant_weights, const int64_t *mapping)
+{
+    for (int64_t j = 0; j < n_rep; ++j) {
+        int64_t e = mapping[j];
+        if (e < 0 || e >= E)
+            continue;
+        memcpy(redundant_weights + j * P, expert_weights + e * P, (size_t)P * sizeof(uint16_t));
+    }
 }

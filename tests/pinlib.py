@@ -419,3 +419,291 @@ def check_bf16_edges():
     u = np.array(list(cases.keys()), np.uint32)
     got = O.f32_to_bf16(u.view(np.float32))
     np.testing.assert_array_equal(got, np.array(list(cases.values()), np.uint16))
+
+
+# ------------------------------------------------------------ rank masking
+
+
+def masked_topk(topk_idx, E, R, rank_mask):
+    """topk_idx with every slot whose expert sits on a masked rank set to -1."""
+    epr = E // R
+    idx = topk_idx.copy()
+    ranks = np.where(idx >= 0, idx // epr, 0)
+    idx[(idx >= 0) & (np.asarray(rank_mask)[ranks] != 0)] = -1
+    return idx
+
+
+def check_ll_rank_mask(inp, rank_mask):
+    """Masking a rank is the same as masking every slot that names one of its
+    experts: counts, slots, src_info, rows and the combine all agree."""
+    E, R, S = inp.E, inp.R, inp.slots
+    m = np.asarray(rank_mask, np.int32)
+    a = O.ll_dispatch(inp.x, inp.topk_idx, E, R, S, rank_mask=m)
+    idx2 = masked_topk(inp.topk_idx, E, R, m)
+    b = O.ll_dispatch(inp.x, idx2, E, R, S)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    out_a = O.ll_combine(a[0], inp.topk_idx, inp.topk_weights, E, R, rank_mask=m)
+    out_b = O.ll_combine(b[0], idx2, inp.topk_weights, E, R)
+    np.testing.assert_array_equal(out_a, out_b)
+    # masked ranks receive nothing
+    epr = E // R
+    for r in np.nonzero(m)[0]:
+        assert np.all(a[1][:, r] == 0) and np.all(a[2][:, r] == -1)
+    # a rank masked only at combine time drops exactly its pairs' terms
+    out_c = O.ll_combine(b[0], idx2, inp.topk_weights, E, R, combine_mask=m)
+    np.testing.assert_array_equal(out_c, out_b)
+    full = O.ll_dispatch(inp.x, inp.topk_idx, E, R, S)
+    out_d = O.ll_combine(full[0], inp.topk_idx, inp.topk_weights, E, R, combine_mask=m)
+    w2 = np.where(idx2 >= 0, inp.topk_weights, np.float32(0))
+    out_e = O.ll_combine(full[0], inp.topk_idx, w2, E, R)
+    np.testing.assert_array_equal(f32_from_bits(out_d), f32_from_bits(out_e))
+    return a
+
+
+def check_ll_mask_extremes(inp):
+    E, R, S = inp.E, inp.R, inp.slots
+    none = O.ll_dispatch(inp.x, inp.topk_idx, E, R, S, rank_mask=np.zeros(R, np.int32))
+    plain = O.ll_dispatch(inp.x, inp.topk_idx, E, R, S)
+    for u, v in zip(none, plain):
+        np.testing.assert_array_equal(u, v)
+    allm = O.ll_dispatch(inp.x, inp.topk_idx, E, R, S, rank_mask=np.ones(R, np.int32))
+    assert np.all(allm[1] == 0) and np.all(allm[2] == -1) and np.all(allm[3] == -1)
+    out = O.ll_combine(allm[0], inp.topk_idx, inp.topk_weights, E, R, rank_mask=np.ones(R, np.int32))
+    assert np.all((out & 0x7FFF) == 0)
+
+
+# -------------------------------------------------------------- combine bias
+
+
+def check_combine_bias(seed=0, T=96, H=40, E=24, K=4, R=6, C=3):
+    inp = random_case(seed, T, H, E, K, R, C, mask=0.2)
+    L = O.layout(inp.topk_idx, E, R, C)
+    rng = np.random.default_rng(seed + 21)
+    y = (rng.standard_normal((L.num_recv, H)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    zero = np.zeros((T, H), np.uint16)
+    a, _ = O.combine(y, L)
+    b, _ = O.combine(y, L, bias0=zero, bias1=zero)
+    np.testing.assert_array_equal(f32_from_bits(a), f32_from_bits(b))  # +0 bias changes nothing
+    # zero rows: the output is the bias sum, exact for small integers
+    b0 = rng.integers(-20, 21, (T, H)).astype(np.float32)
+    b1 = rng.integers(-20, 21, (T, H)).astype(np.float32)
+    out, _ = O.combine(np.zeros_like(y), L, bias0=bits_from_f32_exact(b0),
+                       bias1=bits_from_f32_exact(b1))
+    np.testing.assert_array_equal(f32_from_bits(out), b0 + b1)
+    # integer rows and integer biases: exact total
+    yi = rng.integers(-8, 9, (L.num_recv, H)).astype(np.float32)
+    out, _ = O.combine(bits_from_f32_exact(yi), L, bias0=bits_from_f32_exact(b0))
+    exp = b0.copy()
+    for r in range(R):
+        S = L.rank_prefix_matrix[r - 1] if r > 0 else 0
+        ts = np.nonzero(L.send_head[:, r] >= 0)[0]
+        exp[ts] += yi[S + L.send_head[ts, r]]
+    np.testing.assert_array_equal(f32_from_bits(out), exp)
+    # only bias1 given: the same as bias0 alone with those values
+    o1, _ = O.combine(y, L, bias1=bits_from_f32_exact(b1))
+    o0, _ = O.combine(y, L, bias0=bits_from_f32_exact(b1))
+    np.testing.assert_array_equal(f32_from_bits(o1), f32_from_bits(o0))
+
+
+# ------------------------------------------------------------ load balancing
+
+
+def check_lb_ops(seed=0, E=12, n_rep=7, P=37):
+    rng = np.random.default_rng(seed)
+    mapping = rng.integers(-1, E, n_rep).astype(np.int64)
+    mapping[0] = E + 3  # an invalid entry is ignored
+    ew = rng.integers(-30, 31, (E, P)).astype(np.float32)
+    rg = rng.integers(-30, 31, (n_rep, P)).astype(np.float32)
+    # reduce: small integers sum exactly; replicas in any order give the same
+    out = f32_from_bits(O.lb_reduce_grads(bits_from_f32_exact(rg), bits_from_f32_exact(ew), mapping))
+    exp = ew.copy()
+    for j in range(n_rep):
+        if 0 <= mapping[j] < E:
+            exp[mapping[j]] += rg[j]
+    np.testing.assert_array_equal(out, exp)
+    # zero replica gradients leave every expert bitwise unchanged (even -0)
+    egb = (rng.standard_normal((E, P)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out0 = O.lb_reduce_grads(np.zeros((n_rep, P), np.uint16), egb, mapping)
+    np.testing.assert_array_equal(f32_from_bits(out0), f32_from_bits(egb))
+    # fp64 bound on random values: n terms summed in fp32 then rounded once
+    rgb = (rng.standard_normal((n_rep, P)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    got = f32_from_bits(O.lb_reduce_grads(rgb, egb, mapping)).astype(np.float64)
+    ex = f32_from_bits(egb).astype(np.float64)
+    ab = np.abs(ex).copy()
+    cnt = np.ones(E)
+    for j in range(n_rep):
+        if 0 <= mapping[j] < E:
+            v = f32_from_bits(rgb[j]).astype(np.float64)
+            ex[mapping[j]] += v
+            ab[mapping[j]] += np.abs(v)
+            cnt[mapping[j]] += 1
+    err = np.abs(got - ex)
+    bound = (cnt[:, None] - 1) * 2.0 ** -24 * ab * 1.0001 + 0.5 * _bf16_ulp(np.maximum(np.abs(got), np.abs(ex)))
+    assert np.all(err <= bound)
+    # prefetch copies each replica's source row; invalid entries stay as they were
+    rw0 = rng.integers(0, 65535, (n_rep, P)).astype(np.uint16)
+    rw = O.lb_prefetch_weights(egb, rw0, mapping)
+    for j in range(n_rep):
+        if 0 <= mapping[j] < E:
+            np.testing.assert_array_equal(rw[j], egb[mapping[j]])
+        else:
+            np.testing.assert_array_equal(rw[j], rw0[j])
+    # prefetch then reduce of the copied values doubles each replicated row
+    once = np.bincount(mapping[(mapping >= 0) & (mapping < E)], minlength=E)
+    ewi = rng.integers(-30, 31, (E, P)).astype(np.float32)
+    rwi = O.lb_prefetch_weights(bits_from_f32_exact(ewi), np.zeros((n_rep, P), np.uint16), mapping)
+    red = f32_from_bits(O.lb_reduce_grads(rwi, bits_from_f32_exact(ewi), mapping))
+    np.testing.assert_array_equal(red, ewi * (1 + once)[:, None])
+
+
+# ---------------------------------------------------------------------- FP8
+
+
+def e4m3_table():
+    """The 256 codes decoded from the format definition (sign, 4-bit exponent
+    with bias 7, 3-bit mantissa, subnormals at exponent 0, 0x7F/0xFF NaN)."""
+    vals = np.empty(256, np.float64)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        ex, m = (c >> 3) & 15, c & 7
+        if ex == 15 and m == 7:
+            vals[c] = np.nan
+        elif ex == 0:
+            vals[c] = s * m * 2.0 ** -9
+        else:
+            vals[c] = s * (1 + m / 8) * 2.0 ** (ex - 7)
+    return vals
+
+
+def brute_e4m3(f):
+    """Nearest finite code by exhaustive search; ties go to the even code
+    (mantissa lsb 0); values beyond 448 saturate; sign of zero kept."""
+    vals = e4m3_table()
+    out = np.empty(f.shape, np.uint8)
+    fin = np.arange(256)[~np.isnan(vals)]
+    for i, v in enumerate(np.asarray(f, np.float64).ravel()):
+        if np.isnan(v):
+            out.flat[i] = 0x7F
+            continue
+        v2 = min(max(v, -448.0), 448.0)
+        d = np.abs(vals[fin] - v2)
+        best = fin[d == d.min()]
+        if len(best) > 1:
+            best = best[(best & 1) == 0]
+            if len(best) > 1:  # +0 / -0: keep the sign of the input
+                best = best[(best & 0x80) == (0x80 if np.signbit(v) else 0)]
+        out.flat[i] = best[0]
+    return out
+
+
+def check_e4m3(seed=0):
+    vals = e4m3_table()
+    for c in range(256):
+        got = O.e4m3_to_f32(c)
+        assert (np.isnan(got) and np.isnan(vals[c])) or got == vals[c], c
+    # torch's own float8_e4m3fn decoding agrees with the format definition
+    tv = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    ok = ~np.isnan(vals)
+    np.testing.assert_array_equal(tv[ok], vals[ok].astype(np.float32))
+    # every code, every midpoint between neighbours (ties), and points next to them
+    fin = np.sort(np.unique(vals[~np.isnan(vals)]))
+    mids = (fin[:-1] + fin[1:]) / 2
+    pts = np.concatenate([fin, mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                          np.nextafter(mids.astype(np.float32), np.float32(-np.inf)),
+                          [449.0, 463.9, 464.0, 465.0, 1e6, -1e6, 1e-12, -1e-12, -0.0]])
+    rng = np.random.default_rng(seed)
+    rnd = (rng.standard_normal(20000) * np.exp(rng.uniform(-12, 6, 20000))).astype(np.float32)
+    pts = np.concatenate([pts.astype(np.float32), rnd])
+    np.testing.assert_array_equal(O.f32_to_e4m3(pts), brute_e4m3(pts))
+    # torch's rounding conversion agrees inside the finite range
+    inr = pts[np.abs(pts) <= 448]
+    tq = torch.from_numpy(inr).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.f32_to_e4m3(inr), tq)
+
+
+def check_ll_fp8(inp, rank_mask=None):
+    """Metadata equals the bf16 dispatch's; each block's scale is amax/448
+    (amax clamped at 1e-4); every code is the rounding of x * (448/amax); and
+    dequantized rows are within half an e4m3 step (times the scale) of x."""
+    E, R, S = inp.E, inp.R, inp.slots
+    q, sc, cnt, src, ts = O.ll_dispatch_fp8(inp.x, inp.topk_idx, E, R, S, rank_mask=rank_mask)
+    _, cnt2, src2, ts2 = O.ll_dispatch(inp.x, inp.topk_idx, E, R, S, with_buf=False,
+                                       rank_mask=rank_mask)
+    np.testing.assert_array_equal(cnt, cnt2)
+    np.testing.assert_array_equal(src, src2)
+    np.testing.assert_array_equal(ts, ts2)
+    H = inp.x.shape[1]
+    vals = e4m3_table()
+    used = src >= 0
+    xs = f32_from_bits(inp.x)[src[used]]                     # [n, H]
+    qs = q[used].astype(np.int64)
+    ss = sc[used]                                            # [n, H/128]
+    blocks = xs.reshape(len(xs), H // 128, 128)
+    amax = np.maximum(np.abs(blocks).max(axis=2), np.float32(1e-4)).astype(np.float32)
+    np.testing.assert_array_equal(ss, (amax / np.float32(448.0)).astype(np.float32))
+    sinv = (np.float32(448.0) / amax).astype(np.float32)
+    scaled = (blocks * sinv[:, :, None]).astype(np.float32)
+    np.testing.assert_array_equal(qs.reshape(scaled.shape), O.f32_to_e4m3(scaled).astype(np.int64))
+    deq = vals[qs].reshape(scaled.shape) * ss[:, :, None]
+    # half a step of e4m3 around the scaled value: step = 2^(e-3) for normals, 2^-9 below
+    a = np.maximum(np.abs(scaled.astype(np.float64)), 2.0 ** -6)
+    step = 2.0 ** (np.floor(np.log2(a)) - 3)
+    err = np.abs(deq - blocks)
+    assert np.all(err <= (0.5 * step + 1e-6 * a) * ss[:, :, None] * 1.0001 + 1e-30)
+    assert np.all(q[~used] == 0)
+    return q, sc
+
+
+# -------------------------------------------------------- exact tie rounding
+
+
+def check_tie_rounding():
+    """Sums that land exactly on a bf16 tie (halfway between neighbours) must
+    round to the even neighbour; any perturbation of the sum (a scaled term, a
+    lost term, a different rounding) moves it off the tie and flips the
+    result.  Every term and partial sum here is exact in fp32."""
+    # normal combine: token 0 sends to ranks 0 and 1 of R=2 (experts 0, 1)
+    idx = np.array([[0, 1], [1, -1], [-1, -1]], np.int64)
+    L = O.layout(idx, 2, 2, 1)
+    rows = np.array([[1.0, 1.0, -3.0, 256.0],             # row of (token 0, rank 0)
+                     [2.0 ** -8, 3 * 2.0 ** -8, -2.0 ** -7 * 3, 1.0],  # (token 0, rank 1)
+                     [1.0 + 2.0 ** -7, 0.0, 0.0, 0.0]], np.float32)    # (token 1, rank 1)
+    # rows are in segment order: rank 0 = [t0], rank 1 = [t0, t1]
+    out, _ = O.combine(bits_from_f32_exact(rows), L)
+    got = f32_from_bits(out)
+    # 1 + 2^-8: tie between 1 and 1 + 2^-7 -> even 1;  1 + 3*2^-8: tie -> even 1 + 2^-6
+    # -3 - 3*2^-7 = -3.0234375: tie between -3.015625 (odd mantissa) and -3.03125 (even) ->
+    # -3.03125;  256 + 1: tie between 256 (even) and 258 -> 256
+    np.testing.assert_array_equal(got[0], np.array([1.0, 1.0 + 2.0 ** -6, -3.03125, 256.0], np.float32))
+    np.testing.assert_array_equal(got[1], rows[2])
+    # LL combine: one token, experts 0, 1, 2 on one rank, one slot each
+    idx = np.array([[0, 1, 2]], np.int64)
+    w = np.array([[0.5, 0.5, 0.0]], np.float32)
+    b = np.zeros((3, 1, 1, 8), np.float32)
+    b[1, 0, 0, 0] = 1.0
+    # 0.5 * (1 + 2^-7) + 0.5 * 1 = 1 + 2^-8: a tie -> even 1.0
+    b[0, 0, 0, 0] = 1.0 + 2.0 ** -7
+    out = f32_from_bits(O.ll_combine(bits_from_f32_exact(b), idx, w, 3, 1))
+    assert out[0, 0] == np.float32(1.0)
+    # 0.5 * (1 + 3*2^-7) + 0.5 = 1 + 3*2^-8: a tie between 1 + 2^-7 and 1 + 2^-6 -> even 1 + 2^-6
+    b[0, 0, 0, 0] = 1.0 + 3 * 2.0 ** -7
+    out = f32_from_bits(O.ll_combine(bits_from_f32_exact(b), idx, w, 3, 1))
+    assert out[0, 0] == np.float32(1.0 + 2.0 ** -6)
+    # lb_reduce_grads: the same two ties
+    eg = bits_from_f32_exact(np.array([[1.0, -3.0]], np.float32))
+    rg = bits_from_f32_exact(np.array([[2.0 ** -8, -3 * 2.0 ** -7]], np.float32))
+    got = f32_from_bits(O.lb_reduce_grads(rg, eg, np.array([0], np.int64)))
+    np.testing.assert_array_equal(got, np.array([[1.0, -3.03125]], np.float32))
+
+
+def fp8_edge_case(seed=4):
+    """A decode batch whose rows hold an all-zero block and a block of values
+    far below the amax floor, next to ordinary blocks."""
+    inp = random_case(seed, 40, 256, 16, 4, 4, 1, mask=0.2, slots=40)
+    x = inp.x.copy()
+    x[0, :128] = 0
+    x[1, 128:] = bits_from_f32_exact(np.full(128, 2.0 ** -20, np.float32))
+    x[2, :64] = 0x8000  # -0
+    inp.x = x
+    return inp

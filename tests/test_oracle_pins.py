@@ -1,5 +1,6 @@
 """The CPU oracle against its pins (no GPU needed)."""
 
+import numpy as np
 import pytest
 
 import pinlib
@@ -86,3 +87,54 @@ def test_bf16_edges():
 
 def test_bf16_all_fp32_patterns():
     pinlib.check_bf16_patterns(step=1)
+
+
+# ------------------------------------------------------------------- NEXT rows
+
+
+def test_ll_rank_mask_config3():
+    inp = config_inputs(3)
+    m = np.zeros(inp.R, np.int32)
+    m[[3, 17, 31]] = 1
+    pinlib.check_ll_rank_mask(inp, m)
+
+
+def test_ll_rank_mask_random():
+    inp = random_case(8, 50, 24, 16, 4, 8, 1, mask=0.1, dup=0.3, slots=60)
+    pinlib.check_ll_rank_mask(inp, np.array([0, 1, 0, 0, 1, 1, 0, 0], np.int32))
+
+
+def test_ll_rank_mask_extremes():
+    pinlib.check_ll_mask_extremes(random_case(9, 30, 16, 8, 3, 4, 1, slots=30))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_combine_bias(seed):
+    pinlib.check_combine_bias(seed)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_lb_ops(seed):
+    pinlib.check_lb_ops(seed)
+
+
+def test_e4m3_rounding():
+    pinlib.check_e4m3()
+
+
+def test_ll_fp8_config3_shape():
+    inp = config_inputs(3)
+    pinlib.check_ll_fp8(inp)
+
+
+def test_ll_fp8_masked_small():
+    inp = random_case(4, 40, 256, 16, 4, 4, 1, mask=0.2, slots=40)
+    pinlib.check_ll_fp8(inp, rank_mask=np.array([0, 1, 0, 0], np.int32))
+
+
+def test_tie_rounding():
+    pinlib.check_tie_rounding()
+
+
+def test_ll_fp8_zero_and_tiny_blocks():
+    pinlib.check_ll_fp8(pinlib.fp8_edge_case())
