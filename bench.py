@@ -184,14 +184,15 @@ def main():
         abi.check(L.ep_dispatch(ctypes.byref(d), P(x2), None, None, ctypes.byref(h), P(recv_x2),
                                 None, None, cap, None, s), "cached dispatch")
         mark(3)
-        abi.check(L.ep_combine(h, H, P(recv_x), cap, P(rtw), P(out), P(cw), s), "combine")
+        abi.check(L.ep_combine(h, H, P(recv_x), cap, P(rtw), None, None, P(out), P(cw), s),
+                  "combine")
         mark(4)
         L.ep_handle_free(h)
-        abi.check(L.ep_ll_dispatch(ctypes.byref(dd), S, P(lx), P(ltopk), P(packed), P(lcount),
-                                   P(lsrc), P(lslot), s), "ll dispatch")
+        abi.check(L.ep_ll_dispatch(ctypes.byref(dd), S, P(lx), P(ltopk), None, P(packed),
+                                   P(lcount), P(lsrc), P(lslot), s), "ll dispatch")
         mark(5)
         abi.check(L.ep_ll_combine(ctypes.byref(dd), S, P(packed), P(ltopk), P(lw), P(lslot),
-                                  P(lout), s), "ll combine")
+                                  None, P(lout), s), "ll combine")
         mark(6)
 
     # N and M for the byte counts
@@ -287,6 +288,11 @@ def main():
     copy_gbs = 2 * copy_bytes / (copy_us * 1e-6) / 1e9
     del src, dst
 
+    # ------------------------------------------- NEXT rows (not in ``value``)
+    next_report = measure_next(args, L, abi, tr, dc, xs[0], topk, w, d, cap, recv_xs[0], rtw,
+                               out, cw, packed, lcount, lsrc, lslot, lout, lx, ltopk, lw, dd, S,
+                               epr)
+
     # ---------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline and args.cpu_seconds > 0:
@@ -317,12 +323,109 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "next": next_report,
         "copy_ceiling": {"bytes_read_plus_written": 2 * copy_bytes, "avg_us": round(copy_us, 2),
                          "gbs": round(copy_gbs, 1),
                          "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
         "ops": op_report,
     }
     print(json.dumps(rec))
+
+
+def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw, packed, lcount,
+                 lsrc, lslot, lout, lx, ltopk, lw, dd, S, epr):
+    """Per-call times (HIP events, mean of ``args.steps`` calls after warmup)
+    of the operations beyond the step: low-latency calls with three ranks
+    masked, the FP8 low-latency dispatch, combine with two bias rows, and the
+    load-balance operations over the large workload's 32 redundant experts."""
+    import numpy as np
+    import torch
+    from gen import config_inputs, random_rows
+
+    P = abi.ptr
+    dev = torch.device("cuda", 0)
+
+    def timed(fn, n):
+        for _ in range(max(args.warmup, 2)):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(n):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / n
+
+    rep = {}
+    T, H, K = tr.T, tr.H, tr.K
+    s = abi.current_stream()
+    # combine with two bias rows
+    h = ctypes.c_void_p()
+    abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), ctypes.byref(h), P(recv_x),
+                            None, P(rtw), cap, None, s), "dispatch")
+    n = ctypes.c_int64()
+    abi.check(L.ep_handle_num_recv(h, ctypes.byref(n)), "num_recv")
+    N = int(n.value)
+    b0 = torch.from_numpy(random_rows(T, H, 0, tag=21).view(np.int16)).to(dev)
+    b1 = torch.from_numpy(random_rows(T, H, 0, tag=22).view(np.int16)).to(dev)
+    us = timed(lambda: abi.check(L.ep_combine(h, H, P(recv_x), cap, P(rtw), P(b0), P(b1), P(out),
+                                              P(cw), s), "combine"), args.steps)
+    byt = (N + T) * H * 2 + N * 4 + N * K * 4 + T * K * 4 + 2 * T * H * 2
+    rep["combine_with_bias"] = {"avg_us": round(us, 2), "bytes": byt,
+                                "gbs": round(byt / (us * 1e-6) / 1e9, 1)}
+    L.ep_handle_free(h)
+
+    # low-latency with three ranks masked
+    mask = torch.zeros(dc.R, dtype=torch.int32, device=dev)
+    for r in (3, 17, 31):
+        abi.check(L.ep_mask_update(P(mask), dc.R, r, 1, s), "mask")
+    us_d = timed(lambda: abi.check(L.ep_ll_dispatch(ctypes.byref(dd), S, P(lx), P(ltopk), P(mask),
+                                                    P(packed), P(lcount), P(lsrc), P(lslot), s),
+                                   "ll"), args.steps)
+    us_c = timed(lambda: abi.check(L.ep_ll_combine(ctypes.byref(dd), S, P(packed), P(ltopk), P(lw),
+                                                   P(lslot), P(mask), P(lout), s), "ll"),
+                 args.steps)
+    rep["ll_dispatch_masked3"] = {"avg_us": round(us_d, 2)}
+    rep["ll_combine_masked3"] = {"avg_us": round(us_c, 2)}
+
+    # FP8 low-latency dispatch
+    q = torch.empty((epr, dc.R, S, dc.H), dtype=torch.uint8, device=dev)
+    sc = torch.empty((epr, dc.R, S, dc.H // 128), dtype=torch.float32, device=dev)
+    us = timed(lambda: abi.check(L.ep_ll_dispatch_fp8(ctypes.byref(dd), S, P(lx), P(ltopk), None,
+                                                      P(q), P(sc), P(lcount), P(lsrc), P(lslot),
+                                                      s), "fp8"), args.steps)
+    M = int((dc.topk_idx >= 0).sum())
+    byt = dc.T * dc.H * 2 + M * dc.H + M * (dc.H // 128) * 4 + dc.T * dc.K * 12 + M * 4
+    rep["ll_dispatch_fp8"] = {"avg_us": round(us, 2), "bytes": byt,
+                              "gbs": round(byt / (us * 1e-6) / 1e9, 1)}
+
+    # load balancing: 32 replicas of the large workload's most popular experts
+    big = config_inputs(4, with_x=False)
+    table = big.extra["redundancy"]
+    n_rep = int((table >= 0).sum())
+    e_log = big.E - n_rep
+    mapping = np.full(n_rep, -1, np.int64)
+    for e, r in enumerate(table):
+        if r >= 0:
+            mapping[r - e_log] = e
+    elems = 4 << 20  # 4 Mi bf16 per expert (8 MiB)
+    ew = torch.empty((e_log, elems), dtype=torch.bfloat16, device=dev).normal_()
+    rw = torch.empty((n_rep, elems), dtype=torch.bfloat16, device=dev)
+    mp = torch.from_numpy(mapping).to(dev)
+    us = timed(lambda: abi.check(L.ep_lb_prefetch_weights(P(ew), P(rw), P(mp), n_rep, e_log,
+                                                          elems, s), "lb"), max(args.steps // 5, 3))
+    byt = 2 * n_rep * elems * 2
+    rep["lb_prefetch_weights"] = {"avg_us": round(us, 2), "bytes": byt,
+                                  "gbs": round(byt / (us * 1e-6) / 1e9, 1),
+                                  "replicas": n_rep, "elems_per_expert": elems}
+    us = timed(lambda: abi.check(L.ep_lb_reduce_grads(P(rw), P(ew), P(mp), n_rep, e_log, elems, s),
+                                 "lb"), max(args.steps // 5, 3))
+    n_targets = len(set(mapping.tolist()))
+    byt = (n_rep + 2 * n_targets) * elems * 2
+    rep["lb_reduce_grads"] = {"avg_us": round(us, 2), "bytes": byt,
+                              "gbs": round(byt / (us * 1e-6) / 1e9, 1)}
+    del ew, rw
+    return rep
 
 
 def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int):

@@ -27,7 +27,9 @@ EXPORTS = (
     "ep_max_recv_rows", "ep_get_dispatch_layout", "ep_dispatch", "ep_combine",
     "ep_ll_dispatch", "ep_ll_combine", "ep_handle_copy_layout", "ep_handle_num_recv",
     "ep_handle_dims", "ep_handle_nbytes", "ep_handle_free", "ep_pool_trim", "ep_status_str",
-    "ep_last_hip_error", "ep_version", "ep_set_tuning", "ep_tuning_list",
+    "ep_last_hip_error", "ep_version", "ep_set_tuning", "ep_tuning_list", "ep_ll_dispatch_fp8",
+    "ep_mask_update", "ep_mask_clean", "ep_mask_query", "ep_lb_prefetch_weights",
+    "ep_lb_reduce_grads",
 )
 
 
@@ -75,9 +77,15 @@ def _load():
         "ep_get_dispatch_layout": (ctypes.c_int, [pdims, vp, pout, ctypes.POINTER(vp), vp]),
         "ep_dispatch": (ctypes.c_int, [pdims, vp, vp, vp, ctypes.POINTER(vp), vp, vp, vp, i64,
                                        ctypes.POINTER(i64), vp]),
-        "ep_combine": (ctypes.c_int, [vp, i32, vp, i64, vp, vp, vp, vp]),
-        "ep_ll_dispatch": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp]),
-        "ep_ll_combine": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp]),
+        "ep_combine": (ctypes.c_int, [vp, i32, vp, i64, vp, vp, vp, vp, vp, vp]),
+        "ep_ll_dispatch": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "ep_ll_dispatch_fp8": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "ep_ll_combine": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "ep_mask_update": (ctypes.c_int, [vp, i32, i32, i32, vp]),
+        "ep_mask_clean": (ctypes.c_int, [vp, i32, vp]),
+        "ep_mask_query": (ctypes.c_int, [vp, i32, vp, vp]),
+        "ep_lb_prefetch_weights": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, vp]),
+        "ep_lb_reduce_grads": (ctypes.c_int, [vp, vp, vp, i32, i32, i64, vp]),
         "ep_handle_copy_layout": (ctypes.c_int, [vp, pout, vp]),
         "ep_handle_num_recv": (ctypes.c_int, [vp, ctypes.POINTER(i64)]),
         "ep_handle_dims": (ctypes.c_int, [vp, pdims]),

@@ -3,7 +3,9 @@
 "DeepEP Buffer Class API for Expert Parallel Communication" describes a
 ``Buffer`` with ``get_dispatch_layout``, ``dispatch`` (6 results),
 ``combine`` (3 results), ``low_latency_dispatch`` (5 results),
-``low_latency_combine`` (3 results) and ``destroy``.  This class keeps those
+``low_latency_combine`` (3 results), the low-latency mask-buffer utilities
+and ``destroy``; "Chapter 10, V2: buffers beyond EP" (10.2) adds
+``lb_prefetch_weights`` and ``lb_reduce_grads``.  This class keeps those
 names and result arities so callers can switch; the slots that carried a CUDA
 event or receive hook hold ``None`` (work is ordered on torch's current
 stream instead).  The R ranks are logical partitions of this GPU's memory.
@@ -127,6 +129,38 @@ class Buffer:
         self.num_experts = int(num_experts)
         self.num_channels = int(num_channels)
         self.destroyed = False
+        self._mask = None  # device int32 [R], created by the first mask update
+
+    # ------------------------------------------------------- rank masking
+    def _mask_ptr(self):
+        return abi.ptr(self._mask) if self._mask is not None else None
+
+    def low_latency_update_mask_buffer(self, rank_to_mask: int, mask: bool = False) -> None:
+        """Mask (True) or unmask (False) one rank for the low-latency calls."""
+        if self._mask is None:
+            self._mask = torch.zeros(self.num_ranks, dtype=torch.int32, device="cuda")
+        abi.check(abi.lib().ep_mask_update(abi.ptr(self._mask), self.num_ranks, int(rank_to_mask),
+                                           1 if mask else 0, abi.current_stream()),
+                  "ep_mask_update")
+
+    def low_latency_query_mask_buffer(self, mask_status: torch.Tensor) -> None:
+        """Write the mask (0 active, 1 masked) into a CPU int32 tensor [R]."""
+        if (mask_status.dtype != torch.int32 or mask_status.numel() != self.num_ranks
+                or mask_status.is_cuda or not mask_status.is_contiguous()):
+            raise ValueError("mask_status must be a contiguous CPU int32 tensor with one entry "
+                             "per rank")
+        if self._mask is None:
+            mask_status.zero_()
+            return
+        abi.check(abi.lib().ep_mask_query(abi.ptr(self._mask), self.num_ranks,
+                                          ctypes.c_void_p(mask_status.data_ptr()),
+                                          abi.current_stream()), "ep_mask_query")
+
+    def low_latency_clean_mask_buffer(self) -> None:
+        """Mark every rank active again."""
+        if self._mask is not None:
+            abi.check(abi.lib().ep_mask_clean(abi.ptr(self._mask), self.num_ranks,
+                                              abi.current_stream()), "ep_mask_clean")
 
     @property
     def num_local_experts(self) -> int:
@@ -210,29 +244,45 @@ class Buffer:
         return ntpe.view(self.num_ranks, self.num_local_experts)
 
     # ------------------------------------------------------------- combine
-    def combine(self, x: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None):
+    def combine(self, x: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None,
+                bias=None):
         """Returns (combined_x [T, H] bf16, combined_topk_weights [T, K] or
-        None, None): the ascending-rank fp32 sum of each token's rows."""
+        None, None): the ascending-rank fp32 sum of each token's rows, plus
+        the optional bias terms (a [T, H] bf16 tensor or a tuple of up to
+        two), added before the single rounding."""
         _need(x, torch.bfloat16, "x", 2)
         if topk_weights is not None:
             _need(topk_weights, torch.float32, "topk_weights", 2)
         d = handle.dims
         T, H = d.num_tokens, x.shape[1]
+        biases = [] if bias is None else ([bias] if isinstance(bias, torch.Tensor) else list(bias))
+        if len(biases) > 2:
+            raise ValueError("at most two bias tensors")
+        for b in biases:
+            _need(b, torch.bfloat16, "bias", 2)
+            if tuple(b.shape) != (T, H):
+                raise ValueError("bias must be [num_tokens, hidden]")
+        b0 = biases[0] if len(biases) > 0 else None
+        b1 = biases[1] if len(biases) > 1 else None
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
         cw = None
         if topk_weights is not None:
             cw = torch.empty((T, d.num_topk), dtype=torch.float32, device=x.device)
         abi.check(abi.lib().ep_combine(handle.raw, H, abi.ptr(x), x.shape[0], abi.ptr(topk_weights),
-                                       abi.ptr(out), abi.ptr(cw), abi.current_stream()),
+                                       abi.ptr(b0), abi.ptr(b1), abi.ptr(out), abi.ptr(cw),
+                                       abi.current_stream()),
                   "ep_combine")
         return out, cw, None
 
     # --------------------------------------------------------- low latency
     def low_latency_dispatch(self, x: torch.Tensor, topk_idx: torch.Tensor,
                              num_max_dispatch_tokens_per_rank: int,
-                             num_experts: Optional[int] = None):
-        """Returns (packed_x [E/R, R, slots, H], packed_count [E/R, R],
-        handle, None, None).  Unused packed cells are left as allocated."""
+                             num_experts: Optional[int] = None, use_fp8: bool = False):
+        """Returns (packed_x, packed_count [E/R, R], handle, None, None).
+        packed_x is [E/R, R, slots, H] bf16, or with use_fp8 the pair
+        (codes [E/R, R, slots, H] float8_e4m3fn, scales [E/R, R, slots, H/128]
+        fp32).  Unused packed cells are left as allocated.  Ranks masked with
+        low_latency_update_mask_buffer receive nothing."""
         if num_experts is not None and num_experts != self.num_experts:
             raise ValueError("num_experts differs from the buffer's")
         _need(x, torch.bfloat16, "x", 2)
@@ -243,14 +293,24 @@ class Buffer:
         d = self._dims(T, H, K)
         dev = x.device
         epr, R = self.num_local_experts, self.num_ranks
-        packed = torch.empty((epr, R, S, H), dtype=torch.bfloat16, device=dev)
         count = torch.empty((epr, R), dtype=torch.int32, device=dev)
         src = torch.empty((epr, R, S), dtype=torch.int32, device=dev)
         slot = torch.empty((T, K), dtype=torch.int32, device=dev)
-        abi.check(abi.lib().ep_ll_dispatch(ctypes.byref(d), S, abi.ptr(x), abi.ptr(topk_idx),
-                                           abi.ptr(packed), abi.ptr(count), abi.ptr(src),
-                                           abi.ptr(slot), abi.current_stream()),
-                  "ep_ll_dispatch")
+        if use_fp8:
+            q = torch.empty((epr, R, S, H), dtype=torch.uint8, device=dev)
+            sc = torch.empty((epr, R, S, H // 128), dtype=torch.float32, device=dev)
+            abi.check(abi.lib().ep_ll_dispatch_fp8(ctypes.byref(d), S, abi.ptr(x), abi.ptr(topk_idx),
+                                                   self._mask_ptr(), abi.ptr(q), abi.ptr(sc),
+                                                   abi.ptr(count), abi.ptr(src), abi.ptr(slot),
+                                                   abi.current_stream()),
+                      "ep_ll_dispatch_fp8")
+            packed = (q.view(torch.float8_e4m3fn), sc)
+        else:
+            packed = torch.empty((epr, R, S, H), dtype=torch.bfloat16, device=dev)
+            abi.check(abi.lib().ep_ll_dispatch(ctypes.byref(d), S, abi.ptr(x), abi.ptr(topk_idx),
+                                               self._mask_ptr(), abi.ptr(packed), abi.ptr(count),
+                                               abi.ptr(src), abi.ptr(slot), abi.current_stream()),
+                      "ep_ll_dispatch")
         return packed, count, LowLatencyHandle(src, slot, S, self.num_experts, H), None, None
 
     def low_latency_combine(self, x: torch.Tensor, topk_idx: torch.Tensor,
@@ -266,10 +326,42 @@ class Buffer:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
         abi.check(abi.lib().ep_ll_combine(ctypes.byref(d), handle.num_slots, abi.ptr(x),
                                           abi.ptr(topk_idx), abi.ptr(topk_weights),
-                                          abi.ptr(handle.topk_slot), abi.ptr(out),
-                                          abi.current_stream()),
+                                          abi.ptr(handle.topk_slot), self._mask_ptr(),
+                                          abi.ptr(out), abi.current_stream()),
                   "ep_ll_combine")
         return out, None, None
+
+    # ------------------------------------------------------ load balancing
+    @staticmethod
+    def _lb_args(a: torch.Tensor, b: torch.Tensor, mapping: torch.Tensor):
+        for t, n in ((a, "weights"), (b, "weights")):
+            _need(t, torch.bfloat16, n, t.dim())
+        _need(mapping, torch.int64, "redundancy_mapping", 1)
+        P = a[0].numel() if a.shape[0] > 0 else (b[0].numel() if b.shape[0] > 0 else 0)
+        return P
+
+    def lb_prefetch_weights(self, redundant_expert_weights: torch.Tensor,
+                            expert_weights: torch.Tensor, redundancy_mapping: torch.Tensor,
+                            num_sms: int = 0, previous_event=None):
+        """redundant_expert_weights[j] = expert_weights[redundancy_mapping[j]]
+        (bf16, one row per expert / replica).  Returns None."""
+        P = self._lb_args(redundant_expert_weights, expert_weights, redundancy_mapping)
+        abi.check(abi.lib().ep_lb_prefetch_weights(
+            abi.ptr(expert_weights), abi.ptr(redundant_expert_weights), abi.ptr(redundancy_mapping),
+            redundancy_mapping.numel(), expert_weights.shape[0], P, abi.current_stream()),
+            "ep_lb_prefetch_weights")
+        return None
+
+    def lb_reduce_grads(self, redundant_expert_grads: torch.Tensor, expert_grads: torch.Tensor,
+                        redundancy_mapping: torch.Tensor, num_sms: int = 0, previous_event=None):
+        """Folds each replica's gradient into its expert (in place, fp32
+        accumulation, replicas in ascending order, one rounding).  Returns None."""
+        P = self._lb_args(redundant_expert_grads, expert_grads, redundancy_mapping)
+        abi.check(abi.lib().ep_lb_reduce_grads(
+            abi.ptr(redundant_expert_grads), abi.ptr(expert_grads), abi.ptr(redundancy_mapping),
+            redundancy_mapping.numel(), expert_grads.shape[0], P, abi.current_stream()),
+            "ep_lb_reduce_grads")
+        return None
 
     def destroy(self) -> None:
         """Return pooled device memory of the current device."""

@@ -10,6 +10,10 @@
 // nearest even.  The optional weight reduction sums the per-row top-k
 // weights the same way.
 //
+// The optional bias terms of the same section (reading: one or two bf16
+// [T][H] tensors) are added in fp32 after the rank sum, bias0 then bias1,
+// before the single rounding.
+//
 // The sum order is fixed (rank ascending, one add per row per element), so the
 // result does not depend on the launch shape.  U rows' loads are issued
 // before any of them is added, so each lane keeps U*VPT 16-byte loads in
@@ -55,10 +59,11 @@ __device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
 // each group walks them with a grid stride.  NTL: rows are loaded
 // nontemporally (each is read exactly once).  The slice-0 group reduces the
 // weights.
-template <int G, int VPT, int U, bool NTL>
+template <int G, int VPT, int U, bool NTL, bool kBias>
 __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
     const u32x4 *__restrict__ y, int T, int V, int K, int kmax, int S,
     const int32_t *__restrict__ dst_row, const float *__restrict__ recv_topk_weights,
+    const u32x4 *__restrict__ bias0, const u32x4 *__restrict__ bias1,
     u32x4 *__restrict__ out, float *__restrict__ combined_topk_weights)
 {
     constexpr int kGroups = kCombineBlock / G;
@@ -99,6 +104,20 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
                     if (j + u < nhit)
                         add_row<VPT>(acc, v[u]);
             }
+            // Bias terms: after the rank sum, before the one rounding.
+            const u32x4 *biases[2] = {bias0, bias1};
+            for (int bi = 0; kBias && bi < 2; ++bi) {
+                const u32x4 *bias = biases[bi];
+                if (bias == nullptr)
+                    continue;
+                u32x4 bv[VPT];
+#pragma unroll
+                for (int i = 0; i < VPT; ++i) {
+                    const int idx = base + i * G + gt;
+                    bv[i] = idx < V ? bias[int64_t(t) * V + idx] : u32x4{0, 0, 0, 0};
+                }
+                add_row<VPT>(acc, bv);
+            }
 
             u32x4 *o = out + int64_t(t) * V;
 #pragma unroll
@@ -128,7 +147,7 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
 }
 
 typedef void (*CombineFn)(const u32x4 *, int, int, int, int, int, const int32_t *,
-                          const float *, u32x4 *, float *);
+                          const float *, const u32x4 *, const u32x4 *, u32x4 *, float *);
 
 // A launch shape: G lanes per group, VPT vectors per lane, S groups per token
 // (row slices), U rows in flight, NTL nontemporal row loads, and P =
@@ -136,10 +155,12 @@ typedef void (*CombineFn)(const u32x4 *, int, int, int, int, int, const int32_t 
 // addresses shapes as (G, VPT, S*1000 + U*100 + NTL*10 + P/256).
 struct CombineCfg {
     int G, VPT, S, U, NTL, P;
-    CombineFn fn;
+    CombineFn fn, fn_bias;
 };
 
-#define EP_COMBINE_CFG(G, VPT, S, U, NTL, P) {G, VPT, S, U, NTL, P, combine_kernel<G, VPT, U, NTL>}
+#define EP_COMBINE_CFG(G, VPT, S, U, NTL, P)                                               \
+    {G, VPT, S, U, NTL, P, combine_kernel<G, VPT, U, NTL, false>,                          \
+     combine_kernel<G, VPT, U, NTL, true>}
 
 const CombineCfg kCombineCfgs[] = {
     EP_COMBINE_CFG(256, 1, 1, 2, 1, 0), EP_COMBINE_CFG(256, 2, 1, 2, 1, 0),
@@ -220,8 +241,8 @@ void combine_tuning_at(int i, int *g, int *vpt, int *u)
 }
 
 hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const LayoutBufs &b,
-                          const float *recv_topk_weights, void *out,
-                          float *combined_topk_weights, hipStream_t stream)
+                          const float *recv_topk_weights, const void *bias0, const void *bias1,
+                          void *out, float *combined_topk_weights, hipStream_t stream)
 {
     if (s.T == 0)
         return hipSuccess;
@@ -232,9 +253,12 @@ hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const
     int blocks = int((groups + per_block - 1) / per_block);
     if (c.P > 0 && c.P < blocks)
         blocks = c.P;
-    hipLaunchKernelGGL(c.fn, dim3(blocks), dim3(kCombineBlock), 0, stream,
+    const bool bias = bias0 != nullptr || bias1 != nullptr;
+    hipLaunchKernelGGL(bias ? c.fn_bias : c.fn, dim3(blocks), dim3(kCombineBlock), 0, stream,
                        static_cast<const u32x4 *>(y), s.T, V, s.K, s.kmax, c.S, b.dst_row,
-                       recv_topk_weights, static_cast<u32x4 *>(out), combined_topk_weights);
+                       recv_topk_weights, static_cast<const u32x4 *>(bias0),
+                       static_cast<const u32x4 *>(bias1), static_cast<u32x4 *>(out),
+                       combined_topk_weights);
     return hipGetLastError();
 }
 

@@ -79,8 +79,8 @@ int trim_pool(DevicePool &P)
             if (e != hipSuccess)
                 rc = hip_fail(e);
         }
-        hipEventDestroy(a.done);
-        hipFree(a.ptr);
+        (void)hipEventDestroy(a.done);
+        (void)hipFree(a.ptr);
     }
     return rc;
 }
@@ -128,7 +128,7 @@ int arena_get(int dev, size_t bytes, hipStream_t stream, Arena *out)
     hipEvent_t ev = nullptr;
     e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
     if (e != hipSuccess) {
-        hipFree(p);
+        (void)hipFree(p);
         return hip_fail(e);
     }
     out->ptr = p;
@@ -146,7 +146,7 @@ void arena_put(int dev, Arena a, hipStream_t stream)
     if (e != hipSuccess) {
         // Cannot order the reuse after the pending work: wait for it here.
         (void)hipGetLastError();
-        hipStreamSynchronize(stream);
+        (void)hipStreamSynchronize(stream);
     }
     DevicePool &P = pool_for(dev);
     std::lock_guard<std::mutex> g(P.mu);
@@ -435,8 +435,8 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
 }
 
 int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
-               const float *recv_topk_weights, void *out, float *combined_topk_weights,
-               ep_stream_t stream_)
+               const float *recv_topk_weights, const void *bias0, const void *bias1, void *out,
+               float *combined_topk_weights, ep_stream_t stream_)
 {
     try {
         if (h == nullptr)
@@ -445,8 +445,8 @@ int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
             return EP_ERR_INVALID;
         if (hidden % 8 != 0)
             return EP_ERR_ALIGN;
-        if (!aligned(y, 16) || !aligned(out, 16) || !aligned(recv_topk_weights, 4) ||
-            !aligned(combined_topk_weights, 4))
+        if (!aligned(y, 16) || !aligned(out, 16) || !aligned(bias0, 16) || !aligned(bias1, 16) ||
+            !aligned(recv_topk_weights, 4) || !aligned(combined_topk_weights, 4))
             return EP_ERR_ALIGN;
         const bool rows = h->dims.num_tokens > 0;
         if (rows && (out == nullptr || y == nullptr))
@@ -459,8 +459,8 @@ int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
         int rc = check_capacity(h, y_rows, stream);
         if (rc != EP_OK)
             return rc;
-        hipError_t e = launch_combine(h->shape, hidden, y, h->bufs, recv_topk_weights, out,
-                                      combined_topk_weights, stream);
+        hipError_t e = launch_combine(h->shape, hidden, y, h->bufs, recv_topk_weights, bias0,
+                                      bias1, out, combined_topk_weights, stream);
         if (e != hipSuccess)
             return hip_fail(e);
         h->last_stream = stream;
@@ -470,9 +470,14 @@ int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
     }
 }
 
-int ep_ll_dispatch(const ep_dims *dims, int32_t num_slots, const void *x,
-                   const int64_t *topk_idx, void *packed_x, int32_t *packed_count,
-                   int32_t *src_info, int32_t *topk_slot, ep_stream_t stream_)
+}  // extern "C"
+
+namespace {
+
+int ll_dispatch_common(const ep_dims *dims, int32_t num_slots, const void *x,
+                       const int64_t *topk_idx, const int32_t *rank_mask, void *packed_x,
+                       void *packed_q, float *packed_scale, int32_t *packed_count,
+                       int32_t *src_info, int32_t *topk_slot, ep_stream_t stream_)
 {
     if (dims == nullptr)
         return EP_ERR_INVALID;
@@ -489,19 +494,63 @@ int ep_ll_dispatch(const ep_dims *dims, int32_t num_slots, const void *x,
         return EP_ERR_INVALID;
     if (d.num_tokens > 0 && (topk_idx == nullptr || topk_slot == nullptr))
         return EP_ERR_INVALID;
-    if (packed_x != nullptr && x == nullptr && d.num_tokens > 0)
+    const bool rows = packed_x != nullptr || packed_q != nullptr;
+    if (rows && x == nullptr && d.num_tokens > 0)
         return EP_ERR_INVALID;
-    if (!aligned(x, 16) || !aligned(packed_x, 16) || !aligned(topk_idx, 8) ||
+    if (packed_q != nullptr && (packed_scale == nullptr || d.hidden % 128 != 0))
+        return packed_scale == nullptr ? EP_ERR_INVALID : EP_ERR_ALIGN;
+    if (!aligned(x, 16) || !aligned(packed_x, 16) || !aligned(packed_q, 8) ||
+        !aligned(packed_scale, 4) || !aligned(topk_idx, 8) || !aligned(rank_mask, 4) ||
         !aligned(packed_count, 4) || !aligned(src_info, 4) || !aligned(topk_slot, 4))
         return EP_ERR_ALIGN;
-    hipError_t e = launch_ll_dispatch(d, num_slots, x, topk_idx, packed_x, packed_count, src_info,
-                                      topk_slot, static_cast<hipStream_t>(stream_));
+    hipError_t e = launch_ll_dispatch(d, num_slots, x, topk_idx, rank_mask, packed_x, packed_q,
+                                      packed_scale, packed_count, src_info, topk_slot,
+                                      static_cast<hipStream_t>(stream_));
     return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
+int check_lb(const void *a, const void *b, const int64_t *mapping, int32_t num_replicas,
+             int32_t num_experts, int64_t elems)
+{
+    if (num_replicas < 0 || num_replicas > 65535 || num_experts < 1 || elems < 0)
+        return EP_ERR_INVALID;
+    if (elems % 8 != 0)
+        return EP_ERR_ALIGN;
+    if (num_replicas > 0 && elems > 0 && (a == nullptr || b == nullptr || mapping == nullptr))
+        return EP_ERR_INVALID;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(mapping, 8))
+        return EP_ERR_ALIGN;
+    return EP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ep_ll_dispatch(const ep_dims *dims, int32_t num_slots, const void *x,
+                   const int64_t *topk_idx, const int32_t *rank_mask, void *packed_x,
+                   int32_t *packed_count, int32_t *src_info, int32_t *topk_slot,
+                   ep_stream_t stream)
+{
+    return ll_dispatch_common(dims, num_slots, x, topk_idx, rank_mask, packed_x, nullptr, nullptr,
+                              packed_count, src_info, topk_slot, stream);
+}
+
+int ep_ll_dispatch_fp8(const ep_dims *dims, int32_t num_slots, const void *x,
+                       const int64_t *topk_idx, const int32_t *rank_mask, void *packed_q,
+                       float *packed_scale, int32_t *packed_count, int32_t *src_info,
+                       int32_t *topk_slot, ep_stream_t stream)
+{
+    if (packed_q == nullptr || packed_scale == nullptr)
+        return EP_ERR_INVALID;
+    return ll_dispatch_common(dims, num_slots, x, topk_idx, rank_mask, nullptr, packed_q,
+                              packed_scale, packed_count, src_info, topk_slot, stream);
 }
 
 int ep_ll_combine(const ep_dims *dims, int32_t num_slots, const void *packed_y,
                   const int64_t *topk_idx, const float *topk_weights,
-                  const int32_t *topk_slot, void *out, ep_stream_t stream_)
+                  const int32_t *topk_slot, const int32_t *rank_mask, void *out,
+                  ep_stream_t stream_)
 {
     if (dims == nullptr)
         return EP_ERR_INVALID;
@@ -518,10 +567,76 @@ int ep_ll_combine(const ep_dims *dims, int32_t num_slots, const void *packed_y,
                              topk_weights == nullptr || topk_slot == nullptr || out == nullptr))
         return EP_ERR_INVALID;
     if (!aligned(packed_y, 16) || !aligned(out, 16) || !aligned(topk_idx, 8) ||
-        !aligned(topk_weights, 4) || !aligned(topk_slot, 4))
+        !aligned(topk_weights, 4) || !aligned(topk_slot, 4) || !aligned(rank_mask, 4))
         return EP_ERR_ALIGN;
     hipError_t e = launch_ll_combine(d, num_slots, packed_y, topk_idx, topk_weights, topk_slot,
-                                     out, static_cast<hipStream_t>(stream_));
+                                     rank_mask, out, static_cast<hipStream_t>(stream_));
+    return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
+int ep_mask_update(int32_t *rank_mask, int32_t num_ranks, int32_t rank, int32_t masked,
+                   ep_stream_t stream)
+{
+    if (rank_mask == nullptr || num_ranks < 1 || num_ranks > kMaxRanks || rank < 0 ||
+        rank >= num_ranks)
+        return EP_ERR_INVALID;
+    if (!aligned(rank_mask, 4))
+        return EP_ERR_ALIGN;
+    hipError_t e = launch_mask_set(rank_mask, num_ranks, rank, masked ? 1 : 0,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
+int ep_mask_clean(int32_t *rank_mask, int32_t num_ranks, ep_stream_t stream)
+{
+    if (rank_mask == nullptr || num_ranks < 1 || num_ranks > kMaxRanks)
+        return EP_ERR_INVALID;
+    if (!aligned(rank_mask, 4))
+        return EP_ERR_ALIGN;
+    hipError_t e = launch_mask_set(rank_mask, num_ranks, -1, 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
+int ep_mask_query(const int32_t *rank_mask, int32_t num_ranks, int32_t *host_out,
+                  ep_stream_t stream_)
+{
+    if (rank_mask == nullptr || host_out == nullptr || num_ranks < 1 || num_ranks > kMaxRanks)
+        return EP_ERR_INVALID;
+    if (!aligned(rank_mask, 4))
+        return EP_ERR_ALIGN;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    hipError_t e = hipMemcpyAsync(host_out, rank_mask, size_t(num_ranks) * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
+int ep_lb_reduce_grads(const void *redundant_grads, void *expert_grads, const int64_t *mapping,
+                       int32_t num_replicas, int32_t num_experts, int64_t elems_per_expert,
+                       ep_stream_t stream)
+{
+    int rc = check_lb(redundant_grads, expert_grads, mapping, num_replicas, num_experts,
+                      elems_per_expert);
+    if (rc != EP_OK)
+        return rc;
+    hipError_t e = launch_lb_reduce_grads(redundant_grads, expert_grads, mapping, num_replicas,
+                                          num_experts, elems_per_expert,
+                                          static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
+int ep_lb_prefetch_weights(const void *expert_weights, void *redundant_weights,
+                           const int64_t *mapping, int32_t num_replicas, int32_t num_experts,
+                           int64_t elems_per_expert, ep_stream_t stream)
+{
+    int rc = check_lb(expert_weights, redundant_weights, mapping, num_replicas, num_experts,
+                      elems_per_expert);
+    if (rc != EP_OK)
+        return rc;
+    hipError_t e = launch_lb_prefetch_weights(expert_weights, redundant_weights, mapping,
+                                              num_replicas, num_experts, elems_per_expert,
+                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? EP_OK : hip_fail(e);
 }
 
@@ -566,10 +681,10 @@ void ep_handle_free(ep_handle *h)
     int cur = 0;
     const bool switch_dev = hipGetDevice(&cur) == hipSuccess && cur != h->device;
     if (switch_dev)
-        hipSetDevice(h->device);
+        (void)hipSetDevice(h->device);
     arena_put(h->device, h->arena, h->last_stream.load());
     if (switch_dev)
-        hipSetDevice(cur);
+        (void)hipSetDevice(cur);
     delete h;
 }
 
@@ -628,6 +743,6 @@ const char *ep_status_str(int status)
 
 const char *ep_last_hip_error(void) { return g_last_hip.c_str(); }
 
-int ep_version(void) { return (1 << 16) | 0; }
+int ep_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

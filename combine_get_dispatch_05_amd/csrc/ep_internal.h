@@ -60,16 +60,30 @@ hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, cons
                            int64_t *recv_topk_idx, float *recv_topk_weights, hipStream_t stream);
 
 hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const LayoutBufs &b,
-                          const float *recv_topk_weights, void *out,
-                          float *combined_topk_weights, hipStream_t stream);
+                          const float *recv_topk_weights, const void *bias0, const void *bias1,
+                          void *out, float *combined_topk_weights, hipStream_t stream);
 
+// packed_q (nullable) selects the FP8 variant: codes [cells][H] bytes and
+// packed_scale [cells][H/128]; packed_x is then unused.
 hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
-                              const int64_t *topk_idx, void *packed_x, int32_t *packed_count,
+                              const int64_t *topk_idx, const int32_t *rank_mask, void *packed_x,
+                              void *packed_q, float *packed_scale, int32_t *packed_count,
                               int32_t *src_info, int32_t *topk_slot, hipStream_t stream);
 
 hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed_y,
                              const int64_t *topk_idx, const float *topk_weights,
-                             const int32_t *topk_slot, void *out, hipStream_t stream);
+                             const int32_t *topk_slot, const int32_t *rank_mask, void *out,
+                             hipStream_t stream);
+
+hipError_t launch_mask_set(int32_t *mask, int num_ranks, int rank, int value, hipStream_t stream);
+
+hipError_t launch_lb_reduce_grads(const void *redundant_grads, void *expert_grads,
+                                  const int64_t *mapping, int num_replicas, int num_experts,
+                                  int64_t elems, hipStream_t stream);
+
+hipError_t launch_lb_prefetch_weights(const void *expert_weights, void *redundant_weights,
+                                      const int64_t *mapping, int num_replicas, int num_experts,
+                                      int64_t elems, hipStream_t stream);
 
 // Launch-shape overrides (never change results).  (-1, ...) restores the
 // default choice.  Return false for a shape that is not compiled in.

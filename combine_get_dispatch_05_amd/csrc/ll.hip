@@ -15,7 +15,12 @@
 //
 // Combine: one workgroup per (token, row chunk).  All K cell addresses of the
 // token are resolved once into LDS; each lane then issues its K loads before
-// the fused multiply-adds, which run in ascending slot order from +0.
+// the fused multiply-adds, which run in ascending slot order from +0.  A rank
+// masked at combine time contributes nothing.
+//
+// FP8 ("use_fp8" of the same section, which the pages' code example sets on
+// the dispatch): the dispatch can store e4m3 codes with one fp32 scale per
+// 128 elements instead of bf16 rows.
 
 #include "ep_internal.h"
 
@@ -38,15 +43,69 @@ __device__ __forceinline__ int ll_wave_inclusive_scan(int v)
     return v;
 }
 
+// OCP FP8 E4M3 ("e4m3fn") code of an fp32 value: round to nearest, ties to
+// even, saturating at +-448 (no infinities in this format; 0x7F is NaN).
+// Normal results: add just under half of the 20 dropped mantissa bits (plus
+// one when the kept lsb is odd) and let a carry bump the exponent.  Results
+// below 2^-6: scale by 2^9 (exact) and round to an integer count of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u)
+        return sign | 0x7fu;
+    if (a >= 0x43e00000u)  // 448.0f and above (infinity included)
+        return sign | 0x7eu;
+    if (a < 0x3c800000u)  // below 2^-6
+        return sign | uint32_t(__builtin_rintf(__uint_as_float(a) * 512.0f));
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    const uint32_t e = (r >> 23) - 127u + 7u;
+    const uint32_t code = (e << 3) | ((r >> 20) & 7u);
+    return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// Max over each row of 16 lanes (the DPP row), every lane of the row gets
+// the result: swaps within quads, then rotations by 4 and 8 inside the row.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v)
+{
+    uint32_t t = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0xB1, 0xF, 0xF, false));
+    v = v > t ? v : t;
+    t = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x4E, 0xF, 0xF, false));
+    v = v > t ? v : t;
+    t = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x124, 0xF, 0xF, false));
+    v = v > t ? v : t;
+    t = uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xF, 0xF, false));
+    return v > t ? v : t;
+}
+
+__device__ __forceinline__ float row16_fmax(float v)
+{
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1)
+        v = fmaxf(v, __shfl_xor(v, m, 16));
+    return v;
+}
+
 // One workgroup per expert.  Each thread owns a contiguous chunk of the
 // flattened [T][K] table (held in registers when it is short), counts the
 // pairs naming its expert, and one block-wide exclusive scan of those counts
 // gives every thread the first slot of its chunk, so slots follow (token,
 // slot) order.  The rows are then copied with the (row, vector) pairs spread
 // flat over the block, kUnroll independent 16-byte loads in flight per lane.
+// A masked rank ("Dynamic Rank Masking") takes part in nothing: its experts'
+// pairs get no slot and its counts are 0.
+// kFP8: instead of bf16 rows, each 128-element block of a sent row is scaled
+// by 448 / max(amax, 1e-4) and stored as e4m3 codes, with its scale
+// amax / 448; a 16-lane group handles one block (8 elements per lane).
+// The copy of one expert's rows is split over gridDim.y workgroups; each
+// recomputes the (cheap, cached) slot scan, and only the y = 0 workgroup
+// writes the metadata.
+template <bool kFP8>
 __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
     const u32x4 *__restrict__ x, int T, int V, int K, int E, int R, int epr, int S,
-    const int64_t *__restrict__ topk_idx, u32x4 *__restrict__ packed_x,
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask,
+    u32x4 *__restrict__ packed_x, uint2 *__restrict__ packed_q, float *__restrict__ packed_scale,
     int32_t *__restrict__ packed_count, int32_t *__restrict__ src_info,
     int32_t *__restrict__ topk_slot)
 {
@@ -59,6 +118,7 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
     const int e = blockIdx.x;
     const int le = e % epr;
     const int r = e / epr;
+    const bool masked = rank_mask != nullptr && rank_mask[r] != 0;
     const int64_t cell0 = (int64_t(le) * R + r) * S;
     const int TK = T * K;
     const int chunk = (TK + kLLBlock - 1) / kLLBlock;
@@ -72,11 +132,11 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
 #pragma unroll
         for (int q = 0; q < kHold; ++q) {
             v[q] = i0 + q < i1 ? topk_idx[i0 + q] : -1;
-            mine += v[q] == e ? 1 : 0;
+            mine += (v[q] == e && !masked) ? 1 : 0;
         }
     } else {
         for (int i = i0; i < i1; ++i)
-            mine += topk_idx[i] == e ? 1 : 0;
+            mine += (topk_idx[i] == e && !masked) ? 1 : 0;
     }
 
     const int incl = ll_wave_inclusive_scan(mine);
@@ -92,17 +152,20 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
     }
     int s = before + incl - mine;  // first slot of this thread's chunk
 
+    const bool meta = blockIdx.y == 0;
     auto place = [&](int i, int64_t val) {
         if (val == e) {
-            if (s < S) {
-                topk_slot[i] = s;
-                src_info[cell0 + s] = i / K;
+            if (!masked && s < S) {
+                if (meta) {
+                    topk_slot[i] = s;
+                    src_info[cell0 + s] = i / K;
+                }
                 s_tok[s] = i / K;
-            } else {
+            } else if (meta) {
                 topk_slot[i] = -1;
             }
-            ++s;
-        } else if (e == 0 && !(val >= 0 && val < E)) {
+            s += masked ? 0 : 1;
+        } else if (meta && e == 0 && !(val >= 0 && val < E)) {
             topk_slot[i] = -1;  // masked or invalid slots: workgroup 0 marks them
         }
     };
@@ -116,17 +179,20 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
             place(i, topk_idx[i]);
     }
 
-    if (tid == 0)
-        packed_count[int64_t(le) * R + r] = total;
     const int used = total < S ? total : S;
-    for (int q = used + tid; q < S; q += kLLBlock)
-        src_info[cell0 + q] = -1;
+    if (blockIdx.y == 0) {
+        if (tid == 0)
+            packed_count[int64_t(le) * R + r] = total;
+        for (int q = used + tid; q < S; q += kLLBlock)
+            src_info[cell0 + q] = -1;
+    }
     __syncthreads();
+    const int ny = gridDim.y, yb = blockIdx.y;
 
-    if (packed_x != nullptr) {
+    if (!kFP8 && packed_x != nullptr) {
         constexpr int kUnroll = 8;
         const int n = used * V;
-        for (int p0 = 0; p0 < n; p0 += kLLBlock * kUnroll) {
+        for (int p0 = yb * kLLBlock * kUnroll; p0 < n; p0 += ny * kLLBlock * kUnroll) {
             u32x4 buf[kUnroll];
             int64_t dst[kUnroll];
 #pragma unroll
@@ -146,13 +212,108 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
                     packed_x[dst[u]] = buf[u];
         }
     }
+
+    if (kFP8) {
+        // 16 vectors of 8 bf16 per 128-element block; V is a multiple of 16.
+        // A wave takes 4 blocks per round and kRounds rounds at once, so
+        // kRounds loads are in flight before any block is quantized.  Lanes
+        // past the end load row 0's block (always valid when items > 0) and
+        // store nothing.
+        constexpr int kRounds = 4;
+        const int nb = V / 16;
+        const int items = used * nb;
+        const int g16 = lane >> 4;  // group of 16 lanes inside the wave
+        const int l16 = lane & 15;
+        const int wave = yb * kLLWaves + wid;
+        const int nwaves = ny * kLLWaves;
+        for (int w0 = wave * 4 * kRounds; w0 < items; w0 += nwaves * 4 * kRounds) {
+            u32x4 vv[kRounds];
+            int row[kRounds], blk[kRounds], tok[kRounds];
+#pragma unroll
+            for (int k = 0; k < kRounds; ++k) {
+                const int item = w0 + k * 4 + g16;
+                const int it = item < items ? item : 0;
+                row[k] = item < items ? it / nb : -1;
+                blk[k] = it - (it / nb) * nb;
+                tok[k] = s_tok[it / nb];
+            }
+#pragma unroll
+            for (int k = 0; k < kRounds; ++k)
+                vv[k] = x[int64_t(tok[k]) * V + int64_t(blk[k]) * 16 + l16];
+#pragma unroll
+            for (int k = 0; k < kRounds; ++k) {
+                // max |x| of the block as bf16 bits: for finite values the
+                // integer order of the magnitude bits is the numeric order.
+                uint32_t bits = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = vv[k][q];
+                    const uint32_t lo = w & 0x7fffu, hi = (w >> 16) & 0x7fffu;
+                    bits = bits > lo ? bits : lo;
+                    bits = bits > hi ? bits : hi;
+                }
+                bits = row16_max(bits);
+                uint2 codes;
+                float amax;
+                if (bits < 0x7f80u) {
+                    // finite block: |x * 448 / amax| stays below 464, where the
+                    // hardware conversion rounds to nearest even exactly as
+                    // e4m3_rne does (checked over every fp32 input).
+                    amax = __uint_as_float(bits << 16);
+                    amax = amax < 1e-4f ? 1e-4f : amax;
+                    const float sinv = 448.0f / amax;
+                    uint32_t c[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const uint32_t w0v = vv[k][2 * h], w1v = vv[k][2 * h + 1];
+                        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w0v) * sinv,
+                                                                 bf16_hi(w0v) * sinv, 0, false);
+                        pk = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w1v) * sinv,
+                                                             bf16_hi(w1v) * sinv, pk, true);
+                        c[h] = uint32_t(pk);
+                    }
+                    codes = make_uint2(c[0], c[1]);
+                } else {
+                    // an infinity or NaN in the block: the general path
+                    float f[8];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        f[2 * q] = bf16_lo(vv[k][q]);
+                        f[2 * q + 1] = bf16_hi(vv[k][q]);
+                    }
+                    amax = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+                        amax = fmaxf(amax, fabsf(f[q]));
+                    amax = row16_fmax(amax);
+                    amax = amax < 1e-4f ? 1e-4f : amax;
+                    const float sinv = 448.0f / amax;
+                    uint32_t lo = 0, hi = 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        lo |= e4m3_rne(f[q] * sinv) << (8 * q);
+                        hi |= e4m3_rne(f[q + 4] * sinv) << (8 * q);
+                    }
+                    codes = make_uint2(lo, hi);
+                }
+                if (row[k] >= 0) {
+                    const int64_t cell = cell0 + row[k];
+                    const int64_t col = int64_t(blk[k]) * 16 + l16;
+                    packed_q[cell * V + col] = codes;  // 8 codes per lane
+                    if (l16 == 0)
+                        packed_scale[cell * nb + blk[k]] = amax / 448.0f;
+                }
+            }
+        }
+    }
 }
 
 template <int VPT>
 __global__ __launch_bounds__(kLLBlock) void ll_combine_kernel(
     const u32x4 *__restrict__ packed_y, int V, int K, int E, int R, int epr, int S,
     const int64_t *__restrict__ topk_idx, const float *__restrict__ topk_weights,
-    const int32_t *__restrict__ topk_slot, u32x4 *__restrict__ out)
+    const int32_t *__restrict__ topk_slot, const int32_t *__restrict__ rank_mask,
+    u32x4 *__restrict__ out)
 {
     __shared__ int64_t s_cell[kMaxTopk];
     __shared__ float s_w[kMaxTopk];
@@ -161,7 +322,8 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_kernel(
     if (tid < K) {
         const int64_t e = topk_idx[t * K + tid];
         const int s = topk_slot[t * K + tid];
-        const bool ok = e >= 0 && e < E && s >= 0 && s < S;
+        const bool ok = e >= 0 && e < E && s >= 0 && s < S &&
+                        !(rank_mask != nullptr && rank_mask[int(e) / epr] != 0);
         s_cell[tid] = ok ? ((int64_t(int(e) % epr) * R + int(e) / epr) * S + s) : -1;
         s_w[tid] = topk_weights[t * K + tid];
     }
@@ -223,20 +385,32 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_kernel(
 }  // namespace
 
 hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
-                              const int64_t *topk_idx, void *packed_x, int32_t *packed_count,
+                              const int64_t *topk_idx, const int32_t *rank_mask, void *packed_x,
+                              void *packed_q, float *packed_scale, int32_t *packed_count,
                               int32_t *src_info, int32_t *topk_slot, hipStream_t stream)
 {
     const int E = d.num_experts, R = d.num_ranks;
-    hipLaunchKernelGGL(ll_dispatch_kernel, dim3(E), dim3(kLLBlock), 0, stream,
+    const bool fp8 = packed_q != nullptr;
+    auto kernel = fp8 ? ll_dispatch_kernel<true> : ll_dispatch_kernel<false>;
+    // Copy splits per expert, from the expected rows per expert T*K/E: one
+    // workgroup round copies 2048 vectors (bf16) or 64 blocks (fp8).
+    const int64_t rows = (int64_t(d.num_tokens) * d.num_topk + E - 1) / E;
+    const int64_t work = fp8 ? rows * (d.hidden / 128) : rows * (d.hidden / 8);
+    const int64_t per = fp8 ? 64 : 2048;
+    int ny = int((work + per - 1) / per);
+    ny = ny < 1 ? 1 : (ny > 8 ? 8 : ny);
+    hipLaunchKernelGGL(kernel, dim3(E, ny), dim3(kLLBlock), 0, stream,
                        static_cast<const u32x4 *>(x), d.num_tokens, d.hidden / 8, d.num_topk, E,
-                       R, E / R, num_slots, topk_idx, static_cast<u32x4 *>(packed_x),
-                       packed_count, src_info, topk_slot);
+                       R, E / R, num_slots, topk_idx, rank_mask, static_cast<u32x4 *>(packed_x),
+                       static_cast<uint2 *>(packed_q), packed_scale, packed_count, src_info,
+                       topk_slot);
     return hipGetLastError();
 }
 
 hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed_y,
                              const int64_t *topk_idx, const float *topk_weights,
-                             const int32_t *topk_slot, void *out, hipStream_t stream)
+                             const int32_t *topk_slot, const int32_t *rank_mask, void *out,
+                             hipStream_t stream)
 {
     if (d.num_tokens == 0)
         return hipSuccess;
@@ -246,7 +420,8 @@ hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed
     const int chunks = (V + kLLBlock * VPT - 1) / (kLLBlock * VPT);
     hipLaunchKernelGGL((ll_combine_kernel<VPT>), dim3(d.num_tokens, chunks), dim3(kLLBlock), 0,
                        stream, static_cast<const u32x4 *>(packed_y), V, d.num_topk, E, R, E / R,
-                       num_slots, topk_idx, topk_weights, topk_slot, static_cast<u32x4 *>(out));
+                       num_slots, topk_idx, topk_weights, topk_slot, rank_mask,
+                       static_cast<u32x4 *>(out));
     return hipGetLastError();
 }
 

@@ -13,6 +13,8 @@
  *   [P4] "How DeepEP Optimizes Handle Reuse for Repeated Dispatches": "What
  *        the Handle Contains", "Fast Path Dispatch with Handle Reuse",
  *        "Performance Contract and Constraints".
+ *   [P5] "Chapter 10, V2: buffers beyond EP", section 10.2 (load-balance
+ *        operations over redundant experts).
  *
  * The R destination ranks are logical partitions of this GPU's memory: a
  * "segment" is a contiguous range of rows of one caller buffer.  Nothing here
@@ -28,8 +30,8 @@
  *   - Layouts are dense row-major.  bf16 tensors are 16-bit words.  topk_idx
  *     is int64 with -1 for a masked slot; weights are fp32.
  *   - Expert e belongs to rank e / (E/R) as local expert e % (E/R).
- *   - Alignment ([P3]): token-row pointers (x, recv_x, y, out, packed_x,
- *     packed_y) must be 16-byte aligned and hidden*2 must be a multiple of 16
+ *   - Alignment ([P3]): token-row pointers (x, recv_x, y, out, bias0, bias1,
+ *     packed_x, packed_y, load-balance tensors) must be 16-byte aligned and hidden*2 must be a multiple of 16
  *     (rows are whole int4 vectors); int64 arrays 8-byte, others 4-byte
  *     aligned.  Violations return EP_ERR_ALIGN before any work is enqueued.
  *   - Expert ids outside [-1, E) are invalid input.  The kernels ignore such
@@ -169,8 +171,12 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
  * y [y_rows][hidden] (bf16, same segment layout as the dispatch that made
  * handle) back to token order:
  *   out[t] = bf16_rne( sum over ranks r ascending that t went to of
- *                      fp32(y[S[r] + send_head[t][r]]) ),  fp32 accumulation
- *   starting at +0; a token that went nowhere gets +0.
+ *                      fp32(y[S[r] + send_head[t][r]])
+ *                      + fp32(bias0[t]) + fp32(bias1[t]) ),
+ *   fp32 accumulation starting at +0, in that order; a token that went
+ *   nowhere gets the bias sum (+0 without bias).
+ * bias0, bias1 [T][hidden] bf16 (each nullable): the optional bias terms of
+ *   the same section, added after the rank sum, before the one rounding.
  * recv_topk_weights [y_rows][K] fp32 (nullable) and combined_topk_weights
  * [T][K] fp32 (nullable, needs the former): the same ascending-rank fp32 sum
  * of the per-row weights (the reduced weights combine returns).
@@ -178,8 +184,8 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
  * when y_rows >= ep_max_recv_rows(), else N is read once per handle).
  */
 int ep_combine(ep_handle *handle, int32_t hidden, const void *y, int64_t y_rows,
-               const float *recv_topk_weights, void *out, float *combined_topk_weights,
-               ep_stream_t stream);
+               const float *recv_topk_weights, const void *bias0, const void *bias1, void *out,
+               float *combined_topk_weights, ep_stream_t stream);
 
 /*
  * [P1] "IB-GDA Kernels", low_latency_dispatch: stream every valid (token,
@@ -194,10 +200,31 @@ int ep_combine(ep_handle *handle, int32_t hidden, const void *y, int64_t y_rows,
  * (EP_ERR_CAPACITY); pairs past num_slots (possible only when a token names
  * one expert twice) are dropped and still counted.  Unused packed_x cells
  * are not written.  packed_x may be NULL (metadata only).  No host sync.
+ * rank_mask [R] int32 (nullable; [P1] "Dynamic Rank Masking"): nonzero
+ *   marks a masked rank, whose experts receive nothing (count 0, no slots;
+ *   their pairs get topk_slot -1), as if those slots were masked.
  */
 int ep_ll_dispatch(const ep_dims *dims, int32_t num_slots, const void *x,
-                   const int64_t *topk_idx, void *packed_x, int32_t *packed_count,
-                   int32_t *src_info, int32_t *topk_slot, ep_stream_t stream);
+                   const int64_t *topk_idx, const int32_t *rank_mask, void *packed_x,
+                   int32_t *packed_count, int32_t *src_info, int32_t *topk_slot,
+                   ep_stream_t stream);
+
+/*
+ * ep_ll_dispatch with an FP8 payload ([P1] "IB-GDA Kernels": FP8 with
+ * use_fp8, which the pages' code example sets on the dispatch).  Slots,
+ * counts, src_info and topk_slot are exactly those of ep_ll_dispatch.
+ * Every sent row is cut into 128-element blocks; per block
+ *   amax = max(max |x|, 1e-4), q = e4m3(x * (448 / amax)), scale = amax / 448
+ * in fp32, e4m3 being OCP FP8 E4M3 ("e4m3fn") with round to nearest even,
+ * saturating at +-448.  x ~ q * scale.
+ *   packed_q     [E/R][R][num_slots][H]     uint8 codes (8-byte aligned)
+ *   packed_scale [E/R][R][num_slots][H/128] fp32
+ * Requires hidden % 128 == 0 (EP_ERR_ALIGN).  Unused cells are not written.
+ */
+int ep_ll_dispatch_fp8(const ep_dims *dims, int32_t num_slots, const void *x,
+                       const int64_t *topk_idx, const int32_t *rank_mask, void *packed_q,
+                       float *packed_scale, int32_t *packed_count, int32_t *src_info,
+                       int32_t *topk_slot, ep_stream_t stream);
 
 /*
  * [P1] "IB-GDA Kernels", low_latency_combine: for every token,
@@ -205,11 +232,45 @@ int ep_ll_dispatch(const ep_dims *dims, int32_t num_slots, const void *x,
  * over k ascending, valid non-dropped slots only, from acc = +0, where cell
  * (t, k) is the packed_y row [le][r][topk_slot[t][k]] of the slot's expert.
  * packed_y has packed_x's layout; topk_slot comes from ep_ll_dispatch.
- * No host sync.
+ * rank_mask [R] (nullable): pairs whose expert sits on a rank masked now
+ * contribute nothing, whatever the dispatch did.  No host sync.
  */
 int ep_ll_combine(const ep_dims *dims, int32_t num_slots, const void *packed_y,
                   const int64_t *topk_idx, const float *topk_weights,
-                  const int32_t *topk_slot, void *out, ep_stream_t stream);
+                  const int32_t *topk_slot, const int32_t *rank_mask, void *out,
+                  ep_stream_t stream);
+
+/* [P1] "Dynamic Rank Masking" on a caller-owned device mask rank_mask[R]
+ * (0 active, 1 masked), stream-ordered like the other calls:
+ *   ep_mask_update  set rank `rank` to masked (nonzero) or active (0)
+ *   ep_mask_clean   set every rank active
+ *   ep_mask_query   copy the mask to host_out[R] (HOST pointer); this call
+ *                   synchronizes the stream. */
+int ep_mask_update(int32_t *rank_mask, int32_t num_ranks, int32_t rank, int32_t masked,
+                   ep_stream_t stream);
+int ep_mask_clean(int32_t *rank_mask, int32_t num_ranks, ep_stream_t stream);
+int ep_mask_query(const int32_t *rank_mask, int32_t num_ranks, int32_t *host_out,
+                  ep_stream_t stream);
+
+/*
+ * Load balancing over redundant expert replicas ([P5] 10.2): replica j is a
+ * copy of expert mapping[j] (mapping: int64 [num_replicas], device; entries
+ * outside [0, num_experts) are ignored).  Tensors are bf16, one row of
+ * elems_per_expert elements per expert / replica (elems % 8 == 0, 16-byte
+ * aligned rows).
+ *   ep_lb_prefetch_weights: redundant[j] = expert[mapping[j]] (bit copy).
+ *   ep_lb_reduce_grads: for every expert e with replicas,
+ *     expert[e] = bf16_rne(fp32(expert[e]) + sum over j ascending with
+ *                          mapping[j] == e of fp32(redundant[j])),
+ *     in place; experts without replicas are untouched.
+ * num_replicas <= 65535.  No host sync.
+ */
+int ep_lb_prefetch_weights(const void *expert_weights, void *redundant_weights,
+                           const int64_t *mapping, int32_t num_replicas, int32_t num_experts,
+                           int64_t elems_per_expert, ep_stream_t stream);
+int ep_lb_reduce_grads(const void *redundant_grads, void *expert_grads, const int64_t *mapping,
+                       int32_t num_replicas, int32_t num_experts, int64_t elems_per_expert,
+                       ep_stream_t stream);
 
 /* Copy the handle's layout into caller buffers (fields may be NULL); same
  * shapes and capacity rule as ep_get_dispatch_layout. */

@@ -655,6 +655,65 @@ def check_ll_fp8(inp, rank_mask=None):
     return q, sc
 
 
+def fp8_nonfinite_case(seed=5):
+    """A decode batch with infinities and NaNs in some 128-element blocks:
+    a lone +inf, a lone -inf, lone NaNs of both signs, an all-NaN block and
+    a block holding both an infinity and a NaN."""
+    inp = random_case(seed, 40, 512, 16, 4, 4, 1, slots=40)
+    x = inp.x.copy()
+    x[0, 5] = 0x7F80        # +inf in block 0
+    x[0, 200] = 0xFF80      # -inf in block 1
+    x[1, 300] = 0x7FC0      # NaN in block 2
+    x[1, 301] = 0xFFC1      # negative NaN, same block
+    x[2, 0:128] = 0x7FC0    # a block of NaNs only
+    x[3, 384] = 0x7F80      # +inf and NaN in block 3
+    x[3, 385] = 0xFFC0
+    inp.x = x
+    return inp
+
+
+def e4m3_is_nan(code):
+    return (np.asarray(code) & 0x7F) == 0x7F
+
+
+def check_ll_fp8_nonfinite():
+    """IEEE arithmetic carried through the FP8 recipe: NaNs do not raise a
+    block's amax (max ignores them), an infinite amax makes the scale infinite
+    and 448/amax zero, so finite values become signed zeros and infinities
+    (inf * 0) and NaNs become NaN codes.  The sign of a NaN is not fixed by
+    IEEE 754, so only NaN-ness is checked there."""
+    inp = fp8_nonfinite_case()
+    E, R, S = inp.E, inp.R, inp.slots
+    q, sc, _, src, _ = O.ll_dispatch_fp8(inp.x, inp.topk_idx, E, R, S)
+    xf = f32_from_bits(inp.x)
+    checked = 0
+    for le in range(E // R):
+        for r in range(R):
+            for s_ in range(S):
+                t = src[le, r, s_]
+                if t < 0 or t > 3:
+                    continue
+                for b in range(inp.x.shape[1] // 128):
+                    blk = xf[t, b * 128:(b + 1) * 128]
+                    code = q[le, r, s_, b * 128:(b + 1) * 128].astype(np.int64)
+                    fin = np.isfinite(blk)
+                    finite_amax = np.abs(blk[~np.isnan(blk)]).max(initial=0.0)
+                    if np.isinf(finite_amax):
+                        assert np.isinf(sc[le, r, s_, b])
+                        assert np.all(e4m3_is_nan(code[~fin]))
+                        assert np.all(code[fin] == np.where(np.signbit(blk[fin]), 0x80, 0))
+                    else:
+                        amax = np.float32(max(finite_amax, np.float32(1e-4)))
+                        assert sc[le, r, s_, b] == np.float32(amax / np.float32(448.0))
+                        assert np.all(e4m3_is_nan(code[np.isnan(blk)]))
+                        sinv = np.float32(np.float32(448.0) / amax)
+                        exp = O.f32_to_e4m3((blk[fin] * sinv).astype(np.float32)).astype(np.int64)
+                        np.testing.assert_array_equal(code[fin], exp)
+                    checked += 1
+    assert checked >= 16
+    return q, sc
+
+
 # -------------------------------------------------------- exact tie rounding
 
 

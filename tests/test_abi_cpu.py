@@ -60,7 +60,7 @@ def test_product_package_never_touches_the_oracle():
 
 
 def test_version_and_status_text():
-    assert abi.version() == (1, 0)
+    assert abi.version() == (1, 1)
     for code in range(7):
         assert L.ep_status_str(code)
     assert L.ep_status_str(99) == b"unknown status"
@@ -128,7 +128,7 @@ def test_argument_rules_rejected_before_device_work():
 
 
 def test_combine_and_handle_calls_without_handle():
-    assert L.ep_combine(None, 64, None, 0, None, None, None, S) == abi.EP_ERR_HANDLE
+    assert L.ep_combine(None, 64, None, 0, None, None, None, None, None, S) == abi.EP_ERR_HANDLE
     n = ctypes.c_int64()
     assert L.ep_handle_num_recv(None, ctypes.byref(n)) == abi.EP_ERR_HANDLE
     assert L.ep_handle_copy_layout(None, None, S) == abi.EP_ERR_HANDLE
@@ -141,20 +141,44 @@ def test_low_latency_rules():
     d = abi.dims(129, 64, 2, 8, 4, 1)
     fake = ctypes.c_void_p(0x10000)
     # more tokens than slots per (local expert, rank)
-    assert L.ep_ll_dispatch(ctypes.byref(d), 128, fake, fake, fake, fake, fake, fake,
+    assert L.ep_ll_dispatch(ctypes.byref(d), 128, fake, fake, None, fake, fake, fake, fake,
                             S) == abi.EP_ERR_CAPACITY
-    assert L.ep_ll_combine(ctypes.byref(d), 128, fake, fake, fake, fake, fake,
+    assert L.ep_ll_combine(ctypes.byref(d), 128, fake, fake, fake, fake, None, fake,
                            S) == abi.EP_ERR_CAPACITY
     d = abi.dims(16, 64, 2, 8, 4, 1)
-    assert L.ep_ll_dispatch(ctypes.byref(d), 0, fake, fake, fake, fake, fake, fake,
+    assert L.ep_ll_dispatch(ctypes.byref(d), 0, fake, fake, None, fake, fake, fake, fake,
                             S) == abi.EP_ERR_INVALID
-    assert L.ep_ll_dispatch(ctypes.byref(d), 5000, fake, fake, fake, fake, fake, fake,
+    assert L.ep_ll_dispatch(ctypes.byref(d), 5000, fake, fake, None, fake, fake, fake, fake,
                             S) == abi.EP_ERR_INVALID
     # missing metadata outputs
-    assert L.ep_ll_dispatch(ctypes.byref(d), 16, fake, fake, fake, None, fake, fake,
+    assert L.ep_ll_dispatch(ctypes.byref(d), 16, fake, fake, None, fake, None, fake, fake,
                             S) == abi.EP_ERR_INVALID
-    # misaligned packed buffer
-    assert L.ep_ll_dispatch(ctypes.byref(d), 16, fake, fake, ctypes.c_void_p(0x10008), fake, fake,
-                            fake, S) == abi.EP_ERR_ALIGN
-    assert L.ep_ll_combine(ctypes.byref(d), 16, fake, fake, fake, fake, None,
+    # misaligned packed buffer / mask
+    assert L.ep_ll_dispatch(ctypes.byref(d), 16, fake, fake, None, ctypes.c_void_p(0x10008), fake,
+                            fake, fake, S) == abi.EP_ERR_ALIGN
+    assert L.ep_ll_dispatch(ctypes.byref(d), 16, fake, fake, ctypes.c_void_p(0x10002), fake, fake,
+                            fake, fake, S) == abi.EP_ERR_ALIGN
+    assert L.ep_ll_combine(ctypes.byref(d), 16, fake, fake, fake, fake, None, None,
                            S) == abi.EP_ERR_INVALID
+    # FP8: rows must be whole 128-element blocks; scales required
+    assert L.ep_ll_dispatch_fp8(ctypes.byref(d), 16, fake, fake, None, fake, fake, fake, fake,
+                                fake, S) == abi.EP_ERR_ALIGN
+    d = abi.dims(16, 128, 2, 8, 4, 1)
+    assert L.ep_ll_dispatch_fp8(ctypes.byref(d), 16, fake, fake, None, fake, None, fake, fake,
+                                fake, S) == abi.EP_ERR_INVALID
+
+
+def test_mask_and_load_balance_rules():
+    fake = ctypes.c_void_p(0x10000)
+    assert L.ep_mask_update(None, 4, 0, 1, S) == abi.EP_ERR_INVALID
+    assert L.ep_mask_update(fake, 4, 4, 1, S) == abi.EP_ERR_INVALID
+    assert L.ep_mask_update(fake, 4, -1, 1, S) == abi.EP_ERR_INVALID
+    assert L.ep_mask_clean(fake, 0, S) == abi.EP_ERR_INVALID
+    assert L.ep_mask_query(fake, 4, None, S) == abi.EP_ERR_INVALID
+    assert L.ep_mask_update(ctypes.c_void_p(0x10002), 4, 1, 1, S) == abi.EP_ERR_ALIGN
+    for fn in (L.ep_lb_reduce_grads, L.ep_lb_prefetch_weights):
+        assert fn(fake, fake, fake, 4, 8, 12, S) == abi.EP_ERR_ALIGN      # rows not 16-byte vectors
+        assert fn(fake, fake, fake, -1, 8, 16, S) == abi.EP_ERR_INVALID
+        assert fn(fake, fake, fake, 70000, 8, 16, S) == abi.EP_ERR_INVALID
+        assert fn(None, fake, fake, 4, 8, 16, S) == abi.EP_ERR_INVALID
+        assert fn(fake, fake, ctypes.c_void_p(0x10004), 4, 8, 16, S) == abi.EP_ERR_ALIGN

@@ -212,8 +212,8 @@ def test_errors_and_reuse_contract():
     assert rc == abi.EP_ERR_CAPACITY
     assert bool((small.view(torch.int16) == 7).all())
     out = torch.empty((inp.T, inp.H), dtype=torch.bfloat16, device="cuda")
-    rc = abi.lib().ep_combine(h.raw, inp.H, abi.ptr(small), n - 1, None, abi.ptr(out), None,
-                              abi.current_stream())
+    rc = abi.lib().ep_combine(h.raw, inp.H, abi.ptr(small), n - 1, None, None, None,
+                              abi.ptr(out), None, abi.current_stream())
     assert rc == abi.EP_ERR_CAPACITY
     # misaligned row pointer
     off = torch.empty((n + 1, inp.H), dtype=torch.bfloat16, device="cuda")
@@ -283,8 +283,8 @@ def test_guard_bands_and_determinism():
         assert np.all(b[:G] == 0x7FC1) and np.all(b[G + N:] == 0x7FC1)
         obig = torch.full((inp.T + 2 * G, H), 0x7FC1, dtype=torch.int16, device="cuda")
         out = obig[G:G + inp.T].view(torch.bfloat16)
-        rc = abi.lib().ep_combine(raw, H, abi.ptr(recv), cap, None, abi.ptr(out), None,
-                                  abi.current_stream())
+        rc = abi.lib().ep_combine(raw, H, abi.ptr(recv), cap, None, None, None, abi.ptr(out),
+                                  None, abi.current_stream())
         assert rc == abi.EP_OK
         ob = host(obig)
         assert np.all(ob[:G] == 0x7FC1) and np.all(ob[G + inp.T:] == 0x7FC1)

@@ -138,3 +138,7 @@ def test_tie_rounding():
 
 def test_ll_fp8_zero_and_tiny_blocks():
     pinlib.check_ll_fp8(pinlib.fp8_edge_case())
+
+
+def test_ll_fp8_nonfinite_blocks():
+    pinlib.check_ll_fp8_nonfinite()
