@@ -38,11 +38,11 @@ def _configure(lib):
     p, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.oracle_f32_to_bf16.argtypes = [p, p, i64]
     lib.oracle_f32_to_bf16.restype = None
-    lib.oracle_layout.argtypes = [i64] * 5 + [p] * 9 + [i64]
+    lib.oracle_layout.argtypes = [i64] * 5 + [p] * 10 + [i64]
     lib.oracle_layout.restype = i64
     lib.oracle_dispatch.argtypes = [i64] * 5 + [p] * 8
     lib.oracle_dispatch.restype = None
-    lib.oracle_combine.argtypes = [i64] * 4 + [p] * 8
+    lib.oracle_combine.argtypes = [i64] * 4 + [p] * 9
     lib.oracle_combine.restype = None
     lib.oracle_ll_dispatch.argtypes = [i64] * 6 + [p] * 7
     lib.oracle_ll_dispatch.restype = ctypes.c_int
@@ -105,8 +105,11 @@ class Layout:
         return int(self.recv_src_idx.shape[0])
 
 
-def layout(topk_idx: np.ndarray, E: int, R: int, C: int) -> Layout:
+def layout(topk_idx: np.ndarray, E: int, R: int, C: int, rank_mask=None) -> Layout:
+    """rank_mask: optional int32 [R], nonzero = masked rank (its slots act as
+    masked slots)."""
     topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    m = _mask(rank_mask, R)
     T, K = topk_idx.shape
     cap = T * min(K, R)
     ntpr = np.empty(R, np.int32)
@@ -117,7 +120,7 @@ def layout(topk_idx: np.ndarray, E: int, R: int, C: int) -> Layout:
     rcpm = np.empty((R, C), np.int32)
     sh = np.empty((T, R), np.int32)
     rsi = np.empty(max(cap, 1), np.int32)
-    n = _load().oracle_layout(T, K, E, R, C, _ptr(topk_idx), _ptr(ntpr), _ptr(ntpe), _ptr(itr),
+    n = _load().oracle_layout(T, K, E, R, C, _ptr(topk_idx), _ptr(m), _ptr(ntpr), _ptr(ntpe), _ptr(itr),
                               _ptr(rpm), _ptr(cpm), _ptr(rcpm), _ptr(sh), _ptr(rsi), cap)
     if n < 0:
         raise ValueError("oracle_layout rejected its arguments")
@@ -148,9 +151,10 @@ def dispatch(x: np.ndarray, topk_idx, topk_weights, E: int, R: int, lay: Layout,
 
 
 def combine(y: np.ndarray, lay: Layout, recv_topk_weights=None, K: int = 0, bias0=None,
-            bias1=None):
+            bias1=None, rank_mask=None):
     """Returns (out bf16 bits [T, H], combined_topk_weights [T, K] or None).
-    bias0 / bias1: optional bf16 bits [T, H] added after the rank sum."""
+    bias0 / bias1: optional bf16 bits [T, H] added after the rank sum.
+    rank_mask: optional int32 [R]; masked ranks are skipped."""
     y = np.ascontiguousarray(y, dtype=np.uint16)
     T, R = lay.send_head.shape
     H = y.shape[1]
@@ -165,8 +169,9 @@ def combine(y: np.ndarray, lay: Layout, recv_topk_weights=None, K: int = 0, bias
     b1 = None if bias1 is None else np.ascontiguousarray(bias1, dtype=np.uint16)
     for b in (b0, b1):
         assert b is None or b.shape == (T, H)
+    m = _mask(rank_mask, R)
     _load().oracle_combine(T, H, max(K, 1), R, _ptr(y), _ptr(rw), _ptr(lay.rank_prefix_matrix),
-                           _ptr(lay.send_head), _ptr(b0), _ptr(b1), _ptr(out), _ptr(cw))
+                           _ptr(lay.send_head), _ptr(b0), _ptr(b1), _ptr(m), _ptr(out), _ptr(cw))
     return out, cw
 
 

@@ -67,6 +67,13 @@ void oracle_f32_to_bf16(const float *in, uint16_t *out, int64_t n)
 
 /* --------------------------------------------------------------- layout --- */
 
+/* [P1] "Dynamic Rank Masking": rank r is masked when rank_mask is given and
+ * rank_mask[r] is nonzero (1 = masked, 0 = active). */
+static int rank_masked(const int32_t *rank_mask, int64_t r)
+{
+    return rank_mask != NULL && rank_mask[r] != 0;
+}
+
 /* Channel c covers tokens [min(c*per, T), min((c+1)*per, T)) with
  * per = ceil(T / C).  Reading: "channels" are contiguous token ranges of equal
  * length, the last one short (or empty when C does not divide the tokens). */
@@ -99,10 +106,13 @@ static int64_t channel_end(int64_t c, int64_t T, int64_t C)
  *                             -1 when t does not go to r.
  *   recv_src_idx[N]           source token of each packed row: the inverse of
  *                             send_head, N = rank_prefix_matrix[R-1].
+ * rank_mask[R] (nullable): reading of "Dynamic Rank Masking" for this path: a
+ * slot whose expert lives on a masked rank is treated exactly like a masked
+ * slot, so a masked rank receives nothing and its experts count 0.
  * Returns N, or -1 on invalid arguments.
  */
 int64_t oracle_layout(int64_t T, int64_t K, int64_t E, int64_t R, int64_t C,
-                      const int64_t *topk_idx,
+                      const int64_t *topk_idx, const int32_t *rank_mask,
                       int32_t *num_tokens_per_rank, int32_t *num_tokens_per_expert,
                       uint8_t *is_token_in_rank, int32_t *rank_prefix_matrix,
                       int32_t *channel_prefix_matrix, int32_t *recv_channel_prefix_matrix,
@@ -122,6 +132,8 @@ int64_t oracle_layout(int64_t T, int64_t K, int64_t E, int64_t R, int64_t C,
                 continue; /* masked slot: takes part in nothing */
             if (e >= E)
                 return -1;
+            if (rank_masked(rank_mask, e / epr))
+                continue; /* expert on a masked rank: as a masked slot */
             num_tokens_per_expert[e] += 1;
             is_token_in_rank[t * R + e / epr] = 1;
         }
@@ -232,11 +244,13 @@ void oracle_dispatch(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R,
  * the rank sum and before the single rounding to bf16.
  * The optional weight output is the same reduction of recv_topk_weights,
  * kept in fp32 (the reduced weights the pages' combine returns).
+ * rank_mask[R] (nullable, "Dynamic Rank Masking"): ranks masked at combine
+ * time are skipped, as if t had not gone there (rows and weights).
  */
 void oracle_combine(int64_t T, int64_t H, int64_t K, int64_t R,
                     const uint16_t *y, const float *recv_topk_weights,
                     const int32_t *rank_prefix_matrix, const int32_t *send_head,
-                    const uint16_t *bias0, const uint16_t *bias1,
+                    const uint16_t *bias0, const uint16_t *bias1, const int32_t *rank_mask,
                     uint16_t *out, float *combined_topk_weights)
 {
     float *acc = (float *)malloc((size_t)(H > 0 ? H : 1) * sizeof(float));
@@ -245,6 +259,8 @@ void oracle_combine(int64_t T, int64_t H, int64_t K, int64_t R,
             acc[h] = 0.0f;
         for (int64_t r = 0; r < R; ++r) {
             int32_t p = send_head[t * R + r];
+            if (rank_masked(rank_mask, r))
+                continue;
             if (p < 0)
                 continue;
             int64_t row = (r > 0 ? rank_prefix_matrix[r - 1] : 0) + p;
@@ -265,7 +281,7 @@ void oracle_combine(int64_t T, int64_t H, int64_t K, int64_t R,
                 float w = 0.0f;
                 for (int64_t r = 0; r < R; ++r) {
                     int32_t p = send_head[t * R + r];
-                    if (p < 0)
+                    if (p < 0 || rank_masked(rank_mask, r))
                         continue;
                     int64_t row = (r > 0 ? rank_prefix_matrix[r - 1] : 0) + p;
                     w += recv_topk_weights[row * K + k];

@@ -473,6 +473,68 @@ def check_ll_mask_extremes(inp):
     assert np.all((out & 0x7FFF) == 0)
 
 
+def check_layout_rank_mask(inp, rank_mask):
+    """Normal-path masking: the masked layout is the sorted-pair brute force
+    of the table whose slots on masked ranks are set to -1; masked ranks get
+    no tokens, their experts count 0, and the dispatch rows follow."""
+    E, R, C, T = inp.E, inp.R, inp.C, inp.T
+    m = np.asarray(rank_mask, np.int32)
+    L = O.layout(inp.topk_idx, E, R, C, rank_mask=m)
+    idx2 = masked_topk(inp.topk_idx, E, R, m)
+    _compare_layout(L, brute_layout(idx2, E, R, C), T, R, C)
+    epr = E // R
+    for r in np.nonzero(m)[0]:
+        assert L.num_tokens_per_rank[r] == 0
+        assert np.all(L.is_token_in_rank[:, r] == 0) and np.all(L.send_head[:, r] == -1)
+        assert np.all(L.num_tokens_per_expert[r * epr:(r + 1) * epr] == 0)
+    # dispatch of the masked layout = dispatch of the slot-masked table
+    a = O.dispatch(inp.x, inp.topk_idx, inp.topk_weights, E, R, L)
+    L2 = O.layout(idx2, E, R, C)
+    b = O.dispatch(inp.x, idx2, inp.topk_weights, E, R, L2)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    return L
+
+
+def check_combine_rank_mask(seed=0, T=80, H=48, E=24, K=4, R=6, C=3):
+    """A rank masked at combine time contributes nothing: the result equals
+    the unmasked combine of rows (and weights) in which that rank's segment
+    holds +0.  The fp32 accumulator starts at +0 and so never becomes -0;
+    adding +0 then leaves every value unchanged, which makes the two
+    bit-identical.  The identity combine counts only unmasked hits."""
+    inp = random_case(seed, T, H, E, K, R, C, mask=0.15)
+    L, rx, rtw = check_dispatch_props(inp)
+    rng = np.random.default_rng(seed + 11)
+    m = (rng.random(R) < 0.4).astype(np.int32)
+    m[0], m[-1] = 1, 0
+    yf = rng.standard_normal((L.num_recv, H)).astype(np.float32)
+    y = (yf.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    out, cw = O.combine(y, L, rtw, rank_mask=m)
+    y0, w0 = y.copy(), rtw.copy()
+    for r in np.nonzero(m)[0]:
+        a = L.rank_prefix_matrix[r - 1] if r > 0 else 0
+        b = L.rank_prefix_matrix[r]
+        y0[a:b] = 0
+        w0[a:b] = 0
+    out0, cw0 = O.combine(y0, L, w0)
+    np.testing.assert_array_equal(out, out0)
+    np.testing.assert_array_equal(cw.view(np.uint32), cw0.view(np.uint32))
+    # identity: n'_t unmasked copies of x_t sum exactly
+    outi, cwi = O.combine(rx, L, rtw, rank_mask=m)
+    n = (L.is_token_in_rank.astype(np.float32) * (1 - m)[None, :]).sum(axis=1)
+    exp = torch_bf16_bits(f32_from_bits(inp.x) * n[:, None])
+    np.testing.assert_array_equal(f32_from_bits(outi), f32_from_bits(exp))
+    epr = E // R
+    live = (inp.topk_idx >= 0) & (m[np.maximum(inp.topk_idx, 0) // epr] == 0)
+    np.testing.assert_array_equal(cwi, np.where(live, inp.topk_weights, np.float32(0)))
+    # nothing masked = the plain combine
+    outn, cwn = O.combine(y, L, rtw, rank_mask=np.zeros(R, np.int32))
+    outp, cwp = O.combine(y, L, rtw)
+    np.testing.assert_array_equal(outn, outp)
+    np.testing.assert_array_equal(cwn, cwp)
+    return m
+
+
 # -------------------------------------------------------------- combine bias
 
 

@@ -58,6 +58,12 @@ MUTANTS = [
     ("fp8 amax floor dropped", "if (amax < 1e-4f)\n                amax = 1e-4f;",
      "if (amax < 0.0f)\n                amax = 1e-4f;"),
     ("reduce grads from zero", "acc[p] = bf16_to_f32(expert_grads[e * P + p]);", "acc[p] = 0.0f;"),
+    ("layout rank mask ignored", "if (rank_masked(rank_mask, e / epr))",
+     "if (0 && rank_masked(rank_mask, e / epr))"),
+    ("combine rank mask ignored", "            if (rank_masked(rank_mask, r))\n                continue;",
+     "            if (0)\n                continue;"),
+    ("combine weights ignore the rank mask", "if (p < 0 || rank_masked(rank_mask, r))",
+     "if (p < 0)"),
     ("prefetch ignores mapping", "memcpy(redundant_weights + j * P, expert_weights + e * P,",
      "memcpy(redundant_weights + j * P, expert_weights + j % E * P,"),
 ]
@@ -81,6 +87,9 @@ def quick_pins():
     pinlib.check_ll_rank_mask(random_case(8, 50, 24, 16, 4, 8, 1, mask=0.1, dup=0.3, slots=60), m)
     pinlib.check_ll_mask_extremes(random_case(9, 30, 16, 8, 3, 4, 1, slots=30))
     pinlib.check_combine_bias(0)
+    pinlib.check_layout_rank_mask(random_case(21, 60, 8, 24, 5, 6, 4, mask=0.1, dup=0.2),
+                                  np.array([0, 1, 0, 1, 0, 0], np.int32))
+    pinlib.check_combine_rank_mask(0)
     pinlib.check_lb_ops(0)
     pinlib.check_e4m3()
     pinlib.check_ll_fp8(random_case(4, 40, 256, 16, 4, 4, 1, mask=0.2, slots=40))

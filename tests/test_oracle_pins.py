@@ -142,3 +142,37 @@ def test_ll_fp8_zero_and_tiny_blocks():
 
 def test_ll_fp8_nonfinite_blocks():
     pinlib.check_ll_fp8_nonfinite()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_layout_rank_mask_random(seed):
+    inp = random_case(20 + seed, 150, 8, 24, 5, 6, 4, mask=0.1, dup=0.2)
+    m = np.zeros(6, np.int32)
+    m[[seed % 6, (seed + 3) % 6]] = 1
+    pinlib.check_layout_rank_mask(inp, m)
+
+
+def test_layout_rank_mask_full_config():
+    inp = config_inputs(2, with_x=False)
+    inp.x = random_case(0, inp.T, 8, inp.E, inp.K, inp.R, inp.C).x
+    m = np.zeros(inp.R, np.int32)
+    m[[0, 7, 31]] = 1
+    pinlib.check_layout_rank_mask(inp, m)
+
+
+def test_layout_rank_mask_exhaustive_tiny():
+    """Every table over {-1, 0..3} for T=2, K=2 under every mask of R=2."""
+    import itertools
+    for flat in itertools.product(range(-1, 4), repeat=4):
+        idx = np.array(flat, np.int64).reshape(2, 2)
+        for mk in itertools.product((0, 1), repeat=2):
+            m = np.array(mk, np.int32)
+            for C in (1, 3):
+                L = __import__("oracle").layout(idx, 4, 2, C, rank_mask=m)
+                B = pinlib.brute_layout(pinlib.masked_topk(idx, 4, 2, m), 4, 2, C)
+                pinlib._compare_layout(L, B, 2, 2, C)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_combine_rank_mask(seed):
+    pinlib.check_combine_rank_mask(seed)
