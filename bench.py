@@ -171,20 +171,20 @@ def main():
 
         h = ctypes.c_void_p()
         mark(0)
-        abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, ctypes.byref(h), s),
-                  "layout")
+        abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, None, ctypes.byref(h),
+                                           s), "layout")
         mark(1)
         if roof_events is not None:
             roof_events[0].record()
-        abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), ctypes.byref(h), P(recv_x),
-                                P(rti), P(rtw), cap, None, s), "dispatch")
+        abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), None, ctypes.byref(h),
+                                P(recv_x), P(rti), P(rtw), cap, None, s), "dispatch")
         if roof_events is not None:
             roof_events[1].record()
         mark(2)
-        abi.check(L.ep_dispatch(ctypes.byref(d), P(x2), None, None, ctypes.byref(h), P(recv_x2),
-                                None, None, cap, None, s), "cached dispatch")
+        abi.check(L.ep_dispatch(ctypes.byref(d), P(x2), None, None, None, ctypes.byref(h),
+                                P(recv_x2), None, None, cap, None, s), "cached dispatch")
         mark(3)
-        abi.check(L.ep_combine(h, H, P(recv_x), cap, P(rtw), None, None, P(out), P(cw), s),
+        abi.check(L.ep_combine(h, H, P(recv_x), cap, P(rtw), None, None, None, P(out), P(cw), s),
                   "combine")
         mark(4)
         L.ep_handle_free(h)
@@ -199,7 +199,7 @@ def main():
     step()
     torch.cuda.synchronize()
     h = ctypes.c_void_p()
-    abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, ctypes.byref(h),
+    abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, None, ctypes.byref(h),
                                        abi.current_stream()), "layout")
     n = ctypes.c_int64()
     abi.check(L.ep_handle_num_recv(h, ctypes.byref(n)), "num_recv")
@@ -361,15 +361,15 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     s = abi.current_stream()
     # combine with two bias rows
     h = ctypes.c_void_p()
-    abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), ctypes.byref(h), P(recv_x),
-                            None, P(rtw), cap, None, s), "dispatch")
+    abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), None, ctypes.byref(h),
+                            P(recv_x), None, P(rtw), cap, None, s), "dispatch")
     n = ctypes.c_int64()
     abi.check(L.ep_handle_num_recv(h, ctypes.byref(n)), "num_recv")
     N = int(n.value)
     b0 = torch.from_numpy(random_rows(T, H, 0, tag=21).view(np.int16)).to(dev)
     b1 = torch.from_numpy(random_rows(T, H, 0, tag=22).view(np.int16)).to(dev)
-    us = timed(lambda: abi.check(L.ep_combine(h, H, P(recv_x), cap, P(rtw), P(b0), P(b1), P(out),
-                                              P(cw), s), "combine"), args.steps)
+    us = timed(lambda: abi.check(L.ep_combine(h, H, P(recv_x), cap, P(rtw), P(b0), P(b1), None,
+                                              P(out), P(cw), s), "combine"), args.steps)
     byt = (N + T) * H * 2 + N * 4 + N * K * 4 + T * K * 4 + 2 * T * H * 2
     rep["combine_with_bias"] = {"avg_us": round(us, 2), "bytes": byt,
                                 "gbs": round(byt / (us * 1e-6) / 1e9, 1)}

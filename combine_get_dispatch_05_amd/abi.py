@@ -74,10 +74,10 @@ def _load():
     pdims, pout = ctypes.POINTER(Dims), ctypes.POINTER(LayoutOut)
     sig = {
         "ep_max_recv_rows": (i64, [pdims]),
-        "ep_get_dispatch_layout": (ctypes.c_int, [pdims, vp, pout, ctypes.POINTER(vp), vp]),
-        "ep_dispatch": (ctypes.c_int, [pdims, vp, vp, vp, ctypes.POINTER(vp), vp, vp, vp, i64,
+        "ep_get_dispatch_layout": (ctypes.c_int, [pdims, vp, vp, pout, ctypes.POINTER(vp), vp]),
+        "ep_dispatch": (ctypes.c_int, [pdims, vp, vp, vp, vp, ctypes.POINTER(vp), vp, vp, vp, i64,
                                        ctypes.POINTER(i64), vp]),
-        "ep_combine": (ctypes.c_int, [vp, i32, vp, i64, vp, vp, vp, vp, vp, vp]),
+        "ep_combine": (ctypes.c_int, [vp, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "ep_ll_dispatch": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "ep_ll_dispatch_fp8": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "ep_ll_combine": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp]),

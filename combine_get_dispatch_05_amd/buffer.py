@@ -173,7 +173,9 @@ class Buffer:
     def get_dispatch_layout(self, topk_idx: torch.Tensor, keep_handle: bool = False):
         """Returns (num_tokens_per_rank [R], num_tokens_per_expert [E],
         is_token_in_rank [T, R] bool, handle or None).  A kept handle can be
-        passed to one ``dispatch`` together with the same ``topk_idx``."""
+        passed to one ``dispatch`` together with the same ``topk_idx``.
+        Ranks masked in the mask buffer receive nothing (their slots act as
+        masked slots)."""
         _need(topk_idx, torch.int64, "topk_idx", 2)
         T, K = topk_idx.shape
         d = self._dims(T, 8, K)
@@ -185,7 +187,7 @@ class Buffer:
                             None, None, 0)
         raw = ctypes.c_void_p()
         abi.check(abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk_idx),
-                                                   ctypes.byref(out),
+                                                   abi.ptr(self._mask), ctypes.byref(out),
                                                    ctypes.byref(raw) if keep_handle else None,
                                                    abi.current_stream()),
                   "ep_get_dispatch_layout")
@@ -199,7 +201,8 @@ class Buffer:
         recv_topk_weights [N, K] or None, num_recv_tokens_per_expert [R, E/R],
         handle, None).  Without a handle the layout is computed and N is read
         back (one host sync); with a handle from an earlier dispatch only the
-        rows are packed and topk arguments are refused."""
+        rows are packed and topk arguments are refused.  A fresh dispatch
+        leaves out the ranks masked in the mask buffer."""
         _need(x, torch.bfloat16, "x", 2)
         T, H = x.shape
         if handle is None and topk_idx is None:
@@ -221,8 +224,10 @@ class Buffer:
         rti = torch.empty((cap, K), dtype=torch.int64, device=dev) if topk_idx is not None else None
         rtw = torch.empty((cap, K), dtype=torch.float32, device=dev) if topk_weights is not None else None
         n = ctypes.c_int64(-1)
+        mask = abi.ptr(self._mask) if handle is None else None
         abi.check(abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), abi.ptr(topk_idx),
-                                        abi.ptr(topk_weights), ctypes.byref(raw), abi.ptr(recv_x),
+                                        abi.ptr(topk_weights), mask, ctypes.byref(raw),
+                                        abi.ptr(recv_x),
                                         abi.ptr(rti), abi.ptr(rtw), cap, ctypes.byref(n),
                                         abi.current_stream()),
                   "ep_dispatch")
@@ -249,7 +254,8 @@ class Buffer:
         """Returns (combined_x [T, H] bf16, combined_topk_weights [T, K] or
         None, None): the ascending-rank fp32 sum of each token's rows, plus
         the optional bias terms (a [T, H] bf16 tensor or a tuple of up to
-        two), added before the single rounding."""
+        two), added before the single rounding.  Ranks masked in the mask
+        buffer now are left out of the sums."""
         _need(x, torch.bfloat16, "x", 2)
         if topk_weights is not None:
             _need(topk_weights, torch.float32, "topk_weights", 2)
@@ -269,7 +275,8 @@ class Buffer:
         if topk_weights is not None:
             cw = torch.empty((T, d.num_topk), dtype=torch.float32, device=x.device)
         abi.check(abi.lib().ep_combine(handle.raw, H, abi.ptr(x), x.shape[0], abi.ptr(topk_weights),
-                                       abi.ptr(b0), abi.ptr(b1), abi.ptr(out), abi.ptr(cw),
+                                       abi.ptr(b0), abi.ptr(b1), abi.ptr(self._mask),
+                                       abi.ptr(out), abi.ptr(cw),
                                        abi.current_stream()),
                   "ep_combine")
         return out, cw, None

@@ -14,6 +14,11 @@
 // [T][H] tensors) are added in fp32 after the rank sum, bias0 then bias1,
 // before the single rounding.
 //
+// A rank mask given at combine time ("Dynamic Rank Masking": nonzero =
+// masked) drops that rank's rows and weights: the wavefront moves the live
+// entries of the row list to its front (a bijective lane permute) before
+// the sum, keeping their ascending order.
+//
 // The sum order is fixed (rank ascending, one add per row per element), so the
 // result does not depend on the launch shape.  U rows' loads are issued
 // before any of them is added, so each lane keeps U*VPT 16-byte loads in
@@ -62,7 +67,8 @@ __device__ __forceinline__ u32x4 load_row_vec(const u32x4 *p)
 template <int G, int VPT, int U, bool NTL, bool kBias>
 __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
     const u32x4 *__restrict__ y, int T, int V, int K, int kmax, int S,
-    const int32_t *__restrict__ dst_row, const float *__restrict__ recv_topk_weights,
+    const int32_t *__restrict__ dst_row, const int32_t *__restrict__ dst_rank,
+    const int32_t *__restrict__ rank_mask, const float *__restrict__ recv_topk_weights,
     const u32x4 *__restrict__ bias0, const u32x4 *__restrict__ bias1,
     u32x4 *__restrict__ out, float *__restrict__ combined_topk_weights)
 {
@@ -74,7 +80,16 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
     for (int ts = first; ts < T * S; ts += stride) {
         const int t = ts / S;
         const int slice = ts - t * S;
-        const int rowv = lane < kmax ? dst_row[int64_t(t) * kmax + lane] : -1;
+        int rowv = lane < kmax ? dst_row[int64_t(t) * kmax + lane] : -1;
+        if (rank_mask != nullptr) {
+            const int rk = rowv >= 0 ? dst_rank[int64_t(t) * kmax + lane] : 0;
+            const bool live = rowv >= 0 && rank_mask[rk] == 0;
+            const uint64_t lm = wave_ballot(live);
+            const uint64_t below = lanemask_lt();
+            const int nl = __popcll(lm);
+            const int to = live ? __popcll(lm & below) : nl + __popcll(~lm & below);
+            rowv = __builtin_amdgcn_ds_permute(to << 2, live ? rowv : -1);
+        }
         const int nhit = __popcll(wave_ballot(rowv >= 0));
 
         for (int base = slice * G * VPT; base < V; base += S * G * VPT) {
@@ -147,7 +162,8 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
 }
 
 typedef void (*CombineFn)(const u32x4 *, int, int, int, int, int, const int32_t *,
-                          const float *, const u32x4 *, const u32x4 *, u32x4 *, float *);
+                          const int32_t *, const int32_t *, const float *, const u32x4 *,
+                          const u32x4 *, u32x4 *, float *);
 
 // A launch shape: G lanes per group, VPT vectors per lane, S groups per token
 // (row slices), U rows in flight, NTL nontemporal row loads, and P =
@@ -242,7 +258,8 @@ void combine_tuning_at(int i, int *g, int *vpt, int *u)
 
 hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const LayoutBufs &b,
                           const float *recv_topk_weights, const void *bias0, const void *bias1,
-                          void *out, float *combined_topk_weights, hipStream_t stream)
+                          const int32_t *rank_mask, void *out, float *combined_topk_weights,
+                          hipStream_t stream)
 {
     if (s.T == 0)
         return hipSuccess;
@@ -256,7 +273,7 @@ hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const
     const bool bias = bias0 != nullptr || bias1 != nullptr;
     hipLaunchKernelGGL(bias ? c.fn_bias : c.fn, dim3(blocks), dim3(kCombineBlock), 0, stream,
                        static_cast<const u32x4 *>(y), s.T, V, s.K, s.kmax, c.S, b.dst_row,
-                       recv_topk_weights, static_cast<const u32x4 *>(bias0),
+                       b.dst_rank, rank_mask, recv_topk_weights, static_cast<const u32x4 *>(bias0),
                        static_cast<const u32x4 *>(bias1), static_cast<u32x4 *>(out),
                        combined_topk_weights);
     return hipGetLastError();

@@ -209,7 +209,8 @@ struct ep_handle {
 
 namespace {
 
-int create_handle(const ep_dims &d, const int64_t *topk_idx, hipStream_t stream, ep_handle **out)
+int create_handle(const ep_dims &d, const int64_t *topk_idx, const int32_t *rank_mask,
+                  hipStream_t stream, ep_handle **out)
 {
     ep_handle *h = new (std::nothrow) ep_handle();
     if (h == nullptr)
@@ -229,7 +230,7 @@ int create_handle(const ep_dims &d, const int64_t *topk_idx, hipStream_t stream,
         return rc;
     }
     h->bufs = layout_bufs_at(h->arena.ptr, off);
-    e = launch_layout(h->shape, topk_idx, h->bufs, stream);
+    e = launch_layout(h->shape, topk_idx, rank_mask, h->bufs, stream);
     h->last_stream = stream;
     if (e != hipSuccess) {
         ep_handle_free(h);
@@ -331,8 +332,8 @@ int64_t ep_max_recv_rows(const ep_dims *dims)
     return max_rows(*dims);
 }
 
-int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, ep_layout_out *out,
-                           ep_handle **handle_out, ep_stream_t stream_)
+int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, const int32_t *rank_mask,
+                           ep_layout_out *out, ep_handle **handle_out, ep_stream_t stream_)
 {
     try {
         int rc = check_dims(dims);
@@ -340,13 +341,13 @@ int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, ep_layo
             return rc;
         if (dims->num_tokens > 0 && topk_idx == nullptr)
             return EP_ERR_INVALID;
-        if (!aligned(topk_idx, 8))
+        if (!aligned(topk_idx, 8) || !aligned(rank_mask, 4))
             return EP_ERR_ALIGN;
         if (out == nullptr && handle_out == nullptr)
             return EP_ERR_INVALID;
         hipStream_t stream = static_cast<hipStream_t>(stream_);
         ep_handle *h = nullptr;
-        rc = create_handle(*dims, topk_idx, stream, &h);
+        rc = create_handle(*dims, topk_idx, rank_mask, stream, &h);
         if (rc != EP_OK)
             return rc;
         if (out != nullptr)
@@ -364,8 +365,8 @@ int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, ep_layo
 }
 
 int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
-                const float *topk_weights, ep_handle **handle, void *recv_x,
-                int64_t *recv_topk_idx, float *recv_topk_weights, int64_t recv_cap,
+                const float *topk_weights, const int32_t *rank_mask, ep_handle **handle,
+                void *recv_x, int64_t *recv_topk_idx, float *recv_topk_weights, int64_t recv_cap,
                 int64_t *num_recv, ep_stream_t stream_)
 {
     try {
@@ -377,7 +378,7 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
         const bool rows = dims->num_tokens > 0;
         if (!aligned(x, 16) || !aligned(recv_x, 16) || !aligned(topk_idx, 8) ||
             !aligned(recv_topk_idx, 8) || !aligned(topk_weights, 4) ||
-            !aligned(recv_topk_weights, 4))
+            !aligned(recv_topk_weights, 4) || !aligned(rank_mask, 4))
             return EP_ERR_ALIGN;
         if (recv_x != nullptr && x == nullptr && rows)
             return EP_ERR_INVALID;
@@ -397,13 +398,16 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
         } else {
             if (!same_layout_dims(h->dims, *dims))
                 return EP_ERR_HANDLE;
+            // The mask shapes the layout; a handle already holds one.
+            if (rank_mask != nullptr)
+                return EP_ERR_INVALID;
             // A handle returned by a dispatch is the cached fast path: the
             // layout is known, so new routing is refused.
             if (h->dispatched.load() && (topk_idx != nullptr || topk_weights != nullptr))
                 return EP_ERR_INVALID;
         }
         if (fresh) {
-            rc = create_handle(*dims, topk_idx, stream, &h);
+            rc = create_handle(*dims, topk_idx, rank_mask, stream, &h);
             if (rc != EP_OK)
                 return rc;
             *handle = h;
@@ -435,8 +439,9 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
 }
 
 int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
-               const float *recv_topk_weights, const void *bias0, const void *bias1, void *out,
-               float *combined_topk_weights, ep_stream_t stream_)
+               const float *recv_topk_weights, const void *bias0, const void *bias1,
+               const int32_t *rank_mask, void *out, float *combined_topk_weights,
+               ep_stream_t stream_)
 {
     try {
         if (h == nullptr)
@@ -446,7 +451,8 @@ int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
         if (hidden % 8 != 0)
             return EP_ERR_ALIGN;
         if (!aligned(y, 16) || !aligned(out, 16) || !aligned(bias0, 16) || !aligned(bias1, 16) ||
-            !aligned(recv_topk_weights, 4) || !aligned(combined_topk_weights, 4))
+            !aligned(recv_topk_weights, 4) || !aligned(combined_topk_weights, 4) ||
+            !aligned(rank_mask, 4))
             return EP_ERR_ALIGN;
         const bool rows = h->dims.num_tokens > 0;
         if (rows && (out == nullptr || y == nullptr))
@@ -460,7 +466,7 @@ int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
         if (rc != EP_OK)
             return rc;
         hipError_t e = launch_combine(h->shape, hidden, y, h->bufs, recv_topk_weights, bias0,
-                                      bias1, out, combined_topk_weights, stream);
+                                      bias1, rank_mask, out, combined_topk_weights, stream);
         if (e != hipSuccess)
             return hip_fail(e);
         h->last_stream = stream;
@@ -743,6 +749,6 @@ const char *ep_status_str(int status)
 
 const char *ep_last_hip_error(void) { return g_last_hip.c_str(); }
 
-int ep_version(void) { return (1 << 16) | 1; }
+int ep_version(void) { return (2 << 16) | 0; }
 
 }  // extern "C"

@@ -52,8 +52,9 @@ LayoutShape layout_shape(const ep_dims &d);
 size_t layout_arena_bytes(const LayoutShape &s, size_t off[kArenaFields]);
 LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields]);
 
-hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const LayoutBufs &b,
-                         hipStream_t stream);
+// rank_mask [R] int32 (nullable): nonzero ranks are masked.
+hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const int32_t *rank_mask,
+                         const LayoutBufs &b, hipStream_t stream);
 
 hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, const LayoutBufs &b,
                            const int64_t *topk_idx, const float *topk_weights, void *recv_x,
@@ -61,7 +62,8 @@ hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, cons
 
 hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const LayoutBufs &b,
                           const float *recv_topk_weights, const void *bias0, const void *bias1,
-                          void *out, float *combined_topk_weights, hipStream_t stream);
+                          const int32_t *rank_mask, void *out, float *combined_topk_weights,
+                          hipStream_t stream);
 
 // packed_q (nullable) selects the FP8 variant: codes [cells][H] bytes and
 // packed_scale [cells][H/128]; packed_x is then unused.

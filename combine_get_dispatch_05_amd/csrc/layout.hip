@@ -27,6 +27,11 @@
 //          last token).
 // Positions come from ballots and scans, never from atomics, so every output
 // is deterministic and segments are in token order.
+//
+// An optional rank mask ("Dynamic Rank Masking" of the same page: nonzero =
+// masked) is folded in where membership is formed: every block ANDs the
+// tokens' rank bitmasks with the live ranks, and the expert histogram skips
+// slots on masked ranks, so a masked rank's slots act as masked slots.
 
 #include "ep_internal.h"
 
@@ -36,6 +41,24 @@ namespace {
 
 constexpr int kCountBlock = 512;  // 8 wavefronts = 512 tokens per count block
 
+// Live ranks as NW 64-bit words in LDS (bit r: rank r exists and is not
+// masked), one ballot per word.  The caller synchronizes before reading.
+template <int NW>
+__device__ __forceinline__ void build_live(const int32_t *__restrict__ rank_mask, int R,
+                                           uint64_t *s_live)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int nwaves = blockDim.x / kWave;
+    for (int w = threadIdx.x / kWave; w < NW; w += nwaves) {
+        const int r = w * kWave + lane;
+        const bool live = r < R && (rank_mask == nullptr || rank_mask[r] == 0);
+        const uint64_t b = wave_ballot(live);
+        if (lane == 0)
+            s_live[w] = b;
+    }
+}
+
+// Rank bitmask of one token's valid slots (before masking ranks).
 template <int NW>
 __device__ __forceinline__ void token_rank_mask(const int64_t *__restrict__ row, int K, int E,
                                                 int epr, uint64_t (&m)[NW])
@@ -53,6 +76,14 @@ __device__ __forceinline__ void token_rank_mask(const int64_t *__restrict__ row,
                     m[w] |= 1ull << (r & 63);
         }
     }
+}
+
+template <int NW>
+__device__ __forceinline__ void keep_live(const uint64_t *s_live, uint64_t (&m)[NW])
+{
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        m[w] &= s_live[w];
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v)
@@ -73,34 +104,42 @@ __device__ __forceinline__ int wave_inclusive_scan(int v)
 // its per-rank totals and its LDS expert histogram.
 template <int NW>
 __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
-    const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int epr, int nW,
-    uint64_t *__restrict__ wave_mask, int32_t *__restrict__ wave_base,
-    int32_t *__restrict__ blk_count, int32_t *__restrict__ blk_ecount)
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
+    int E, int R, int epr, int nW, uint64_t *__restrict__ wave_mask,
+    int32_t *__restrict__ wave_base, int32_t *__restrict__ blk_count,
+    int32_t *__restrict__ blk_ecount)
 {
     constexpr int kWaves = kCountBlock / kWave;
     extern __shared__ int32_t s_ecount[];  // [E]
     __shared__ int32_t s_wcnt[kWaves][kMaxRanks];
+    __shared__ uint64_t s_live[NW];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
     const int wg = blockIdx.x * kWaves + wid;
     const int64_t t = int64_t(blockIdx.x) * kCountBlock + tid;
 
-    for (int i = tid; i < E; i += kCountBlock)
-        s_ecount[i] = 0;
-    __syncthreads();
-
     uint64_t m[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w)
         m[w] = 0;
-    if (t < T) {
-        const int64_t *row = topk_idx + t * K;
+    const int64_t *row = topk_idx + t * K;
+    if (t < T)
         token_rank_mask<NW>(row, K, E, epr, m);
+    for (int i = tid; i < E; i += kCountBlock)
+        s_ecount[i] = 0;
+    build_live<NW>(rank_mask, R, s_live);
+    __syncthreads();
+
+    if (t < T) {
+        keep_live<NW>(s_live, m);
         for (int k = 0; k < K; ++k) {
             const int64_t e = row[k];
-            if (e >= 0 && e < E)
-                atomicAdd(&s_ecount[int(e)], 1);
+            if (e >= 0 && e < E) {
+                const int r = int(e) / epr;
+                if ((s_live[r >> 6] >> (r & 63)) & 1ull)
+                    atomicAdd(&s_ecount[int(e)], 1);
+            }
         }
     }
 
@@ -269,7 +308,8 @@ __global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
 // pack and reduce kernels read.
 template <int NW, bool kSelfScan>
 __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
-    const int64_t *__restrict__ topk_idx, int T, int K, int E, int R, int C, int epr, int kmax,
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
+    int E, int R, int C, int epr, int kmax,
     int nB, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
     const int32_t *__restrict__ blk_count, const int32_t *__restrict__ blk_ecount,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
@@ -284,6 +324,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     __shared__ int32_t s_off[NW * kWave];  // position of this tile's first hit inside segment r
     __shared__ int32_t s_tot[NW * kWave];
     __shared__ int32_t s_wsum[kPosBlock / kWave];
+    __shared__ uint64_t s_live[NW];
     const int tid = threadIdx.x;
     const int wg = blockIdx.x;
     const int blk = wg / (kCountBlock / kWave);
@@ -293,6 +334,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     uint64_t m[NW];
     if (tid < ntok)
         token_rank_mask<NW>(topk_idx + (t0 + tid) * K, K, E, epr, m);
+    build_live<NW>(rank_mask, R, s_live);
     for (int r = tid; r < R; r += kPosBlock) {
         s_mask[r] = wave_mask[size_t(wg) * R + r];
         int before = 0, tot = 0;
@@ -315,6 +357,8 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
         s_off[r] = before + wave_base[size_t(wg) * R + r];
     }
     __syncthreads();
+    if (tid < ntok)
+        keep_live<NW>(s_live, m);
     if (kSelfScan) {
         const int N = rank_exclusive_scan(s_tot, s_seg, R, s_wsum);
         __syncthreads();
@@ -389,12 +433,12 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
 }
 
 template <int NW>
-hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx, const LayoutBufs &b,
-                            hipStream_t stream)
+hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
+                            const int32_t *rank_mask, const LayoutBufs &b, hipStream_t stream)
 {
     if (s.T > 0)
         hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(s.nB), dim3(kCountBlock),
-                           size_t(s.E) * sizeof(int32_t), stream, topk_idx, s.T, s.K, s.E, s.R,
+                           size_t(s.E) * sizeof(int32_t), stream, topk_idx, rank_mask, s.T, s.K, s.E, s.R,
                            s.epr, s.nW, b.wave_mask, b.wave_base, b.blk_count, b.blk_ecount);
     const bool self_scan = s.T > 0 && s.nB <= kSelfScanBlocks;
     if (!self_scan)
@@ -404,7 +448,8 @@ hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx, const
                            b.recv_channel_prefix_matrix, b.num_recv);
     auto pos_kernel = self_scan ? layout_pos_kernel<NW, true> : layout_pos_kernel<NW, false>;
     if (s.T > 0)
-        hipLaunchKernelGGL(pos_kernel, dim3(s.nW), dim3(kPosBlock), 0, stream, topk_idx, s.T, s.K, s.E, s.R,
+        hipLaunchKernelGGL(pos_kernel, dim3(s.nW), dim3(kPosBlock), 0, stream, topk_idx, rank_mask,
+                           s.T, s.K, s.E, s.R,
                            s.C, s.epr, s.kmax, s.nB, b.wave_mask, b.wave_base, b.blk_count,
                            b.blk_ecount, b.is_token_in_rank, b.send_head, b.recv_src_idx,
                            b.dst_row, b.dst_rank, b.num_tokens_per_rank, b.num_tokens_per_expert,
@@ -468,18 +513,18 @@ LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields])
     return b;
 }
 
-hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const LayoutBufs &b,
-                         hipStream_t stream)
+hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const int32_t *rank_mask,
+                         const LayoutBufs &b, hipStream_t stream)
 {
     switch ((s.R + kWave - 1) / kWave) {
-    case 1: return launch_layout_nw<1>(s, topk_idx, b, stream);
-    case 2: return launch_layout_nw<2>(s, topk_idx, b, stream);
-    case 3: return launch_layout_nw<3>(s, topk_idx, b, stream);
-    case 4: return launch_layout_nw<4>(s, topk_idx, b, stream);
+    case 1: return launch_layout_nw<1>(s, topk_idx, rank_mask, b, stream);
+    case 2: return launch_layout_nw<2>(s, topk_idx, rank_mask, b, stream);
+    case 3: return launch_layout_nw<3>(s, topk_idx, rank_mask, b, stream);
+    case 4: return launch_layout_nw<4>(s, topk_idx, rank_mask, b, stream);
     case 5:
-    case 6: return launch_layout_nw<6>(s, topk_idx, b, stream);
+    case 6: return launch_layout_nw<6>(s, topk_idx, rank_mask, b, stream);
     case 7:
-    case 8: return launch_layout_nw<8>(s, topk_idx, b, stream);
+    case 8: return launch_layout_nw<8>(s, topk_idx, rank_mask, b, stream);
     default: return hipErrorInvalidValue;
     }
 }

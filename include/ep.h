@@ -127,10 +127,14 @@ int64_t ep_max_recv_rows(const ep_dims *dims);
  * handle_out (nullable): receives a new handle holding the layout.  Such a
  *   handle may be given to one ep_dispatch together with the same topk_idx
  *   (the "pre-computed layout" of [P1] "Dispatch Operation").
+ * rank_mask [R] int32 (nullable; [P1] "Dynamic Rank Masking", nonzero =
+ *   masked): every slot whose expert lives on a masked rank is treated as a
+ *   masked slot, so a masked rank gets no tokens and its experts count 0.
+ *   The mask is read on the device when the layout kernels run.
  * No host synchronization unless noted above.
  */
-int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, ep_layout_out *out,
-                           ep_handle **handle_out, ep_stream_t stream);
+int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, const int32_t *rank_mask,
+                           ep_layout_out *out, ep_handle **handle_out, ep_stream_t stream);
 
 /*
  * [P1] "Dispatch Operation" and [P4] "Fast Path Dispatch with Handle Reuse":
@@ -159,12 +163,16 @@ int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, ep_layo
  *   is needed to check it.
  * num_recv (HOST pointer, nullable): receives N; asking for it synchronizes
  *   the stream once per handle (later calls use the cached value).
+ * rank_mask [R] int32 (nullable): as for ep_get_dispatch_layout; used only
+ *   by a fresh dispatch (the layout it computes).  A handle already holds
+ *   its layout, so a non-NULL rank_mask with *handle != NULL returns
+ *   EP_ERR_INVALID.
  * dims must equal the handle's dims except hidden, which may differ.
  */
 int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
-                const float *topk_weights, ep_handle **handle, void *recv_x,
-                int64_t *recv_topk_idx, float *recv_topk_weights, int64_t recv_cap,
-                int64_t *num_recv, ep_stream_t stream);
+                const float *topk_weights, const int32_t *rank_mask, ep_handle **handle,
+                void *recv_x, int64_t *recv_topk_idx, float *recv_topk_weights,
+                int64_t recv_cap, int64_t *num_recv, ep_stream_t stream);
 
 /*
  * [P1] "Combine Operation": addition-based reduction of the packed rows
@@ -180,12 +188,16 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
  * recv_topk_weights [y_rows][K] fp32 (nullable) and combined_topk_weights
  * [T][K] fp32 (nullable, needs the former): the same ascending-rank fp32 sum
  * of the per-row weights (the reduced weights combine returns).
+ * rank_mask [R] int32 (nullable; [P1] "Dynamic Rank Masking"): ranks masked
+ *   now (nonzero) are left out of both sums, as if t had not gone there;
+ *   the order of the remaining terms is unchanged.
  * y_rows below N returns EP_ERR_CAPACITY (checked without synchronizing
  * when y_rows >= ep_max_recv_rows(), else N is read once per handle).
  */
 int ep_combine(ep_handle *handle, int32_t hidden, const void *y, int64_t y_rows,
-               const float *recv_topk_weights, const void *bias0, const void *bias1, void *out,
-               float *combined_topk_weights, ep_stream_t stream);
+               const float *recv_topk_weights, const void *bias0, const void *bias1,
+               const int32_t *rank_mask, void *out, float *combined_topk_weights,
+               ep_stream_t stream);
 
 /*
  * [P1] "IB-GDA Kernels", low_latency_dispatch: stream every valid (token,
@@ -319,7 +331,8 @@ const char *ep_status_str(int status);
 /* Text of the last HIP error seen by this thread (empty if none). */
 const char *ep_last_hip_error(void);
 
-/* ABI version: (major << 16) | minor. */
+/* ABI version: (major << 16) | minor.  2.0: rank_mask arguments of
+ * ep_get_dispatch_layout, ep_dispatch and ep_combine. */
 int ep_version(void);
 
 #ifdef __cplusplus

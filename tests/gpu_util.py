@@ -41,3 +41,20 @@ def assert_bf16_close(got_bits: np.ndarray, exp_bits: np.ndarray, max_ulp: int =
     assert worst <= max_ulp, f"{what}: max {worst} ulp apart ({n_off} elements differ)"
     if exact:
         assert n_off == 0, f"{what}: {n_off} elements differ by <= {max_ulp} ulp"
+
+
+LAYOUT_FIELDS = ["num_tokens_per_rank", "num_tokens_per_expert", "rank_prefix_matrix",
+                 "channel_prefix_matrix", "recv_channel_prefix_matrix", "send_head",
+                 "recv_src_idx"]
+
+
+def compare_layout(lay, ora) -> None:
+    """Every layout output of a handle against the oracle's, bit-exact."""
+    for name in LAYOUT_FIELDS:
+        np.testing.assert_array_equal(host(getattr(lay, name)), getattr(ora, name), err_msg=name)
+    np.testing.assert_array_equal(host(lay.is_token_in_rank).astype(np.uint8),
+                                  ora.is_token_in_rank, err_msg="is_token_in_rank")
+
+
+def f32_bits(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)

@@ -60,7 +60,7 @@ def test_product_package_never_touches_the_oracle():
 
 
 def test_version_and_status_text():
-    assert abi.version() == (1, 1)
+    assert abi.version() == (2, 0)
     for code in range(7):
         assert L.ep_status_str(code)
     assert L.ep_status_str(99) == b"unknown status"
@@ -86,49 +86,52 @@ def test_max_recv_rows():
 def test_dims_rejected(dims, code):
     d = abi.dims(*dims)
     h = ctypes.c_void_p()
-    rc = L.ep_dispatch(ctypes.byref(d), None, None, None, ctypes.byref(h), None, None, None, 0,
-                       None, S)
+    rc = L.ep_dispatch(ctypes.byref(d), None, None, None, None, ctypes.byref(h), None, None, None,
+                       0, None, S)
     assert rc == code
     assert h.value is None
-    rc = L.ep_get_dispatch_layout(ctypes.byref(d), None, None, ctypes.byref(h), S)
+    rc = L.ep_get_dispatch_layout(ctypes.byref(d), None, None, None, ctypes.byref(h), S)
     assert rc == code
 
 
 def test_argument_rules_rejected_before_device_work():
     d = abi.dims(16, 64, 2, 8, 4, 1)
     h = ctypes.c_void_p()
+    hp = ctypes.byref(h)
     fake = ctypes.c_void_p(0x10000)
     mis = ctypes.c_void_p(0x10008)  # 8-byte aligned, not 16
-    # no handle slot
-    assert L.ep_dispatch(ctypes.byref(d), fake, fake, None, None, fake, None, None, 64, None,
-                         S) == abi.EP_ERR_INVALID
-    # misaligned x / recv_x
-    assert L.ep_dispatch(ctypes.byref(d), mis, fake, None, ctypes.byref(h), fake, None, None, 64,
-                         None, S) == abi.EP_ERR_ALIGN
-    assert L.ep_dispatch(ctypes.byref(d), fake, fake, None, ctypes.byref(h), mis, None, None, 64,
-                         None, S) == abi.EP_ERR_ALIGN
-    # misaligned topk_idx
-    assert L.ep_dispatch(ctypes.byref(d), fake, ctypes.c_void_p(0x10004), None, ctypes.byref(h),
-                         fake, None, None, 64, None, S) == abi.EP_ERR_ALIGN
-    # recv_x without x
-    assert L.ep_dispatch(ctypes.byref(d), None, fake, None, ctypes.byref(h), fake, None, None, 64,
-                         None, S) == abi.EP_ERR_INVALID
-    # recv weights without topk weights
-    assert L.ep_dispatch(ctypes.byref(d), fake, fake, None, ctypes.byref(h), fake, None, fake, 64,
-                         None, S) == abi.EP_ERR_INVALID
-    # fresh dispatch without routing
-    assert L.ep_dispatch(ctypes.byref(d), fake, None, None, ctypes.byref(h), fake, None, None, 64,
-                         None, S) == abi.EP_ERR_INVALID
-    # negative capacity
-    assert L.ep_dispatch(ctypes.byref(d), fake, fake, None, ctypes.byref(h), fake, None, None, -1,
-                         None, S) == abi.EP_ERR_INVALID
+
+    def disp(x, topk, w, mask, handle, recv_x, rw, cap):
+        # (dims, x, topk_idx, topk_weights, rank_mask, handle, recv_x,
+        #  recv_topk_idx, recv_topk_weights, recv_cap, num_recv, stream)
+        return L.ep_dispatch(ctypes.byref(d), x, topk, w, mask, handle, recv_x, None, rw, cap,
+                             None, S)
+
+    assert disp(fake, fake, None, None, None, fake, None, 64) == abi.EP_ERR_INVALID  # no handle slot
+    assert disp(mis, fake, None, None, hp, fake, None, 64) == abi.EP_ERR_ALIGN  # misaligned x
+    assert disp(fake, fake, None, None, hp, mis, None, 64) == abi.EP_ERR_ALIGN  # misaligned recv_x
+    assert disp(fake, ctypes.c_void_p(0x10004), None, None, hp, fake, None,
+                64) == abi.EP_ERR_ALIGN  # misaligned topk_idx
+    assert disp(fake, fake, None, ctypes.c_void_p(0x10002), hp, fake, None,
+                64) == abi.EP_ERR_ALIGN  # misaligned rank mask
+    assert disp(None, fake, None, None, hp, fake, None, 64) == abi.EP_ERR_INVALID  # recv_x, no x
+    assert disp(fake, fake, None, None, hp, fake, fake,
+                64) == abi.EP_ERR_INVALID  # recv weights without topk weights
+    assert disp(fake, None, None, None, hp, fake, None, 64) == abi.EP_ERR_INVALID  # no routing
+    assert disp(fake, fake, None, None, hp, fake, None, -1) == abi.EP_ERR_INVALID  # capacity < 0
     assert h.value is None
-    # layout with nothing to produce
-    assert L.ep_get_dispatch_layout(ctypes.byref(d), fake, None, None, S) == abi.EP_ERR_INVALID
+    # layout with nothing to produce; misaligned rank mask
+    assert L.ep_get_dispatch_layout(ctypes.byref(d), fake, None, None, None, S) == abi.EP_ERR_INVALID
+    assert L.ep_get_dispatch_layout(ctypes.byref(d), fake, ctypes.c_void_p(0x10002), None, hp,
+                                    S) == abi.EP_ERR_ALIGN
+    # combine: misaligned rank mask is refused before the handle is used
+    assert L.ep_combine(ctypes.c_void_p(0x10000), 64, fake, 0, None, None, None,
+                        ctypes.c_void_p(0x10002), fake, None, S) == abi.EP_ERR_ALIGN
 
 
 def test_combine_and_handle_calls_without_handle():
-    assert L.ep_combine(None, 64, None, 0, None, None, None, None, None, S) == abi.EP_ERR_HANDLE
+    assert L.ep_combine(None, 64, None, 0, None, None, None, None, None, None,
+                        S) == abi.EP_ERR_HANDLE
     n = ctypes.c_int64()
     assert L.ep_handle_num_recv(None, ctypes.byref(n)) == abi.EP_ERR_HANDLE
     assert L.ep_handle_copy_layout(None, None, S) == abi.EP_ERR_HANDLE

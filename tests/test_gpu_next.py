@@ -5,6 +5,7 @@ reductions within 1 ulp (and equal, as both sides round the same sums)."""
 
 from __future__ import annotations
 
+import ctypes
 import sys
 
 import numpy as np
@@ -14,11 +15,12 @@ import torch
 import oracle
 import pinlib
 from gen import config_inputs, random_case, random_rows
-from gpu_util import assert_bf16_close, dev, dev_bf16, host, host_bits
+from gpu_util import assert_bf16_close, compare_layout, dev, dev_bf16, f32_bits, host, host_bits
 
 pytestmark = pytest.mark.gpu
 
 import combine_get_dispatch_05_amd as epm  # noqa: E402
+from combine_get_dispatch_05_amd import abi  # noqa: E402
 
 
 @pytest.fixture(autouse=True)
@@ -27,10 +29,6 @@ def _announce(request):
     sys.__stderr__.flush()
     yield
     torch.cuda.synchronize()
-
-
-def f32_bits(a):
-    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
 
 
 # ------------------------------------------------------------ rank masking
@@ -84,6 +82,76 @@ def test_ll_rank_mask(case):
     assert_bf16_close(host_bits(out), oracle.ll_combine(y, inp.topk_idx, inp.topk_weights, E, R,
                                                         combine_mask=cm),
                       what="combine-time mask")
+
+
+# --------------------------------------------- rank masking, normal path
+
+
+def _normal_mask_case(case):
+    if case == "tiny":
+        return config_inputs(0), [1]
+    if case == "skewed":
+        return config_inputs(2), [0, 7, 31]
+    if case == "large":
+        return config_inputs(4), [3, 64, 130, 143]   # ranks in all three 64-rank words
+    return random_case(31, 257, 136, 512, 8, 512, 7, mask=0.05, dup=0.1), [0, 63, 64, 300, 511]
+
+
+@pytest.mark.parametrize("case", ["tiny", "skewed", "large", "R512"])
+def test_normal_path_rank_mask(case):
+    """Ranks masked before the layout receive nothing (layout, dispatch and
+    handle bit-exact with the oracle's masked layout); a rank masked later,
+    before the combine, drops out of both combine sums."""
+    inp, masked = _normal_mask_case(case)
+    E, R, C, H = inp.E, inp.R, inp.C, inp.H
+    m = np.zeros(R, np.int32)
+    m[masked] = 1
+    ora = oracle.layout(inp.topk_idx, E, R, C, rank_mask=m)
+    buf = epm.Buffer(R, E, C)
+    for r in masked:
+        buf.low_latency_update_mask_buffer(r, mask=True)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+
+    ntpr, ntpe, itr, _ = buf.get_dispatch_layout(topk)
+    np.testing.assert_array_equal(host(ntpr), ora.num_tokens_per_rank)
+    np.testing.assert_array_equal(host(ntpe), ora.num_tokens_per_expert)
+    np.testing.assert_array_equal(host(itr).astype(np.uint8), ora.is_token_in_rank)
+
+    rx, rti, rtw, counts, h, _ = buf.dispatch(x, topk, w)
+    assert h.num_recv == ora.num_recv
+    compare_layout(h.layout(), ora)
+    o_rx, o_rti, o_rtw = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, E, R, ora)
+    np.testing.assert_array_equal(host_bits(rx), o_rx)
+    np.testing.assert_array_equal(host(rti), o_rti)
+    np.testing.assert_array_equal(f32_bits(host(rtw)), f32_bits(o_rtw))
+
+    y = random_rows(ora.num_recv, H, 5, tag=12)
+    out, cw, _ = buf.combine(dev_bf16(y), h, rtw)
+    o_out, o_cw = oracle.combine(y, ora, o_rtw, rank_mask=m)
+    assert_bf16_close(host_bits(out), o_out, what="combine, mask set at dispatch")
+    np.testing.assert_array_equal(f32_bits(host(cw)), f32_bits(o_cw))
+
+    # one more rank fails after the dispatch
+    live = [r for r in range(R) if m[r] == 0 and ora.num_tokens_per_rank[r] > 0]
+    extra = live[len(live) // 2]
+    buf.low_latency_update_mask_buffer(extra, mask=True)
+    m2 = m.copy()
+    m2[extra] = 1
+    out2, cw2, _ = buf.combine(dev_bf16(y), h, rtw)
+    o_out2, o_cw2 = oracle.combine(y, ora, o_rtw, rank_mask=m2)
+    assert_bf16_close(host_bits(out2), o_out2, what="combine, rank masked at combine time")
+    np.testing.assert_array_equal(f32_bits(host(cw2)), f32_bits(o_cw2))
+    assert not np.array_equal(o_out2, o_out)
+
+    if case == "tiny":
+        # a mask cannot be applied to a handle's existing layout
+        d = abi.dims(inp.T, H, inp.K, E, R, C)
+        raw = ctypes.c_void_p(h.raw.value)
+        rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, abi.ptr(buf._mask),
+                                   ctypes.byref(raw), abi.ptr(rx), None, None, rx.shape[0], None,
+                                   abi.current_stream())
+        assert rc == abi.EP_ERR_INVALID
+    h.free()
 
 
 # -------------------------------------------------------------- combine bias

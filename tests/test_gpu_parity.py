@@ -20,7 +20,7 @@ import torch
 
 import oracle
 from gen import config_inputs, random_case, random_rows
-from gpu_util import assert_bf16_close, dev, dev_bf16, host, host_bits
+from gpu_util import assert_bf16_close, compare_layout, dev, dev_bf16, f32_bits, host, host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -34,22 +34,6 @@ def _announce(request):
     sys.__stderr__.flush()
     yield
     torch.cuda.synchronize()
-
-
-LAYOUT_FIELDS = ["num_tokens_per_rank", "num_tokens_per_expert", "rank_prefix_matrix",
-                 "channel_prefix_matrix", "recv_channel_prefix_matrix", "send_head",
-                 "recv_src_idx"]
-
-
-def compare_layout(lay, ora):
-    for name in LAYOUT_FIELDS:
-        np.testing.assert_array_equal(host(getattr(lay, name)), getattr(ora, name), err_msg=name)
-    np.testing.assert_array_equal(host(lay.is_token_in_rank).astype(np.uint8),
-                                  ora.is_token_in_rank, err_msg="is_token_in_rank")
-
-
-def f32_bits(a):
-    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
 
 
 def run_normal_path(inp, seed=0):
@@ -200,26 +184,26 @@ def test_errors_and_reuse_contract():
     d = abi.dims(inp.T, inp.H, inp.K, inp.E, inp.R, inp.C + 1)
     raw = ctypes.c_void_p(h.raw.value)
     rx = torch.empty((4096, inp.H), dtype=torch.bfloat16, device="cuda")
-    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, ctypes.byref(raw),
+    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, None, ctypes.byref(raw),
                                abi.ptr(rx), None, None, 4096, None, abi.current_stream())
     assert rc == abi.EP_ERR_HANDLE
     # too few rows: refused, nothing written
     n = h.num_recv
     small = torch.full((n - 1, inp.H), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
     d = abi.dims(inp.T, inp.H, inp.K, inp.E, inp.R, inp.C)
-    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, ctypes.byref(raw),
+    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, None, ctypes.byref(raw),
                                abi.ptr(small), None, None, n - 1, None, abi.current_stream())
     assert rc == abi.EP_ERR_CAPACITY
     assert bool((small.view(torch.int16) == 7).all())
     out = torch.empty((inp.T, inp.H), dtype=torch.bfloat16, device="cuda")
-    rc = abi.lib().ep_combine(h.raw, inp.H, abi.ptr(small), n - 1, None, None, None,
+    rc = abi.lib().ep_combine(h.raw, inp.H, abi.ptr(small), n - 1, None, None, None, None,
                               abi.ptr(out), None, abi.current_stream())
     assert rc == abi.EP_ERR_CAPACITY
     # misaligned row pointer
     off = torch.empty((n + 1, inp.H), dtype=torch.bfloat16, device="cuda")
     bad = ctypes.c_void_p(off.data_ptr() + 2)
-    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, ctypes.byref(raw), bad,
-                               None, None, n, None, abi.current_stream())
+    rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), None, None, None, ctypes.byref(raw),
+                               bad, None, None, n, None, abi.current_stream())
     assert rc == abi.EP_ERR_ALIGN
     h.free()
 
@@ -246,14 +230,14 @@ def test_layout_capacity_out():
     n = ora.num_recv
     src = torch.full((n - 1,), -5, dtype=torch.int32, device="cuda")
     o = abi.LayoutOut(None, None, None, None, None, None, None, src.data_ptr(), n - 1)
-    rc = abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk), ctypes.byref(o), None,
-                                          abi.current_stream())
+    rc = abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk), None, ctypes.byref(o),
+                                          None, abi.current_stream())
     assert rc == abi.EP_ERR_CAPACITY
     assert bool((src == -5).all())
     src = torch.full((n,), -5, dtype=torch.int32, device="cuda")
     o = abi.LayoutOut(None, None, None, None, None, None, None, src.data_ptr(), n)
-    rc = abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk), ctypes.byref(o), None,
-                                          abi.current_stream())
+    rc = abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk), None, ctypes.byref(o),
+                                          None, abi.current_stream())
     assert rc == abi.EP_OK
     np.testing.assert_array_equal(host(src), ora.recv_src_idx)
 
@@ -274,7 +258,7 @@ def test_guard_bands_and_determinism():
         recv = big[G:G + cap].view(torch.bfloat16)
         raw = ctypes.c_void_p()
         n = ctypes.c_int64()
-        rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), abi.ptr(topk), abi.ptr(w),
+        rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), abi.ptr(topk), abi.ptr(w), None,
                                    ctypes.byref(raw), abi.ptr(recv), None, None, cap,
                                    ctypes.byref(n), abi.current_stream())
         assert rc == abi.EP_OK
@@ -283,8 +267,8 @@ def test_guard_bands_and_determinism():
         assert np.all(b[:G] == 0x7FC1) and np.all(b[G + N:] == 0x7FC1)
         obig = torch.full((inp.T + 2 * G, H), 0x7FC1, dtype=torch.int16, device="cuda")
         out = obig[G:G + inp.T].view(torch.bfloat16)
-        rc = abi.lib().ep_combine(raw, H, abi.ptr(recv), cap, None, None, None, abi.ptr(out),
-                                  None, abi.current_stream())
+        rc = abi.lib().ep_combine(raw, H, abi.ptr(recv), cap, None, None, None, None,
+                                  abi.ptr(out), None, abi.current_stream())
         assert rc == abi.EP_OK
         ob = host(obig)
         assert np.all(ob[:G] == 0x7FC1) and np.all(ob[G + inp.T:] == 0x7FC1)
