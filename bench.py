@@ -425,6 +425,24 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     rep["lb_reduce_grads"] = {"avg_us": round(us, 2), "bytes": byt,
                               "gbs": round(byt / (us * 1e-6) / 1e9, 1)}
     del ew, rw
+
+    # the decode step (LL dispatch + LL combine) replayed from a HIP graph,
+    # against the same two calls launched one by one
+    def ll_step():
+        st = abi.current_stream()
+        abi.check(L.ep_ll_dispatch(ctypes.byref(dd), S, P(lx), P(ltopk), None, P(packed),
+                                   P(lcount), P(lsrc), P(lslot), st), "ll")
+        abi.check(L.ep_ll_combine(ctypes.byref(dd), S, P(packed), P(ltopk), P(lw), P(lslot), None,
+                                  P(lout), st), "ll")
+    eager = timed(ll_step, args.steps)
+    ll_step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ll_step()
+    torch.cuda.synchronize()
+    graph = timed(g.replay, args.steps)
+    rep["ll_step_graph"] = {"eager_us": round(eager, 2), "graph_replay_us": round(graph, 2)}
     return rep
 
 

@@ -58,24 +58,76 @@ __device__ __forceinline__ void build_live(const int32_t *__restrict__ rank_mask
     }
 }
 
-// Rank bitmask of one token's valid slots (before masking ranks).
-template <int NW>
-__device__ __forceinline__ void token_rank_mask(const int64_t *__restrict__ row, int K, int E,
-                                                int epr, uint64_t (&m)[NW])
+// Rank of expert e: a shift when E/R is a power of two (epr_shift >= 0),
+// else a division.
+__device__ __forceinline__ int rank_of(int e, int epr, int epr_shift)
+{
+    return epr_shift >= 0 ? e >> epr_shift : e / epr;
+}
+
+constexpr int kIdChunk = 8;  // top-k ids loaded per batch (all loads in flight at once)
+
+// Slots k0 .. k0+kIdChunk-1 of a token's row (-1 past K).
+__device__ __forceinline__ void load_ids(const int64_t *__restrict__ row, int k0, int K,
+                                         int64_t (&ids)[kIdChunk])
 {
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
-        m[w] = 0;
-    for (int k = 0; k < K; ++k) {
-        const int64_t e = row[k];
+    for (int q = 0; q < kIdChunk; ++q)
+        ids[q] = k0 + q < K ? row[k0 + q] : -1;
+}
+
+template <int NW>
+__device__ __forceinline__ void add_ranks(const int64_t (&ids)[kIdChunk], int E, int epr,
+                                          int epr_shift, uint64_t (&m)[NW])
+{
+#pragma unroll
+    for (int q = 0; q < kIdChunk; ++q) {
+        const int64_t e = ids[q];
         if (e >= 0 && e < E) {
-            const int r = int(e) / epr;
+            const int r = rank_of(int(e), epr, epr_shift);
 #pragma unroll
             for (int w = 0; w < NW; ++w)
                 if ((r >> 6) == w)
                     m[w] |= 1ull << (r & 63);
         }
     }
+}
+
+// Rank bitmask of one token's valid slots (before masking ranks).  The first
+// kIdChunk ids are returned in ids0 for later use.
+template <int NW>
+__device__ __forceinline__ void token_rank_mask(const int64_t *__restrict__ row, int K, int E,
+                                                int epr, int epr_shift, uint64_t (&m)[NW],
+                                                int64_t (&ids0)[kIdChunk])
+{
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+        m[w] = 0;
+    load_ids(row, 0, K, ids0);
+    add_ranks<NW>(ids0, E, epr, epr_shift, m);
+    for (int k0 = kIdChunk; k0 < K; k0 += kIdChunk) {
+        int64_t ids[kIdChunk];
+        load_ids(row, k0, K, ids);
+        add_ranks<NW>(ids, E, epr, epr_shift, m);
+    }
+}
+
+// Transpose of a 64 x 64 bit matrix held one row per lane (bit j of lane i
+// = entry (i, j)): afterwards lane j holds column j.  Six butterfly stages,
+// each exchanging the off-diagonal halves of 2s x 2s blocks with lane ^ s.
+__device__ __forceinline__ uint64_t wave_transpose64(uint64_t x)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t keep[6] = {0x00000000FFFFFFFFull, 0x0000FFFF0000FFFFull, 0x00FF00FF00FF00FFull,
+                              0x0F0F0F0F0F0F0F0Full, 0x3333333333333333ull, 0x5555555555555555ull};
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+        const int sft = 32 >> i;
+        const uint64_t lo = keep[i];  // columns c with (c & sft) == 0
+        const uint64_t y = __shfl_xor((unsigned long long)x, sft, kWave);
+        x = (lane & sft) ? ((x & ~lo) | ((y & ~lo) >> sft)) : ((x & lo) | ((y & lo) << sft));
+    }
+    return x;
 }
 
 template <int NW>
@@ -105,7 +157,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int v)
 template <int NW>
 __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
-    int E, int R, int epr, int nW, uint64_t *__restrict__ wave_mask,
+    int E, int R, int epr, int epr_shift, int nW, uint64_t *__restrict__ wave_mask,
     int32_t *__restrict__ wave_base, int32_t *__restrict__ blk_count,
     int32_t *__restrict__ blk_ecount)
 {
@@ -120,12 +172,16 @@ __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
     const int64_t t = int64_t(blockIdx.x) * kCountBlock + tid;
 
     uint64_t m[NW];
+    int64_t ids0[kIdChunk];
 #pragma unroll
     for (int w = 0; w < NW; ++w)
         m[w] = 0;
+#pragma unroll
+    for (int q = 0; q < kIdChunk; ++q)
+        ids0[q] = -1;
     const int64_t *row = topk_idx + t * K;
     if (t < T)
-        token_rank_mask<NW>(row, K, E, epr, m);
+        token_rank_mask<NW>(row, K, E, epr, epr_shift, m, ids0);
     for (int i = tid; i < E; i += kCountBlock)
         s_ecount[i] = 0;
     build_live<NW>(rank_mask, R, s_live);
@@ -133,27 +189,43 @@ __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
 
     if (t < T) {
         keep_live<NW>(s_live, m);
-        for (int k = 0; k < K; ++k) {
-            const int64_t e = row[k];
-            if (e >= 0 && e < E) {
-                const int r = int(e) / epr;
-                if ((s_live[r >> 6] >> (r & 63)) & 1ull)
-                    atomicAdd(&s_ecount[int(e)], 1);
+        const bool masking = rank_mask != nullptr;
+        for (int k0 = 0; k0 < K; k0 += kIdChunk) {
+            int64_t ids[kIdChunk];
+            if (k0 == 0) {
+#pragma unroll
+                for (int q = 0; q < kIdChunk; ++q)
+                    ids[q] = ids0[q];
+            } else {
+                load_ids(row, k0, K, ids);
+            }
+#pragma unroll
+            for (int q = 0; q < kIdChunk; ++q) {
+                const int64_t e = ids[q];
+                if (e >= 0 && e < E) {
+                    // The token hits rank(e), so its bit in m says whether
+                    // that rank is live.
+                    bool live = true;
+                    if (masking) {
+                        const int r = rank_of(int(e), epr, epr_shift);
+                        uint64_t word = 0;
+#pragma unroll
+                        for (int w = 0; w < NW; ++w)
+                            word = (r >> 6) == w ? m[w] : word;
+                        live = (word >> (r & 63)) & 1ull;
+                    }
+                    if (live)
+                        atomicAdd(&s_ecount[int(e)], 1);
+                }
             }
         }
     }
 
+    // Lane b of the wave gets the wave's membership mask of rank 64w + b:
+    // the transpose of the tokens' rank bitmasks.
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        uint64_t mine = 0;
-        for (int b = 0; b < kWave; ++b) {
-            const int r = w * kWave + b;
-            if (r >= R)
-                break;
-            const uint64_t bal = wave_ballot((m[w] >> b) & 1ull);
-            if (lane == b)
-                mine = bal;
-        }
+        const uint64_t mine = wave_transpose64(m[w]);
         const int r = w * kWave + lane;
         if (r < R) {
             if (wg < nW)
@@ -309,7 +381,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
 template <int NW, bool kSelfScan>
 __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
-    int E, int R, int C, int epr, int kmax,
+    int E, int R, int C, int epr, int epr_shift, int kmax,
     int nB, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
     const int32_t *__restrict__ blk_count, const int32_t *__restrict__ blk_ecount,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
@@ -325,6 +397,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     __shared__ int32_t s_tot[NW * kWave];
     __shared__ int32_t s_wsum[kPosBlock / kWave];
     __shared__ uint64_t s_live[NW];
+    __shared__ uint64_t s_tokm[NW][kWave];  // live-rank bitmask of each token of the tile
     const int tid = threadIdx.x;
     const int wg = blockIdx.x;
     const int blk = wg / (kCountBlock / kWave);
@@ -332,8 +405,10 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     const int ntok = int(T - t0 < kWave ? T - t0 : kWave);
 
     uint64_t m[NW];
-    if (tid < ntok)
-        token_rank_mask<NW>(topk_idx + (t0 + tid) * K, K, E, epr, m);
+    if (tid < ntok) {
+        int64_t ids0[kIdChunk];
+        token_rank_mask<NW>(topk_idx + (t0 + tid) * K, K, E, epr, epr_shift, m, ids0);
+    }
     build_live<NW>(rank_mask, R, s_live);
     for (int r = tid; r < R; r += kPosBlock) {
         s_mask[r] = wave_mask[size_t(wg) * R + r];
@@ -357,8 +432,13 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
         s_off[r] = before + wave_base[size_t(wg) * R + r];
     }
     __syncthreads();
-    if (tid < ntok)
-        keep_live<NW>(s_live, m);
+    if (tid < kWave) {
+        if (tid < ntok)
+            keep_live<NW>(s_live, m);
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+            s_tokm[w][tid] = tid < ntok ? m[w] : 0;
+    }
     if (kSelfScan) {
         const int N = rank_exclusive_scan(s_tot, s_seg, R, s_wsum);
         __syncthreads();
@@ -372,24 +452,55 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
         __syncthreads();
     }
 
-    // Flat walk over the tile's cells, (token, rank) row-major.
-    const int cells = ntok * R;
-    const int dt = kPosBlock / R, dr = kPosBlock % R;
-    int tl = tid / R, r = tid % R;
-    for (int i = tid; i < cells; i += kPosBlock) {
-        const uint64_t b = s_mask[r];
-        const bool hit = (b >> tl) & 1ull;
-        const int pos = s_off[r] + __popcll(b & ((1ull << tl) - 1ull));
-        const int64_t t = t0 + tl;
-        send_head[size_t(t) * R + r] = hit ? pos : -1;
-        is_token_in_rank[size_t(t) * R + r] = hit ? 1 : 0;
-        if (hit)
-            recv_src_idx[s_seg[r] + pos] = int32_t(t);
-        tl += dt;
-        r += dr;
-        if (r >= R) {
-            r -= R;
-            ++tl;
+    // Flat walk over the tile's cells, (token, rank) row-major, so that
+    // consecutive lanes write consecutive entries of the [T][R] rows.  With R
+    // a multiple of 4 a lane takes 4 ranks: one 16-byte send_head store and
+    // one 4-byte is_token_in_rank store.
+    if ((R & 3) == 0) {
+        const int G = R >> 2;
+        const int items = ntok * G;
+        const int dt = kPosBlock / G, dg = kPosBlock % G;
+        int tl = tid / G, g = tid % G;
+        for (int i = tid; i < items; i += kPosBlock) {
+            const int64_t t = t0 + tl;
+            const uint64_t below = (1ull << tl) - 1ull;
+            int4 sh;
+            uint32_t in4 = 0;
+            int *shp = reinterpret_cast<int *>(&sh);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 4 * g + q;
+                const uint64_t b = s_mask[r];
+                const bool hit = (b >> tl) & 1ull;
+                shp[q] = hit ? s_off[r] + __popcll(b & below) : -1;
+                in4 |= (hit ? 1u : 0u) << (8 * q);
+            }
+            *reinterpret_cast<int4 *>(send_head + size_t(t) * R + 4 * g) = sh;
+            *reinterpret_cast<uint32_t *>(is_token_in_rank + size_t(t) * R + 4 * g) = in4;
+            tl += dt;
+            g += dg;
+            if (g >= G) {
+                g -= G;
+                ++tl;
+            }
+        }
+    } else {
+        const int cells = ntok * R;
+        const int dt = kPosBlock / R, dr = kPosBlock % R;
+        int tl = tid / R, r = tid % R;
+        for (int i = tid; i < cells; i += kPosBlock) {
+            const uint64_t b = s_mask[r];
+            const bool hit = (b >> tl) & 1ull;
+            const int pos = s_off[r] + __popcll(b & ((1ull << tl) - 1ull));
+            const int64_t t = t0 + tl;
+            send_head[size_t(t) * R + r] = hit ? pos : -1;
+            is_token_in_rank[size_t(t) * R + r] = hit ? 1 : 0;
+            tl += dt;
+            r += dr;
+            if (r >= R) {
+                r -= R;
+                ++tl;
+            }
         }
     }
 
@@ -408,26 +519,38 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
         }
     }
 
-    // Lanes = tokens: each token's destination rows, ascending rank.
-    if (tid < ntok) {
-        const int64_t t = t0 + tid;
-        const uint64_t below = lanemask_lt();
-        int j = 0;
+    // Each token's destination rows in ascending rank order (and the inverse
+    // map recv_src_idx): lane = token, and wave p of the block writes the
+    // entries j with j % 4 == p.
+    {
+        const int tl = tid & (kWave - 1);
+        const int part = tid >> 6;
+        if (tl < ntok) {
+            const int64_t t = t0 + tl;
+            const uint64_t below = (1ull << tl) - 1ull;
+            int j = 0;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            uint64_t mm = m[w];
-            while (mm) {
-                const int bit = __ffsll((unsigned long long)mm) - 1;
-                mm &= mm - 1;
-                const int rr = w * kWave + bit;
-                dst_row[size_t(t) * kmax + j] = s_seg[rr] + s_off[rr] + __popcll(s_mask[rr] & below);
-                dst_rank[size_t(t) * kmax + j] = rr;
-                ++j;
+            for (int w = 0; w < NW; ++w) {
+                uint64_t mm = s_tokm[w][tl];
+                while (mm) {
+                    const int bit = __ffsll((unsigned long long)mm) - 1;
+                    mm &= mm - 1;
+                    if ((j & 3) == part) {
+                        const int rr = w * kWave + bit;
+                        const int row = s_seg[rr] + s_off[rr] + __popcll(s_mask[rr] & below);
+                        dst_row[size_t(t) * kmax + j] = row;
+                        dst_rank[size_t(t) * kmax + j] = rr;
+                        recv_src_idx[row] = int32_t(t);
+                    }
+                    ++j;
+                }
             }
-        }
-        for (; j < kmax; ++j) {
-            dst_row[size_t(t) * kmax + j] = -1;
-            dst_rank[size_t(t) * kmax + j] = -1;
+            for (; j < kmax; ++j) {
+                if ((j & 3) == part) {
+                    dst_row[size_t(t) * kmax + j] = -1;
+                    dst_rank[size_t(t) * kmax + j] = -1;
+                }
+            }
         }
     }
 }
@@ -436,10 +559,12 @@ template <int NW>
 hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
                             const int32_t *rank_mask, const LayoutBufs &b, hipStream_t stream)
 {
+    const int epr_shift = (s.epr & (s.epr - 1)) == 0 ? __builtin_ctz(unsigned(s.epr)) : -1;
     if (s.T > 0)
         hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(s.nB), dim3(kCountBlock),
                            size_t(s.E) * sizeof(int32_t), stream, topk_idx, rank_mask, s.T, s.K, s.E, s.R,
-                           s.epr, s.nW, b.wave_mask, b.wave_base, b.blk_count, b.blk_ecount);
+                           s.epr, epr_shift, s.nW, b.wave_mask, b.wave_base, b.blk_count,
+                           b.blk_ecount);
     const bool self_scan = s.T > 0 && s.nB <= kSelfScanBlocks;
     if (!self_scan)
         hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kPosBlock), 0, stream, s.T, s.E, s.R,
@@ -450,7 +575,7 @@ hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
     if (s.T > 0)
         hipLaunchKernelGGL(pos_kernel, dim3(s.nW), dim3(kPosBlock), 0, stream, topk_idx, rank_mask,
                            s.T, s.K, s.E, s.R,
-                           s.C, s.epr, s.kmax, s.nB, b.wave_mask, b.wave_base, b.blk_count,
+                           s.C, s.epr, epr_shift, s.kmax, s.nB, b.wave_mask, b.wave_base, b.blk_count,
                            b.blk_ecount, b.is_token_in_rank, b.send_head, b.recv_src_idx,
                            b.dst_row, b.dst_rank, b.num_tokens_per_rank, b.num_tokens_per_expert,
                            b.rank_prefix_matrix, b.channel_prefix_matrix,

@@ -94,10 +94,12 @@ def _normal_mask_case(case):
         return config_inputs(2), [0, 7, 31]
     if case == "large":
         return config_inputs(4), [3, 64, 130, 143]   # ranks in all three 64-rank words
+    if case == "T20000":   # the layout's separate scan kernel (more than 32 count blocks)
+        return random_case(32, 20000, 72, 96, 6, 24, 9, mask=0.05, dup=0.1), [0, 5, 23]
     return random_case(31, 257, 136, 512, 8, 512, 7, mask=0.05, dup=0.1), [0, 63, 64, 300, 511]
 
 
-@pytest.mark.parametrize("case", ["tiny", "skewed", "large", "R512"])
+@pytest.mark.parametrize("case", ["tiny", "skewed", "large", "R512", "T20000"])
 def test_normal_path_rank_mask(case):
     """Ranks masked before the layout receive nothing (layout, dispatch and
     handle bit-exact with the oracle's masked layout); a rank masked later,

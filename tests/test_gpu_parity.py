@@ -108,6 +108,9 @@ RANDOM_CASES = [
     (4097, 136, 256, 16, 32, 13, 0.3, 0.2),
     (300, 512, 64, 64, 8, 3, 0.1, 0.1),
     (129, 1024, 448, 8, 448, 4096, 0.0, 0.0),
+    # more than 32 count blocks: the separate scan kernel of the layout
+    (20011, 64, 64, 4, 16, 7, 0.1, 0.1),
+    (65537, 16, 130, 3, 65, 33, 0.05, 0.0),
 ]
 
 
