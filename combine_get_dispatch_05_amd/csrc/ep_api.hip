@@ -3,9 +3,9 @@
 // Owns argument validation ("Memory Alignment and Validation" of the DeepEP-Lib
 // "Core Implementation" page: int4-multiple rows, aligned buffers), the
 // dispatch handle ("What the Handle Contains" of "How DeepEP Optimizes Handle
-// Reuse for Repeated Dispatches"), and a stream-ordered per-device pool of
-// handle arenas so that creating a handle per step does not call hipMalloc
-// after the first step.  Every kernel launch is enqueued on the caller's
+// Reuse for Repeated Dispatches"), and a per-device pool of handle arenas,
+// reused on the stream that freed them, so that creating a handle per step
+// does not call hipMalloc after the first step.  Every kernel launch is enqueued on the caller's
 // stream; the host only waits where the ABI says so (reading N back when a
 // caller asks for it or when a buffer is smaller than the worst case).
 
@@ -31,13 +31,19 @@ int hip_fail(hipError_t e)
 }
 
 // ------------------------------------------------------------------ pool
+//
+// A freed arena remembers the stream it was freed on and is handed out again
+// only to a later request on that same stream: stream order then puts the
+// new user's work after every kernel that used the arena, so no event (and
+// no event marker on the stream) is needed.  A request on another stream
+// gets a fresh allocation.  Destroying a stream waits for its work, so an
+// arena tagged with a destroyed stream is idle.  Trimming synchronizes the
+// device before it frees anything.
 
 struct Arena {
     void *ptr = nullptr;
     size_t bytes = 0;
-    hipEvent_t done = nullptr;  // recorded when the arena was returned
     hipStream_t freed_on = nullptr;
-    bool pending = false;
 };
 
 struct DevicePool {
@@ -71,17 +77,14 @@ int trim_pool(DevicePool &P)
         std::lock_guard<std::mutex> g(P.mu);
         drop.swap(P.free_list);
     }
+    if (drop.empty())
+        return EP_OK;
     int rc = EP_OK;
-    for (auto &kv : drop) {
-        Arena &a = kv.second;
-        if (a.pending) {
-            hipError_t e = hipEventSynchronize(a.done);
-            if (e != hipSuccess)
-                rc = hip_fail(e);
-        }
-        (void)hipEventDestroy(a.done);
-        (void)hipFree(a.ptr);
-    }
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess)
+        rc = hip_fail(e);
+    for (auto &kv : drop)
+        (void)hipFree(kv.second.ptr);
     return rc;
 }
 
@@ -89,28 +92,16 @@ int arena_get(int dev, size_t bytes, hipStream_t stream, Arena *out)
 {
     bytes = round_arena(bytes);
     DevicePool &P = pool_for(dev);
-    bool found = false;
     {
         std::lock_guard<std::mutex> g(P.mu);
-        auto it = P.free_list.lower_bound(bytes);
-        if (it != P.free_list.end() && it->first <= 2 * bytes) {
-            *out = it->second;
-            P.free_list.erase(it);
-            found = true;
-        }
-    }
-    if (found) {
-        // Work on the stream that returned the arena is already ordered
-        // before this call; only another stream has to wait for it.
-        if (out->pending && out->freed_on != stream) {
-            hipError_t e = hipStreamWaitEvent(stream, out->done, 0);
-            if (e != hipSuccess) {
-                std::lock_guard<std::mutex> g(P.mu);
-                P.free_list.emplace(out->bytes, *out);
-                return hip_fail(e);
+        for (auto it = P.free_list.lower_bound(bytes);
+             it != P.free_list.end() && it->first <= 2 * bytes; ++it) {
+            if (it->second.freed_on == stream) {
+                *out = it->second;
+                P.free_list.erase(it);
+                return EP_OK;
             }
         }
-        return EP_OK;
     }
     void *p = nullptr;
     hipError_t e = hipMalloc(&p, bytes);
@@ -125,29 +116,15 @@ int arena_get(int dev, size_t bytes, hipStream_t stream, Arena *out)
     }
     if (e != hipSuccess)
         return hip_fail(e);
-    hipEvent_t ev = nullptr;
-    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-    if (e != hipSuccess) {
-        (void)hipFree(p);
-        return hip_fail(e);
-    }
     out->ptr = p;
     out->bytes = bytes;
-    out->done = ev;
-    out->pending = false;
+    out->freed_on = stream;
     return EP_OK;
 }
 
 void arena_put(int dev, Arena a, hipStream_t stream)
 {
-    hipError_t e = hipEventRecord(a.done, stream);
-    a.pending = e == hipSuccess;
     a.freed_on = stream;
-    if (e != hipSuccess) {
-        // Cannot order the reuse after the pending work: wait for it here.
-        (void)hipGetLastError();
-        (void)hipStreamSynchronize(stream);
-    }
     DevicePool &P = pool_for(dev);
     std::lock_guard<std::mutex> g(P.mu);
     P.free_list.emplace(a.bytes, a);
@@ -711,6 +688,11 @@ int ep_set_tuning(const char *op, int a, int b, int c)
         return set_dispatch_tuning(a, b, c) ? EP_OK : EP_ERR_INVALID;
     if (std::strcmp(op, "combine") == 0)
         return set_combine_tuning(a, b, c) ? EP_OK : EP_ERR_INVALID;
+    if (std::strcmp(op, "ll") == 0) {
+        if (a == -1 && b == -1 && c == -1)
+            return set_ll_tuning(0) ? EP_OK : EP_ERR_INVALID;
+        return (b == 0 && c == 0 && set_ll_tuning(a)) ? EP_OK : EP_ERR_INVALID;
+    }
     return EP_ERR_INVALID;
 }
 
@@ -729,6 +711,14 @@ int ep_tuning_list(const char *op, int index, int *a, int *b, int *c)
         if (index >= 0 && index < n)
             combine_tuning_at(index, a, b, c);
         return n;
+    }
+    if (std::strcmp(op, "ll") == 0) {
+        if (index >= 0 && index < 3) {
+            *a = index;
+            *b = 0;
+            *c = 0;
+        }
+        return 3;
     }
     return -1;
 }

@@ -91,6 +91,9 @@ hipError_t launch_lb_prefetch_weights(const void *expert_weights, void *redundan
 // default choice.  Return false for a shape that is not compiled in.
 bool set_dispatch_tuning(int g, int vpt, int code);
 bool set_combine_tuning(int g, int vpt, int u);
+// Low-latency dispatch variant: 0 automatic (token-major for T*K <= 4096),
+// 1 expert-major always, 2 token-major whenever T*K allows.
+bool set_ll_tuning(int mode);
 int dispatch_tuning_count();
 void dispatch_tuning_at(int i, int *g, int *vpt, int *code);
 int combine_tuning_count();

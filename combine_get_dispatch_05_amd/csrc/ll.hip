@@ -22,6 +22,8 @@
 // the dispatch): the dispatch can store e4m3 codes with one fp32 scale per
 // 128 elements instead of bf16 rows.
 
+#include <atomic>
+
 #include "ep_internal.h"
 
 namespace ep {
@@ -84,6 +86,78 @@ __device__ __forceinline__ float row16_fmax(float v)
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1)
         v = fmaxf(v, __shfl_xor(v, m, 16));
+    return v;
+}
+
+// e4m3 codes of one 128-element block held by a 16-lane DPP row, 8 bf16 per
+// lane (v), and the block's amax (after the 1e-4 floor).  Every lane of the
+// row must take part.  Per block: amax = max(max |x|, 1e-4), code =
+// e4m3(x * (448 / amax)) rounded to nearest even, saturating.
+__device__ __forceinline__ uint2 fp8_block(const u32x4 &v, float &amax_out)
+{
+    // max |x| of the block as bf16 bits: for finite values the integer order
+    // of the magnitude bits is the numeric order.
+    uint32_t bits = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w = v[q];
+        const uint32_t lo = w & 0x7fffu, hi = (w >> 16) & 0x7fffu;
+        bits = bits > lo ? bits : lo;
+        bits = bits > hi ? bits : hi;
+    }
+    bits = row16_max(bits);
+    uint2 codes;
+    float amax;
+    if (bits < 0x7f80u) {
+        // finite block: |x * 448 / amax| stays below 464, where the hardware
+        // conversion rounds to nearest even exactly as e4m3_rne does
+        // (checked over every fp32 input).
+        amax = __uint_as_float(bits << 16);
+        amax = amax < 1e-4f ? 1e-4f : amax;
+        const float sinv = 448.0f / amax;
+        uint32_t c[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t w0v = v[2 * h], w1v = v[2 * h + 1];
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w0v) * sinv, bf16_hi(w0v) * sinv, 0,
+                                                     false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w1v) * sinv, bf16_hi(w1v) * sinv, pk,
+                                                 true);
+            c[h] = uint32_t(pk);
+        }
+        codes = make_uint2(c[0], c[1]);
+    } else {
+        // an infinity or NaN in the block: the general path
+        float f[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f[2 * q] = bf16_lo(v[q]);
+            f[2 * q + 1] = bf16_hi(v[q]);
+        }
+        amax = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            amax = fmaxf(amax, fabsf(f[q]));
+        amax = row16_fmax(amax);
+        amax = amax < 1e-4f ? 1e-4f : amax;
+        const float sinv = 448.0f / amax;
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            lo |= e4m3_rne(f[q] * sinv) << (8 * q);
+            hi |= e4m3_rne(f[q + 4] * sinv) << (8 * q);
+        }
+        codes = make_uint2(lo, hi);
+    }
+    amax_out = amax;
+    return codes;
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
     return v;
 }
 
@@ -242,66 +316,164 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
                 vv[k] = x[int64_t(tok[k]) * V + int64_t(blk[k]) * 16 + l16];
 #pragma unroll
             for (int k = 0; k < kRounds; ++k) {
-                // max |x| of the block as bf16 bits: for finite values the
-                // integer order of the magnitude bits is the numeric order.
-                uint32_t bits = 0;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t w = vv[k][q];
-                    const uint32_t lo = w & 0x7fffu, hi = (w >> 16) & 0x7fffu;
-                    bits = bits > lo ? bits : lo;
-                    bits = bits > hi ? bits : hi;
-                }
-                bits = row16_max(bits);
-                uint2 codes;
                 float amax;
-                if (bits < 0x7f80u) {
-                    // finite block: |x * 448 / amax| stays below 464, where the
-                    // hardware conversion rounds to nearest even exactly as
-                    // e4m3_rne does (checked over every fp32 input).
-                    amax = __uint_as_float(bits << 16);
-                    amax = amax < 1e-4f ? 1e-4f : amax;
-                    const float sinv = 448.0f / amax;
-                    uint32_t c[2];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint32_t w0v = vv[k][2 * h], w1v = vv[k][2 * h + 1];
-                        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w0v) * sinv,
-                                                                 bf16_hi(w0v) * sinv, 0, false);
-                        pk = __builtin_amdgcn_cvt_pk_fp8_f32(bf16_lo(w1v) * sinv,
-                                                             bf16_hi(w1v) * sinv, pk, true);
-                        c[h] = uint32_t(pk);
-                    }
-                    codes = make_uint2(c[0], c[1]);
-                } else {
-                    // an infinity or NaN in the block: the general path
-                    float f[8];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        f[2 * q] = bf16_lo(vv[k][q]);
-                        f[2 * q + 1] = bf16_hi(vv[k][q]);
-                    }
-                    amax = 0.0f;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q)
-                        amax = fmaxf(amax, fabsf(f[q]));
-                    amax = row16_fmax(amax);
-                    amax = amax < 1e-4f ? 1e-4f : amax;
-                    const float sinv = 448.0f / amax;
-                    uint32_t lo = 0, hi = 0;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        lo |= e4m3_rne(f[q] * sinv) << (8 * q);
-                        hi |= e4m3_rne(f[q + 4] * sinv) << (8 * q);
-                    }
-                    codes = make_uint2(lo, hi);
-                }
+                const uint2 codes = fp8_block(vv[k], amax);
                 if (row[k] >= 0) {
                     const int64_t cell = cell0 + row[k];
                     const int64_t col = int64_t(blk[k]) * 16 + l16;
                     packed_q[cell * V + col] = codes;  // 8 codes per lane
                     if (l16 == 0)
                         packed_scale[cell * nb + blk[k]] = amax / 448.0f;
+                }
+            }
+        }
+    }
+}
+
+constexpr int kLLTokPairs = 4096;  // token-major path for T*K up to this (ids held in LDS)
+
+// Token-major variant for small batches (T*K <= kLLTokPairs), same results
+// as ll_dispatch_kernel.  Every workgroup first loads the whole [T][K] id
+// table into LDS.  Workgroups [0, T*ny) are token workgroups: (t, slice y);
+// one wave per own pair (t, k) counts the earlier pairs (in (token, slot)
+// order) that name the same expert, which is the pair's slot; the slice of
+// x[t] is then read once and stored to all K destination cells (for FP8 each
+// 128-element block is quantized once).  The remaining workgroups handle
+// four experts each (one per wave): the expert's count and the -1 entries
+// of its unused src_info cells.
+template <bool kFP8>
+__global__ __launch_bounds__(kLLBlock) void ll_dispatch_tok_kernel(
+    const u32x4 *__restrict__ x, int T, int V, int K, int E, int R, int epr, int S, int ny,
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask,
+    u32x4 *__restrict__ packed_x, uint2 *__restrict__ packed_q, float *__restrict__ packed_scale,
+    int32_t *__restrict__ packed_count, int32_t *__restrict__ src_info,
+    int32_t *__restrict__ topk_slot)
+{
+    __shared__ int32_t s_ids[kLLTokPairs];
+    __shared__ int64_t s_cell[kMaxTopk];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid >> 6;
+    const int TK = T * K;
+    const int b = blockIdx.x;
+    const int ntok = T * ny;
+    const int t = b / ny;
+    const int yb = b - t * ny;
+
+    // The first vector of this lane's share of the row slice does not depend
+    // on the slots: its load is issued before anything else.
+    int c0 = 0, c1 = 0, b0 = 0, b1 = 0;
+    u32x4 first = {0, 0, 0, 0};
+    if (b < ntok) {
+        if (!kFP8) {
+            const int per = (V + ny - 1) / ny;
+            c0 = yb * per;
+            c1 = c0 + per < V ? c0 + per : V;
+            if (packed_x != nullptr && c0 + tid < c1)
+                first = x[int64_t(t) * V + c0 + tid];
+        } else {
+            const int nb = V / 16;
+            const int per = (nb + ny - 1) / ny;
+            b0 = yb * per;
+            b1 = b0 + per < nb ? b0 + per : nb;
+            if (b0 + (tid >> 4) < b1)
+                first = x[int64_t(t) * V + int64_t(b0 + (tid >> 4)) * 16 + (tid & 15)];
+        }
+    }
+
+    // expert id of every pair; -1 for masked slots and invalid ids
+    constexpr int kU = 4;
+    for (int i0 = 0; i0 < TK; i0 += kLLBlock * kU) {
+        int64_t v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int i = i0 + u * kLLBlock + tid;
+            v[u] = i < TK ? topk_idx[i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int i = i0 + u * kLLBlock + tid;
+            if (i < TK)
+                s_ids[i] = (v[u] >= 0 && v[u] < E) ? int(v[u]) : -1;
+        }
+    }
+    __syncthreads();
+
+    if (b >= ntok) {
+        const int e = (b - ntok) * kLLWaves + wid;
+        if (e < E) {
+            const int r = e / epr;
+            const bool masked = rank_mask != nullptr && rank_mask[r] != 0;
+            int cnt = 0;
+            if (!masked)
+                for (int i = lane; i < TK; i += kWave)
+                    cnt += s_ids[i] == e ? 1 : 0;
+            cnt = wave_sum(cnt);
+            const int64_t cell0 = (int64_t(e - r * epr) * R + r) * S;
+            if (lane == 0)
+                packed_count[int64_t(e - r * epr) * R + r] = cnt;
+            for (int q = (cnt < S ? cnt : S) + lane; q < S; q += kWave)
+                src_info[cell0 + q] = -1;
+        }
+        return;
+    }
+
+    for (int k = wid; k < K; k += kLLWaves) {
+        const int e = s_ids[t * K + k];
+        int64_t cell = -1;
+        int slot = -1;
+        if (e >= 0) {
+            const int r = e / epr;
+            if (rank_mask == nullptr || rank_mask[r] == 0) {
+                const int lim = t * K + k;
+                int cnt = 0;
+                for (int i = lane; i < lim; i += kWave)
+                    cnt += s_ids[i] == e ? 1 : 0;
+                cnt = wave_sum(cnt);
+                if (cnt < S) {
+                    slot = cnt;
+                    cell = (int64_t(e - r * epr) * R + r) * S + cnt;
+                }
+            }
+        }
+        if (lane == 0) {
+            s_cell[k] = cell;
+            if (yb == 0) {
+                topk_slot[t * K + k] = slot;
+                if (cell >= 0)
+                    src_info[cell] = t;
+            }
+        }
+    }
+    __syncthreads();
+
+    if (!kFP8) {
+        if (packed_x == nullptr)
+            return;
+        for (int c = c0 + tid; c < c1; c += kLLBlock) {
+            const u32x4 v = c == c0 + tid ? first : x[int64_t(t) * V + c];
+            for (int k = 0; k < K; ++k) {
+                const int64_t cell = s_cell[k];
+                if (cell >= 0)
+                    packed_x[cell * V + c] = v;
+            }
+        }
+    } else {
+        // 16 lane groups, one 128-element block each; a group is a DPP row,
+        // and a block's loop bounds are the same for all of its lanes.
+        const int nb = V / 16;
+        const int g = tid >> 4;
+        const int l16 = tid & 15;
+        for (int bb = b0 + g; bb < b1; bb += kLLBlock / 16) {
+            const u32x4 v = bb == b0 + g ? first : x[int64_t(t) * V + int64_t(bb) * 16 + l16];
+            float amax;
+            const uint2 codes = fp8_block(v, amax);
+            for (int k = 0; k < K; ++k) {
+                const int64_t cell = s_cell[k];
+                if (cell >= 0) {
+                    packed_q[cell * V + int64_t(bb) * 16 + l16] = codes;
+                    if (l16 == 0)
+                        packed_scale[cell * nb + bb] = amax / 448.0f;
                 }
             }
         }
@@ -382,7 +554,17 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_kernel(
     }
 }
 
+std::atomic<int> g_ll_mode{0};  // 0 automatic, 1 expert-major, 2 token-major when it fits
+
 }  // namespace
+
+bool set_ll_tuning(int mode)
+{
+    if (mode < 0 || mode > 2)
+        return false;
+    g_ll_mode = mode;
+    return true;
+}
 
 hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
                               const int64_t *topk_idx, const int32_t *rank_mask, void *packed_x,
@@ -391,6 +573,23 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
 {
     const int E = d.num_experts, R = d.num_ranks;
     const bool fp8 = packed_q != nullptr;
+    const int64_t TK = int64_t(d.num_tokens) * d.num_topk;
+    if (g_ll_mode.load() != 1 && TK <= kLLTokPairs) {
+        // token-major: slices of about 256 vectors (bf16) or 16 blocks (fp8)
+        const int V = d.hidden / 8;
+        const bool rows = fp8 || packed_x != nullptr;
+        int ny = 1;
+        if (rows)
+            ny = fp8 ? (V / 16 + 15) / 16 : (V + kLLBlock - 1) / kLLBlock;
+        const int64_t blocks = int64_t(d.num_tokens) * ny + (E + kLLWaves - 1) / kLLWaves;
+        auto tk = fp8 ? ll_dispatch_tok_kernel<true> : ll_dispatch_tok_kernel<false>;
+        hipLaunchKernelGGL(tk, dim3(unsigned(blocks)), dim3(kLLBlock), 0, stream,
+                           static_cast<const u32x4 *>(x), d.num_tokens, V, d.num_topk, E, R,
+                           E / R, num_slots, ny, topk_idx, rank_mask,
+                           static_cast<u32x4 *>(packed_x), static_cast<uint2 *>(packed_q),
+                           packed_scale, packed_count, src_info, topk_slot);
+        return hipGetLastError();
+    }
     auto kernel = fp8 ? ll_dispatch_kernel<true> : ll_dispatch_kernel<false>;
     // Copy splits per expert, from the expected rows per expert T*K/E: one
     // workgroup round copies 2048 vectors (bf16) or 64 blocks (fp8).

@@ -42,8 +42,8 @@
  *   - Concurrency: calls may run on different streams concurrently as long
  *     as they do not write the same caller memory.  One handle may be read by
  *     several calls at once; it must not be freed while they are in flight
- *     on other streams than its last one (ep_handle_free orders the free
- *     after the last call that used the handle).
+ *     on other streams than its last one (the freed memory is reused only by
+ *     work on the handle's last stream).
  */
 #ifndef EP_H
 #define EP_H
@@ -299,13 +299,14 @@ int ep_handle_dims(const ep_handle *handle, ep_dims *dims);
 size_t ep_handle_nbytes(const ep_handle *handle);
 
 /* [P1] "Explicit Resource Cleanup": release a handle.  NULL is a no-op.  The
- * memory returns to the library's per-device pool, ordered after all work
- * enqueued so far on the handle's last stream; it is never reused before
- * that work completes. */
+ * memory returns to the library's per-device pool, tagged with the handle's
+ * last stream; only a later handle made on that same stream reuses it, so
+ * stream order puts every use of the memory before its reuse.  Nothing is
+ * enqueued. */
 void ep_handle_free(ep_handle *handle);
 
 /* Release every pooled device allocation of the calling thread's current
- * device (waits for their pending work).  Returns an ep_status. */
+ * device (synchronizes the device first).  Returns an ep_status. */
 int ep_pool_trim(void);
 
 /* Launch-shape override for the pack ("dispatch") or the reduce ("combine")
@@ -318,7 +319,10 @@ int ep_pool_trim(void);
  * compiled-in shapes.  a = b = c = -1 restores the default choice; a shape
  * that is not compiled in returns EP_ERR_INVALID.  The env vars
  * EP_TUNE_DISPATCH="G,VPT,c" and EP_TUNE_COMBINE="G,VPT,c" set the initial
- * override. */
+ * override.
+ * op "ll" picks the low-latency dispatch kernel (b = c = 0): a = 0 automatic
+ * (token-major when T*K <= 4096, else expert-major), 1 expert-major always,
+ * 2 token-major whenever T*K <= 4096.  Both give identical results. */
 int ep_set_tuning(const char *op, int a, int b, int c);
 
 /* Enumerate the compiled-in shapes of `op`: writes shape `index` (if in

@@ -11,3 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+@pytest.fixture(params=[1, 2], ids=["expert_major", "token_major"])
+def ll_mode(request):
+    """Run a low-latency test under both dispatch kernels (the library picks
+    one by T*K; both must give identical results)."""
+    from combine_get_dispatch_05_amd import abi
+    abi.set_tuning("ll", request.param, 0, 0)
+    yield request.param
+    abi.set_tuning("ll")

@@ -185,3 +185,11 @@ def test_mask_and_load_balance_rules():
         assert fn(fake, fake, fake, 70000, 8, 16, S) == abi.EP_ERR_INVALID
         assert fn(None, fake, fake, 4, 8, 16, S) == abi.EP_ERR_INVALID
         assert fn(fake, fake, ctypes.c_void_p(0x10004), 4, 8, 16, S) == abi.EP_ERR_ALIGN
+
+
+def test_ll_tuning_modes():
+    assert abi.tunings("ll") == [(0, 0, 0), (1, 0, 0), (2, 0, 0)]
+    assert L.ep_set_tuning(b"ll", 3, 0, 0) == abi.EP_ERR_INVALID
+    assert L.ep_set_tuning(b"ll", 1, 1, 0) == abi.EP_ERR_INVALID
+    assert L.ep_set_tuning(b"ll", 2, 0, 0) == abi.EP_OK
+    abi.set_tuning("ll")  # back to automatic

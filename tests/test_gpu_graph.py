@@ -41,7 +41,7 @@ def _eager_noise():
     torch.cuda.synchronize()
 
 
-def test_ll_decode_step_graph():
+def test_ll_decode_step_graph(ll_mode):
     base = config_inputs(3)
     E, R, S, T, H, K = base.E, base.R, base.slots, base.T, base.H, base.K
     epr = E // R

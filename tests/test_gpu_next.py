@@ -35,7 +35,7 @@ def _announce(request):
 
 
 @pytest.mark.parametrize("case", ["decode", "random"])
-def test_ll_rank_mask(case):
+def test_ll_rank_mask(case, ll_mode):
     if case == "decode":
         inp = config_inputs(3)
         masked = [3, 17, 31]
@@ -183,7 +183,7 @@ def test_combine_bias(cfg):
 
 
 @pytest.mark.parametrize("case", ["decode", "edge", "nonfinite", "masked"])
-def test_ll_dispatch_fp8(case):
+def test_ll_dispatch_fp8(case, ll_mode):
     if case == "decode":
         inp, m = config_inputs(3), None
     elif case == "edge":

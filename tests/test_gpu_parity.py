@@ -150,7 +150,7 @@ def run_ll(inp, seed=0):
                       what="ll combine (random)")
 
 
-def test_ll_config3():
+def test_ll_config3(ll_mode):
     run_ll(config_inputs(3))
 
 
@@ -162,11 +162,13 @@ LL_CASES = [
     (200, 2048, 64, 6, 8, 256, 0.1, 0.0),
     (64, 7168, 288, 8, 144, 64, 0.05, 0.0),
     (300, 16384, 32, 8, 32, 300, 0.0, 0.3),
+    (512, 520, 96, 8, 12, 512, 0.1, 0.2),     # T*K = 4096: the largest token-major batch
+    (600, 256, 64, 8, 16, 640, 0.05, 0.1),    # T*K = 4800: expert-major in every mode
 ]
 
 
 @pytest.mark.parametrize("case", LL_CASES, ids=lambda c: "T%d_H%d_E%d_K%d_R%d_S%d" % c[:6])
-def test_ll_random(case):
+def test_ll_random(case, ll_mode):
     T, H, E, K, R, S, mask, dup = case
     run_ll(random_case(3 + T, T, H, E, K, R, 1, mask=mask, dup=dup, slots=S), seed=T)
 
