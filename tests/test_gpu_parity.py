@@ -111,6 +111,8 @@ RANDOM_CASES = [
     # more than 32 count blocks: the separate scan kernel of the layout
     (20011, 64, 64, 4, 16, 7, 0.1, 0.1),
     (65537, 16, 130, 3, 65, 33, 0.05, 0.0),
+    # the largest expert count, top-k and rank count the library accepts
+    (100, 64, 8192, 64, 512, 4096, 0.05, 0.05),
 ]
 
 
@@ -164,6 +166,7 @@ LL_CASES = [
     (300, 16384, 32, 8, 32, 300, 0.0, 0.3),
     (512, 520, 96, 8, 12, 512, 0.1, 0.2),     # T*K = 4096: the largest token-major batch
     (600, 256, 64, 8, 16, 640, 0.05, 0.1),    # T*K = 4800: expert-major in every mode
+    (64, 128, 8192, 64, 512, 64, 0.05, 0.05),  # the largest expert count, top-k, ranks
 ]
 
 
