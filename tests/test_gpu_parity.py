@@ -167,6 +167,7 @@ LL_CASES = [
     (512, 520, 96, 8, 12, 512, 0.1, 0.2),     # T*K = 4096: the largest token-major batch
     (600, 256, 64, 8, 16, 640, 0.05, 0.1),    # T*K = 4800: expert-major in every mode
     (64, 128, 8192, 64, 512, 64, 0.05, 0.05),  # the largest expert count, top-k, ranks
+    (32, 64, 8, 8, 4, 32, 0.0, 0.9),     # repeated experts overflow the slots: 39 pairs dropped
 ]
 
 
