@@ -303,7 +303,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and args.cpu_seconds > 0:
         cpu = cpu_baseline(tr, dc, x2_bits=random_rows(T, H, 0, tag=11), budget=args.cpu_seconds,
-                           step_bytes=step_bytes)
+                           step_bytes=step_bytes, op_bytes=by)
 
     rec = {
         "metric": METRIC,
@@ -452,24 +452,51 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     return rep
 
 
-def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int):
+def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int, op_bytes=None):
     """The oracle, as it stands, on the same rows of the same workload:
     whole passes (layout, dispatch, cached dispatch, combine, LL dispatch,
-    LL combine) until ``budget`` seconds of CPU work are spent."""
+    LL combine) until ``budget`` seconds of CPU work are spent, with the
+    process pinned to one core.  Also the median time of each operation over
+    the passes (and its rate on the same algorithmic bytes)."""
     import oracle
+    pinned = None
+    old_aff = None
+    if hasattr(os, "sched_setaffinity"):
+        try:
+            old_aff = os.sched_getaffinity(0)
+            pinned = min(old_aff)
+            os.sched_setaffinity(0, {pinned})
+        except OSError:
+            pinned = None
+    names = ["layout", "dispatch", "dispatch_cached", "combine", "ll_dispatch", "ll_combine"]
+    times = {n: [] for n in names}
     passes = 0
     t0 = time.perf_counter()
-    while True:
-        lay = oracle.layout(tr.topk_idx, tr.E, tr.R, tr.C)
-        rx, rti, rtw = oracle.dispatch(tr.x, tr.topk_idx, tr.topk_weights, tr.E, tr.R, lay)
-        oracle.dispatch(x2_bits, None, None, tr.E, tr.R, lay, with_topk=False)
-        oracle.combine(rx, lay, rtw)
-        buf, _, _, _ = oracle.ll_dispatch(dc.x, dc.topk_idx, dc.E, dc.R, dc.slots)
-        oracle.ll_combine(buf, dc.topk_idx, dc.topk_weights, dc.E, dc.R)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= budget:
-            break
+    try:
+        while True:
+            c0 = time.perf_counter()
+            lay = oracle.layout(tr.topk_idx, tr.E, tr.R, tr.C)
+            c1 = time.perf_counter()
+            rx, rti, rtw = oracle.dispatch(tr.x, tr.topk_idx, tr.topk_weights, tr.E, tr.R, lay)
+            c2 = time.perf_counter()
+            oracle.dispatch(x2_bits, None, None, tr.E, tr.R, lay, with_topk=False)
+            c3 = time.perf_counter()
+            oracle.combine(rx, lay, rtw)
+            c4 = time.perf_counter()
+            buf, _, _, _ = oracle.ll_dispatch(dc.x, dc.topk_idx, dc.E, dc.R, dc.slots)
+            c5 = time.perf_counter()
+            oracle.ll_combine(buf, dc.topk_idx, dc.topk_weights, dc.E, dc.R)
+            c6 = time.perf_counter()
+            for n, (u, v) in zip(names, [(c0, c1), (c1, c2), (c2, c3), (c3, c4), (c4, c5),
+                                         (c5, c6)]):
+                times[n].append(v - u)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                break
+    finally:
+        if old_aff is not None and pinned is not None:
+            os.sched_setaffinity(0, old_aff)
     model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -478,10 +505,18 @@ def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int):
                 break
     except OSError:
         pass
+    per_op = {}
+    for n in names:
+        med = sorted(times[n])[len(times[n]) // 2]
+        per_op[n] = {"median_ms": round(med * 1e3, 3)}
+        if op_bytes is not None:
+            per_op[n]["gbs"] = round(op_bytes[n] / med / 1e9, 3)
     return {"value": round(step_bytes * passes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{passes} whole passes of the benchmark step (same workload, same rows) "
-                      f"in {el:.1f} s, single-threaded C oracle",
+                      f"in {el:.1f} s, single-threaded C oracle"
+                      + (f" pinned to CPU {pinned}" if pinned is not None else ""),
+            "per_op": per_op,
             "host_cpu": model or platform.processor(), "host_nproc": os.cpu_count()}
 
 

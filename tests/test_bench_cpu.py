@@ -43,8 +43,13 @@ def test_cpu_baseline_leg():
     from gen import config_inputs, random_rows
     tr = config_inputs(1)
     dc = config_inputs(3)
+    names = ["layout", "dispatch", "dispatch_cached", "combine", "ll_dispatch", "ll_combine"]
     out = bench.cpu_baseline(tr, dc, x2_bits=random_rows(tr.T, tr.H, 0, tag=11), budget=0.01,
-                             step_bytes=1_000_000)
+                             step_bytes=1_000_000, op_bytes={n: 10**9 for n in names})
     assert out["kind"] == "oracle" and out["cores"] == 1 and out["unit"] == "GB/s"
     assert out["value"] > 0 and "whole passes" in out["sample"]
     assert np.isfinite(out["value"])
+    assert sorted(out["per_op"]) == sorted(names)
+    assert all(v["median_ms"] > 0 and v["gbs"] > 0 for v in out["per_op"].values())
+    if hasattr(os, "sched_getaffinity"):
+        assert len(os.sched_getaffinity(0)) >= 1  # the affinity is restored
