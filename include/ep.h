@@ -70,7 +70,7 @@ typedef enum ep_status {
 /* Problem sizes.  Limits: 0 <= num_tokens <= 2^24; hidden > 0, hidden % 8 == 0,
  * hidden <= 2^20; 1 <= num_topk <= 64; 1 <= num_ranks <= 512;
  * num_experts % num_ranks == 0, num_experts <= 8192; num_channels >= 1,
- * num_channels <= 2^20. */
+ * num_channels <= 4096. */
 typedef struct ep_dims {
     int32_t num_tokens;   /* T */
     int32_t hidden;       /* H, bf16 elements per token row */

@@ -193,3 +193,17 @@ def test_ll_tuning_modes():
     assert L.ep_set_tuning(b"ll", 1, 1, 0) == abi.EP_ERR_INVALID
     assert L.ep_set_tuning(b"ll", 2, 0, 0) == abi.EP_OK
     abi.set_tuning("ll")  # back to automatic
+
+
+def test_plain_c_program_uses_the_abi():
+    """include/ep.h and libep.so from a C program (no Python binding): static
+    calls and argument validation."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("c_abi_build",
+                                                  os.path.join(ROOT, "tests", "c_abi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    exe = mod.build()
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert "abi_check cpu: ok" in r.stdout
