@@ -14,8 +14,9 @@
 // Both are streaming copies/reductions bound by HBM bandwidth: one workgroup
 // per (replica, 2048-element chunk), 16-byte vectors, two vectors per lane.
 // In the reduction only the workgroup of an expert's first replica works (it
-// walks all of that expert's replicas in order), so every output element is
-// written once, in a fixed order, with no atomics.
+// walks all of that expert's replicas in order, finding them with wave-wide
+// ballots over the mapping), so every output element is written once, in a
+// fixed order, with no atomics.
 //
 // "DeepEP Buffer Class API for Expert Parallel Communication", section
 // "Dynamic Rank Masking": low_latency_update_mask_buffer / clean_mask_buffer
@@ -37,13 +38,19 @@ __global__ __launch_bounds__(kLBBlock) void lb_reduce_grads_kernel(
     const u32x4 *__restrict__ redundant, u32x4 *__restrict__ expert,
     const int64_t *__restrict__ mapping, int num_replicas, int num_experts, int64_t vecs)
 {
+    const int lane = threadIdx.x & (kWave - 1);
     const int j = blockIdx.y;
     const int64_t e = mapping[j];
     if (e < 0 || e >= num_experts)
         return;
-    for (int jj = 0; jj < j; ++jj)  // an earlier replica of e does the work
-        if (mapping[jj] == e)
+    // An earlier replica of e does the work.  The mapping is scanned 64
+    // entries per wave-wide load; every wave of the block reaches the same
+    // answer, and the kernel has no barrier.
+    for (int c = 0; c < j; c += kWave) {
+        const int jj = c + lane;
+        if (wave_ballot(jj < j && mapping[jj] == e) != 0)
             return;
+    }
     const int64_t v0 = int64_t(blockIdx.x) * kLBBlock * kLBVec;
     float acc[kLBVec][8];
     u32x4 cur[kLBVec];
@@ -57,18 +64,25 @@ __global__ __launch_bounds__(kLBBlock) void lb_reduce_grads_kernel(
             acc[i][2 * q + 1] = bf16_hi(cur[i][q]);
         }
     }
-    for (int jj = j; jj < num_replicas; ++jj) {
-        if (mapping[jj] != e)
-            continue;
+    // e's replicas from j on, in ascending order: a ballot per 64 entries,
+    // then its set bits lowest first.
+    for (int c = j; c < num_replicas; c += kWave) {
+        const int jc = c + lane;
+        uint64_t hits = wave_ballot(jc < num_replicas && mapping[jc] == e);
+        while (hits) {
+            const int64_t jj = c + __ffsll((unsigned long long)hits) - 1;
+            hits &= hits - 1;
 #pragma unroll
-        for (int i = 0; i < kLBVec; ++i) {
-            const int64_t idx = v0 + i * kLBBlock + threadIdx.x;
-            const u32x4 rv = idx < vecs ? __builtin_nontemporal_load(redundant + jj * vecs + idx)
-                                        : u32x4{0, 0, 0, 0};
+            for (int i = 0; i < kLBVec; ++i) {
+                const int64_t idx = v0 + i * kLBBlock + threadIdx.x;
+                const u32x4 rv = idx < vecs
+                                     ? __builtin_nontemporal_load(redundant + jj * vecs + idx)
+                                     : u32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[i][2 * q] += bf16_lo(rv[q]);
-                acc[i][2 * q + 1] += bf16_hi(rv[q]);
+                for (int q = 0; q < 4; ++q) {
+                    acc[i][2 * q] += bf16_lo(rv[q]);
+                    acc[i][2 * q + 1] += bf16_hi(rv[q]);
+                }
             }
         }
     }

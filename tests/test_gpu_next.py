@@ -254,3 +254,24 @@ def test_lb_ops(P):
     buf.lb_reduce_grads(dev_bf16(rg), egd, mp)
     exp = oracle.lb_reduce_grads(rg, ew, mapping)
     assert_bf16_close(host_bits(egd), exp, what="lb_reduce_grads")
+
+
+def test_lb_ops_many_replicas():
+    """300 replicas over 40 experts: repeated experts and invalid entries
+    spread over several 64-entry scans of the mapping."""
+    rng = np.random.default_rng(77)
+    E, n_rep, P = 40, 300, 136
+    mapping = rng.integers(-1, E + 3, n_rep).astype(np.int64)
+    mapping[:5] = 7   # one expert replicated in a run, and again later
+    mapping[250] = 7
+    buf = epm.Buffer(1, 1)
+    mp = dev(mapping)
+    ew = random_rows(E, P, 5, tag=41)
+    rw0 = random_rows(n_rep, P, 5, tag=42)
+    rwd = dev_bf16(rw0)
+    buf.lb_prefetch_weights(rwd, dev_bf16(ew), mp)
+    np.testing.assert_array_equal(host_bits(rwd), oracle.lb_prefetch_weights(ew, rw0, mapping))
+    rg = random_rows(n_rep, P, 5, tag=43)
+    egd = dev_bf16(ew)
+    buf.lb_reduce_grads(dev_bf16(rg), egd, mp)
+    assert_bf16_close(host_bits(egd), oracle.lb_reduce_grads(rg, ew, mapping), what="many replicas")
