@@ -149,11 +149,22 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
         }
 
         if (combined_topk_weights != nullptr && slice == 0) {
+            // up to 8 rows' weights loaded at once, then added in rank order
+            constexpr int kW = 8;
             for (int k = gt; k < K; k += G) {
                 float w = 0.0f;
-                for (int j = 0; j < nhit; ++j) {
-                    const int64_t row = __builtin_amdgcn_readlane(rowv, j);
-                    w += recv_topk_weights[row * K + k];
+                for (int j0 = 0; j0 < nhit; j0 += kW) {
+                    float wv[kW];
+#pragma unroll
+                    for (int u = 0; u < kW; ++u) {
+                        const int j = j0 + u < nhit ? j0 + u : 0;
+                        const int64_t row = __builtin_amdgcn_readlane(rowv, j);
+                        wv[u] = recv_topk_weights[row * K + k];
+                    }
+#pragma unroll
+                    for (int u = 0; u < kW; ++u)
+                        if (j0 + u < nhit)
+                            w += wv[u];
                 }
                 combined_topk_weights[int64_t(t) * K + k] = w;
             }
