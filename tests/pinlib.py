@@ -575,6 +575,7 @@ def check_lb_ops(seed=0, E=12, n_rep=7, P=37):
     rng = np.random.default_rng(seed)
     mapping = rng.integers(-1, E, n_rep).astype(np.int64)
     mapping[0] = E + 3  # an invalid entry is ignored
+    mapping[1] = mapping[n_rep - 1] = 2  # an expert with two replicas, far apart
     ew = rng.integers(-30, 31, (E, P)).astype(np.float32)
     rg = rng.integers(-30, 31, (n_rep, P)).astype(np.float32)
     # reduce: small integers sum exactly; replicas in any order give the same

@@ -64,6 +64,20 @@ MUTANTS = [
      "            if (0)\n                continue;"),
     ("combine weights ignore the rank mask", "if (p < 0 || rank_masked(rank_mask, r))",
      "if (p < 0)"),
+    ("LL combine-time mask ignored", "if (combine_mask != NULL && combine_mask[e / epr] != 0)",
+     "if (combine_mask != NULL && combine_mask[e / epr] != 0 && 0)"),
+    ("LL combine cell with rank and local expert swapped",
+     "int64_t cell = ((e % epr) * R + e / epr) * num_slots + s;",
+     "int64_t cell = ((e / epr) * epr + e % epr) * num_slots + s;"),
+    ("fp8 amax always from the first block",
+     "for (int64_t h = b * 128; h < (b + 1) * 128; ++h) {\n                float v = fabsf",
+     "for (int64_t h = 0; h < 128; ++h) {\n                float v = fabsf"),
+    ("e4m3 subnormals in units of 2^-8", "double q = rint(a * 512.0);", "double q = rint(a * 256.0);"),
+    ("e4m3 exponent bias 8", "int code = ((e + 7) << 3) | (int)mi;", "int code = ((e + 8) << 3) | (int)mi;"),
+    ("combine bias1 ignored", "if (bias1 != NULL)", "if (bias1 != NULL && 0)"),
+    ("reduce grads keeps only the last replica",
+     "acc[p] += bf16_to_f32(redundant_grads[j * P + p]);",
+     "acc[p] = bf16_to_f32(expert_grads[e * P + p]) + bf16_to_f32(redundant_grads[j * P + p]);"),
     ("prefetch ignores mapping", "memcpy(redundant_weights + j * P, expert_weights + e * P,",
      "memcpy(redundant_weights + j * P, expert_weights + j % E * P,"),
 ]
