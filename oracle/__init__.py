@@ -54,6 +54,8 @@ def _configure(lib):
     lib.oracle_f32_to_e4m3_array.restype = None
     lib.oracle_ll_dispatch_fp8.argtypes = [i64] * 6 + [p] * 8
     lib.oracle_ll_dispatch_fp8.restype = ctypes.c_int
+    lib.oracle_ll_combine_fp8.argtypes = [i64] * 6 + [p] * 7
+    lib.oracle_ll_combine_fp8.restype = ctypes.c_int
     lib.oracle_lb_reduce_grads.argtypes = [i64] * 3 + [p] * 3
     lib.oracle_lb_reduce_grads.restype = None
     lib.oracle_lb_prefetch_weights.argtypes = [i64] * 3 + [p] * 3
@@ -222,6 +224,27 @@ def ll_combine(buf: np.ndarray, topk_idx: np.ndarray, topk_weights: np.ndarray, 
                                    _ptr(m), _ptr(cm), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_ll_combine rejected its arguments")
+    return out
+
+
+def ll_combine_fp8(q: np.ndarray, scale: np.ndarray, topk_idx: np.ndarray,
+                   topk_weights: np.ndarray, E: int, R: int, rank_mask=None, combine_mask=None):
+    """The LL combine of an FP8 payload: codes q [E/R, R, slots, H] (uint8)
+    and per-128-block scales [E/R, R, slots, H/128] decoded in the sum."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sc = np.ascontiguousarray(scale, dtype=np.float32)
+    epr, R2, num_slots, H = q.shape
+    assert R2 == R and epr == E // R and sc.shape == (epr, R, num_slots, H // 128)
+    ti = np.ascontiguousarray(topk_idx, dtype=np.int64)
+    tw = np.ascontiguousarray(topk_weights, dtype=np.float32)
+    T, K = ti.shape
+    out = np.empty((T, H), np.uint16)
+    m = _mask(rank_mask, R)
+    cm = _mask(combine_mask, R)
+    rc = _load().oracle_ll_combine_fp8(T, H, K, E, R, num_slots, _ptr(q), _ptr(sc), _ptr(ti),
+                                       _ptr(tw), _ptr(m), _ptr(cm), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_ll_combine_fp8 rejected its arguments")
     return out
 
 

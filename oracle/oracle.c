@@ -553,6 +553,54 @@ void oracle_lb_reduce_grads(int64_t n_rep, int64_t E, int64_t P, const uint16_t 
     free(acc);
 }
 
+/*
+ * Low-latency combine of an FP8 payload ([P1] "IB-GDA Kernels": FP8 with
+ * use_fp8; reading: the codes and per-128-element-block scales of
+ * oracle_ll_dispatch_fp8 are decoded in the combine).  Each element of a
+ * cell is decoded exactly to fp32 and multiplied by its block's scale in
+ * fp32 (one rounding); the weighted sum then runs exactly as in
+ * oracle_ll_combine: fmaf over k ascending from +0, one RNE to bf16.
+ *   q     [epr][R][num_slots][H] e4m3 codes
+ *   scale [epr][R][num_slots][H/128] fp32
+ */
+int oracle_ll_combine_fp8(int64_t T, int64_t H, int64_t K, int64_t E, int64_t R,
+                          int64_t num_slots, const uint8_t *q, const float *scale,
+                          const int64_t *topk_idx, const float *topk_weights,
+                          const int32_t *rank_mask, const int32_t *combine_mask, uint16_t *out)
+{
+    if (E % R != 0 || num_slots < 1 || H % 128 != 0)
+        return -1;
+    int64_t epr = E / R, nb = H / 128;
+    int32_t *slot = (int32_t *)malloc((size_t)(T * K > 0 ? T * K : 1) * sizeof(int32_t));
+    int32_t *cnt = (int32_t *)malloc((size_t)E * sizeof(int32_t));
+    float *acc = (float *)malloc((size_t)(H > 0 ? H : 1) * sizeof(float));
+    ll_slots(T, K, E, epr, rank_mask, topk_idx, slot, cnt);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t h = 0; h < H; ++h)
+            acc[h] = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t e = topk_idx[t * K + k];
+            int64_t s = slot[t * K + k];
+            if (e < 0 || s < 0 || s >= num_slots)
+                continue;
+            if (combine_mask != NULL && combine_mask[e / epr] != 0)
+                continue;
+            float w = topk_weights[t * K + k];
+            int64_t cell = ((e % epr) * R + e / epr) * num_slots + s;
+            for (int64_t h = 0; h < H; ++h) {
+                float v = oracle_e4m3_to_f32(q[cell * H + h]) * scale[cell * nb + h / 128];
+                acc[h] = fmaf(w, v, acc[h]);
+            }
+        }
+        for (int64_t h = 0; h < H; ++h)
+            out[t * H + h] = f32_to_bf16_rne(acc[h]);
+    }
+    free(acc);
+    free(cnt);
+    free(slot);
+    return 0;
+}
+
 /* [P5] 10.2: lb_prefetch_weights copies each expert's weights into its
  * replicas' slots before the expert computation: redundant[j] =
  * expert[mapping[j]]; replicas with an invalid mapping entry are untouched. */

@@ -777,6 +777,54 @@ def check_ll_fp8_nonfinite():
     return q, sc
 
 
+def check_ll_combine_fp8(inp, rank_mask=None, seed=0):
+    """The FP8 LL combine reduces to the (pinned) bf16 LL combine: every
+    e4m3 value is exact in bf16, and a power-of-two scale keeps it exact, so
+    with such scales the decoded, scaled payload is a bf16 buffer and both
+    combines must agree bit for bit.  Each 128-element block gets its own
+    scale 2^k (k from -3 to 3), which pins the scale indexing.  A dispatch /
+    combine round trip stays within the quantization error of the bf16 one."""
+    E, R, S = inp.E, inp.R, inp.slots
+    H = inp.x.shape[1]
+    epr = E // R
+    nb = H // 128
+    rng = np.random.default_rng(seed + 91)
+    q = rng.integers(0, 256, (epr, R, S, H)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x3A          # no NaN codes in this pin
+    k = rng.integers(-3, 4, (epr, R, S, nb))
+    sc = np.ldexp(np.ones((epr, R, S, nb)), k).astype(np.float32)
+    vals = e4m3_table()
+    deq = (vals[q.astype(np.int64)] * np.repeat(sc, 128, axis=3)).astype(np.float32)
+    buf = bits_from_f32_exact(deq.reshape(-1, H)).reshape(deq.shape)
+    w = inp.topk_weights
+    a = O.ll_combine_fp8(q, sc, inp.topk_idx, w, E, R, rank_mask=rank_mask)
+    b = O.ll_combine(buf, inp.topk_idx, w, E, R, rank_mask=rank_mask)
+    np.testing.assert_array_equal(a, b)
+    # unit scales: the codes' own values
+    ones = np.ones_like(sc)
+    buf1 = bits_from_f32_exact(vals[q.astype(np.int64)].astype(np.float32).reshape(-1, H))
+    np.testing.assert_array_equal(O.ll_combine_fp8(q, ones, inp.topk_idx, w, E, R, rank_mask=rank_mask),
+                                  O.ll_combine(buf1.reshape(q.shape), inp.topk_idx, w, E, R,
+                                               rank_mask=rank_mask))
+    # combine-time mask: a masked rank's terms drop out as in the bf16 combine
+    cm = np.zeros(R, np.int32)
+    cm[R // 2] = 1
+    np.testing.assert_array_equal(
+        O.ll_combine_fp8(q, sc, inp.topk_idx, w, E, R, combine_mask=cm),
+        O.ll_combine(buf, inp.topk_idx, w, E, R, combine_mask=cm))
+    # round trip through the FP8 dispatch
+    fq, fs, _, _, _ = O.ll_dispatch_fp8(inp.x, inp.topk_idx, E, R, S, rank_mask=rank_mask)
+    rt = f32_from_bits(O.ll_combine_fp8(fq, fs, inp.topk_idx, w, E, R, rank_mask=rank_mask))
+    bq, _, _, _ = O.ll_dispatch(inp.x, inp.topk_idx, E, R, S, rank_mask=rank_mask)
+    ref = f32_from_bits(O.ll_combine(bq, inp.topk_idx, w, E, R, rank_mask=rank_mask))
+    # each term moves by at most half an e4m3 step of its block (<= 2^-4 of
+    # the block's amax); the weights of a token sum to at most 1
+    xs = np.abs(f32_from_bits(inp.x)).reshape(inp.T, nb, 128).max(axis=2)
+    bound = np.repeat(xs.max(axis=0, keepdims=True), 128, axis=1) * 2.0 ** -4 + 2.0 ** -6 * np.abs(ref)
+    assert np.all(np.abs(rt - ref) <= bound * 1.01 + 1e-6)
+    return a
+
+
 # -------------------------------------------------------- exact tie rounding
 
 

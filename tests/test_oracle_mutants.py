@@ -78,6 +78,12 @@ MUTANTS = [
     ("reduce grads keeps only the last replica",
      "acc[p] += bf16_to_f32(redundant_grads[j * P + p]);",
      "acc[p] = bf16_to_f32(expert_grads[e * P + p]) + bf16_to_f32(redundant_grads[j * P + p]);"),
+    ("fp8 combine ignores the scales",
+     "float v = oracle_e4m3_to_f32(q[cell * H + h]) * scale[cell * nb + h / 128];",
+     "float v = oracle_e4m3_to_f32(q[cell * H + h]);"),
+    ("fp8 combine uses the first block's scale",
+     "float v = oracle_e4m3_to_f32(q[cell * H + h]) * scale[cell * nb + h / 128];",
+     "float v = oracle_e4m3_to_f32(q[cell * H + h]) * scale[cell * nb];"),
     ("prefetch ignores mapping", "memcpy(redundant_weights + j * P, expert_weights + e * P,",
      "memcpy(redundant_weights + j * P, expert_weights + j % E * P,"),
 ]
@@ -109,6 +115,8 @@ def quick_pins():
     pinlib.check_ll_fp8(random_case(4, 40, 256, 16, 4, 4, 1, mask=0.2, slots=40))
     pinlib.check_ll_fp8(pinlib.fp8_edge_case())
     pinlib.check_tie_rounding()
+    pinlib.check_ll_combine_fp8(random_case(12, 40, 384, 16, 4, 4, 1, mask=0.2, dup=0.2, slots=40),
+                                rank_mask=np.array([0, 0, 1, 0], np.int32), seed=1)
 
 
 def build_mutant(orig: str, planted: str, workdir: str) -> str:

@@ -176,3 +176,12 @@ def test_layout_rank_mask_exhaustive_tiny():
 @pytest.mark.parametrize("seed", range(3))
 def test_combine_rank_mask(seed):
     pinlib.check_combine_rank_mask(seed)
+
+
+def test_ll_combine_fp8_reduces_to_bf16():
+    pinlib.check_ll_combine_fp8(config_inputs(3))
+
+
+def test_ll_combine_fp8_masked_random():
+    inp = random_case(12, 40, 384, 16, 4, 4, 1, mask=0.2, dup=0.2, slots=40)
+    pinlib.check_ll_combine_fp8(inp, rank_mask=np.array([0, 0, 1, 0], np.int32), seed=1)
