@@ -18,6 +18,16 @@ from gen import config_inputs, random_case
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
+# The two LL combines share their first lines; these tails tell them apart.
+_LL_BF16_TAIL = ("            float w = topk_weights[t * K + k];\n"
+                 "            int64_t cell = ((e % epr) * R + e / epr) * num_slots + s;\n"
+                 "            for (int64_t h = 0; h < H; ++h)\n"
+                 "                acc[h] = fmaf(w, bf16_to_f32")
+_LL_FP8_TAIL = ("            float w = topk_weights[t * K + k];\n"
+                "            int64_t cell = ((e % epr) * R + e / epr) * num_slots + s;\n"
+                "            for (int64_t h = 0; h < H; ++h) {\n"
+                "                float v = oracle_e4m3_to_f32")
+
 # (name, original text, planted text): each original must occur exactly once.
 MUTANTS = [
     ("bf16 ties away from zero", "u += 0x7fffu + lsb;", "u += 0x8000u;"),
@@ -64,11 +74,16 @@ MUTANTS = [
      "            if (0)\n                continue;"),
     ("combine weights ignore the rank mask", "if (p < 0 || rank_masked(rank_mask, r))",
      "if (p < 0)"),
-    ("LL combine-time mask ignored", "if (combine_mask != NULL && combine_mask[e / epr] != 0)",
-     "if (combine_mask != NULL && combine_mask[e / epr] != 0 && 0)"),
-    ("LL combine cell with rank and local expert swapped",
-     "int64_t cell = ((e % epr) * R + e / epr) * num_slots + s;",
-     "int64_t cell = ((e / epr) * epr + e % epr) * num_slots + s;"),
+    ("LL combine-time mask ignored",
+     "if (combine_mask != NULL && combine_mask[e / epr] != 0)\n                continue;\n" + _LL_BF16_TAIL,
+     "if (combine_mask != NULL && combine_mask[e / epr] != 0 && 0)\n                continue;\n"
+     + _LL_BF16_TAIL),
+    ("LL combine cell with rank and local expert swapped", _LL_BF16_TAIL,
+     _LL_BF16_TAIL.replace("((e % epr) * R + e / epr)", "((e / epr) * epr + e % epr)")),
+    ("fp8 combine-time mask ignored",
+     "if (combine_mask != NULL && combine_mask[e / epr] != 0)\n                continue;\n" + _LL_FP8_TAIL,
+     "if (combine_mask != NULL && combine_mask[e / epr] != 0 && 0)\n                continue;\n"
+     + _LL_FP8_TAIL),
     ("fp8 amax always from the first block",
      "for (int64_t h = b * 128; h < (b + 1) * 128; ++h) {\n                float v = fabsf",
      "for (int64_t h = 0; h < 128; ++h) {\n                float v = fabsf"),
