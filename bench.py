@@ -404,6 +404,13 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     byt = dc.T * dc.H * 2 + M * dc.H + M * (dc.H // 128) * 4 + dc.T * dc.K * 12 + M * 4
     rep["ll_dispatch_fp8"] = {"avg_us": round(us, 2), "bytes": byt,
                               "gbs": round(byt / (us * 1e-6) / 1e9, 1)}
+    # FP8 LL combine of that payload (codes and scales decoded in the sum)
+    us = timed(lambda: abi.check(L.ep_ll_combine_fp8(ctypes.byref(dd), S, P(q), P(sc), P(ltopk),
+                                                     P(lw), P(lslot), None, P(lout), s), "fp8c"),
+               args.steps)
+    byt = M * dc.H + M * (dc.H // 128) * 4 + dc.T * dc.H * 2 + dc.T * dc.K * 16
+    rep["ll_combine_fp8"] = {"avg_us": round(us, 2), "bytes": byt,
+                             "gbs": round(byt / (us * 1e-6) / 1e9, 1)}
 
     # load balancing: 32 replicas of the large workload's most popular experts
     big = config_inputs(4, with_x=False)

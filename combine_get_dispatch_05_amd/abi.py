@@ -28,7 +28,7 @@ EXPORTS = (
     "ep_ll_dispatch", "ep_ll_combine", "ep_handle_copy_layout", "ep_handle_num_recv",
     "ep_handle_dims", "ep_handle_nbytes", "ep_handle_free", "ep_pool_trim", "ep_status_str",
     "ep_last_hip_error", "ep_version", "ep_set_tuning", "ep_tuning_list", "ep_ll_dispatch_fp8",
-    "ep_mask_update", "ep_mask_clean", "ep_mask_query", "ep_lb_prefetch_weights",
+    "ep_ll_combine_fp8", "ep_mask_update", "ep_mask_clean", "ep_mask_query", "ep_lb_prefetch_weights",
     "ep_lb_reduce_grads",
 )
 
@@ -81,6 +81,7 @@ def _load():
         "ep_ll_dispatch": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "ep_ll_dispatch_fp8": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "ep_ll_combine": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "ep_ll_combine_fp8": (ctypes.c_int, [pdims, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "ep_mask_update": (ctypes.c_int, [vp, i32, i32, i32, vp]),
         "ep_mask_clean": (ctypes.c_int, [vp, i32, vp]),
         "ep_mask_query": (ctypes.c_int, [vp, i32, vp, vp]),

@@ -320,14 +320,35 @@ class Buffer:
                       "ep_ll_dispatch")
         return packed, count, LowLatencyHandle(src, slot, S, self.num_experts, H), None, None
 
-    def low_latency_combine(self, x: torch.Tensor, topk_idx: torch.Tensor,
-                            topk_weights: torch.Tensor, handle: LowLatencyHandle):
-        """x has packed_x's layout [E/R, R, slots, H].  Returns (combined_x
-        [T, H] bf16, None, None)."""
-        _need(x, torch.bfloat16, "x", 4)
+    def low_latency_combine(self, x, topk_idx: torch.Tensor, topk_weights: torch.Tensor,
+                            handle: LowLatencyHandle):
+        """x has packed_x's layout [E/R, R, slots, H] (bf16), or is the FP8 pair
+        (codes [E/R, R, slots, H] float8_e4m3fn or uint8, scales [E/R, R,
+        slots, H/128] fp32) that low_latency_dispatch(use_fp8=True) returns,
+        decoded with its scales in the sum.  Returns (combined_x [T, H] bf16,
+        None, None)."""
         _need(topk_idx, torch.int64, "topk_idx", 2)
         _need(topk_weights, torch.float32, "topk_weights", 2)
         T, K = topk_idx.shape
+        if isinstance(x, (tuple, list)):
+            q, sc = x
+            if q.dtype == torch.float8_e4m3fn:
+                q = q.view(torch.uint8)
+            _need(q, torch.uint8, "codes", 4)
+            _need(sc, torch.float32, "scales", 4)
+            H = q.shape[3]
+            if tuple(sc.shape) != tuple(q.shape[:3]) + (H // 128,):
+                raise ValueError("scales must be [E/R, R, slots, H/128]")
+            d = self._dims(T, H, K)
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=q.device)
+            abi.check(abi.lib().ep_ll_combine_fp8(ctypes.byref(d), handle.num_slots, abi.ptr(q),
+                                                  abi.ptr(sc), abi.ptr(topk_idx),
+                                                  abi.ptr(topk_weights), abi.ptr(handle.topk_slot),
+                                                  self._mask_ptr(), abi.ptr(out),
+                                                  abi.current_stream()),
+                      "ep_ll_combine_fp8")
+            return out, None, None
+        _need(x, torch.bfloat16, "x", 4)
         H = x.shape[3]
         d = self._dims(T, H, K)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)

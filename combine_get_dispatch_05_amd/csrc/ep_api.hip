@@ -557,6 +557,38 @@ int ep_ll_combine(const ep_dims *dims, int32_t num_slots, const void *packed_y,
     return e == hipSuccess ? EP_OK : hip_fail(e);
 }
 
+int ep_ll_combine_fp8(const ep_dims *dims, int32_t num_slots, const void *packed_q,
+                      const float *packed_scale, const int64_t *topk_idx,
+                      const float *topk_weights, const int32_t *topk_slot,
+                      const int32_t *rank_mask, void *out, ep_stream_t stream_)
+{
+    if (dims == nullptr)
+        return EP_ERR_INVALID;
+    ep_dims d = *dims;
+    d.num_channels = 1;
+    int rc = check_dims(&d);
+    if (rc != EP_OK)
+        return rc;
+    if (d.hidden % 128 != 0)
+        return EP_ERR_ALIGN;  // whole 128-element scale blocks
+    if (num_slots < 1 || num_slots > kMaxLLSlots)
+        return EP_ERR_INVALID;
+    if (d.num_tokens > num_slots)
+        return EP_ERR_CAPACITY;
+    if (d.num_tokens > 0 &&
+        (packed_q == nullptr || packed_scale == nullptr || topk_idx == nullptr ||
+         topk_weights == nullptr || topk_slot == nullptr || out == nullptr))
+        return EP_ERR_INVALID;
+    if (!aligned(packed_q, 8) || !aligned(packed_scale, 4) || !aligned(out, 16) ||
+        !aligned(topk_idx, 8) || !aligned(topk_weights, 4) || !aligned(topk_slot, 4) ||
+        !aligned(rank_mask, 4))
+        return EP_ERR_ALIGN;
+    hipError_t e = launch_ll_combine_fp8(d, num_slots, packed_q, packed_scale, topk_idx,
+                                         topk_weights, topk_slot, rank_mask, out,
+                                         static_cast<hipStream_t>(stream_));
+    return e == hipSuccess ? EP_OK : hip_fail(e);
+}
+
 int ep_mask_update(int32_t *rank_mask, int32_t num_ranks, int32_t rank, int32_t masked,
                    ep_stream_t stream)
 {
@@ -739,6 +771,6 @@ const char *ep_status_str(int status)
 
 const char *ep_last_hip_error(void) { return g_last_hip.c_str(); }
 
-int ep_version(void) { return (2 << 16) | 0; }
+int ep_version(void) { return (2 << 16) | 1; }
 
 }  // extern "C"

@@ -76,6 +76,11 @@ hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed
                              const int64_t *topk_idx, const float *topk_weights,
                              const int32_t *topk_slot, const int32_t *rank_mask, void *out,
                              hipStream_t stream);
+// packed_q: e4m3 codes [cells][H] bytes, packed_scale [cells][H/128].
+hipError_t launch_ll_combine_fp8(const ep_dims &d, int num_slots, const void *packed_q,
+                                 const float *packed_scale, const int64_t *topk_idx,
+                                 const float *topk_weights, const int32_t *topk_slot,
+                                 const int32_t *rank_mask, void *out, hipStream_t stream);
 
 hipError_t launch_mask_set(int32_t *mask, int num_ranks, int rank, int value, hipStream_t stream);
 

@@ -554,6 +554,78 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_kernel(
     }
 }
 
+// The combine of an FP8 payload (codes and per-128-element-block scales, as
+// the FP8 dispatch stores them).  A lane takes 8 elements of the row (one
+// 8-byte word of codes per cell); each code is decoded exactly with the
+// packed hardware conversion (checked against the e4m3 definition for all
+// 256 codes), multiplied by its block's scale in fp32, and added with the
+// same fma sum in ascending k as the bf16 combine.
+__global__ __launch_bounds__(kLLBlock) void ll_combine_fp8_kernel(
+    const uint2 *__restrict__ packed_q, const float *__restrict__ packed_scale, int V, int K,
+    int E, int R, int epr, int S, const int64_t *__restrict__ topk_idx,
+    const float *__restrict__ topk_weights, const int32_t *__restrict__ topk_slot,
+    const int32_t *__restrict__ rank_mask, u32x4 *__restrict__ out)
+{
+    __shared__ int64_t s_cell[kMaxTopk];
+    __shared__ float s_w[kMaxTopk];
+    const int tid = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    if (tid < K) {
+        const int64_t e = topk_idx[t * K + tid];
+        const int s = topk_slot[t * K + tid];
+        const bool ok = e >= 0 && e < E && s >= 0 && s < S &&
+                        !(rank_mask != nullptr && rank_mask[int(e) / epr] != 0);
+        s_cell[tid] = ok ? ((int64_t(int(e) % epr) * R + int(e) / epr) * S + s) : -1;
+        s_w[tid] = topk_weights[t * K + tid];
+    }
+    __syncthreads();
+
+    const int idx = blockIdx.y * kLLBlock + tid;  // 8-element group of the row
+    const int nb = V / 16;                          // 128-element blocks per row
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        acc[q] = 0.0f;
+
+    constexpr int kGroup = 8;
+    for (int k0 = 0; k0 < K; k0 += kGroup) {
+        uint2 c[kGroup];
+        float sc[kGroup];
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+            const int k = k0 + g;
+            const int64_t cell = k < K ? s_cell[k] : -1;
+            const bool live = cell >= 0 && idx < V;
+            c[g] = live ? packed_q[cell * V + idx] : make_uint2(0, 0);
+            sc[g] = live ? packed_scale[cell * nb + idx / 16] : 0.0f;
+        }
+#pragma unroll
+        for (int g = 0; g < kGroup; ++g) {
+            const int k = k0 + g;
+            if (k < K && s_cell[k] >= 0) {
+                const float w = s_w[k];
+                const uint32_t words[2] = {c[g].x, c[g].y};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(int(words[h]), false);
+                    const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(int(words[h]), true);
+                    acc[4 * h + 0] = __builtin_fmaf(w, d01[0] * sc[g], acc[4 * h + 0]);
+                    acc[4 * h + 1] = __builtin_fmaf(w, d01[1] * sc[g], acc[4 * h + 1]);
+                    acc[4 * h + 2] = __builtin_fmaf(w, d23[0] * sc[g], acc[4 * h + 2]);
+                    acc[4 * h + 3] = __builtin_fmaf(w, d23[1] * sc[g], acc[4 * h + 3]);
+                }
+            }
+        }
+    }
+    if (idx < V) {
+        u32x4 rv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            rv[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        out[t * V + idx] = rv;
+    }
+}
+
 std::atomic<int> g_ll_mode{0};  // 0 automatic, 1 expert-major, 2 token-major when it fits
 
 }  // namespace
@@ -603,6 +675,23 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
                        R, E / R, num_slots, topk_idx, rank_mask, static_cast<u32x4 *>(packed_x),
                        static_cast<uint2 *>(packed_q), packed_scale, packed_count, src_info,
                        topk_slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_ll_combine_fp8(const ep_dims &d, int num_slots, const void *packed_q,
+                                 const float *packed_scale, const int64_t *topk_idx,
+                                 const float *topk_weights, const int32_t *topk_slot,
+                                 const int32_t *rank_mask, void *out, hipStream_t stream)
+{
+    if (d.num_tokens == 0)
+        return hipSuccess;
+    const int E = d.num_experts, R = d.num_ranks;
+    const int V = d.hidden / 8;
+    const int chunks = (V + kLLBlock - 1) / kLLBlock;
+    hipLaunchKernelGGL(ll_combine_fp8_kernel, dim3(d.num_tokens, chunks), dim3(kLLBlock), 0,
+                       stream, static_cast<const uint2 *>(packed_q), packed_scale, V, d.num_topk,
+                       E, R, E / R, num_slots, topk_idx, topk_weights, topk_slot, rank_mask,
+                       static_cast<u32x4 *>(out));
     return hipGetLastError();
 }
 

@@ -252,6 +252,24 @@ int ep_ll_combine(const ep_dims *dims, int32_t num_slots, const void *packed_y,
                   const int32_t *topk_slot, const int32_t *rank_mask, void *out,
                   ep_stream_t stream);
 
+/*
+ * ep_ll_combine with an FP8 payload, the layout ep_ll_dispatch_fp8 writes
+ * ([P1] "IB-GDA Kernels", FP8 with use_fp8; reading: the scales are applied
+ * in the combine).  For every element of a cell:
+ *   v = e4m3_decode(code) * scale[block]      (exact decode, one fp32 multiply)
+ * then exactly the weighted sum of ep_ll_combine:
+ *   out[t] = bf16_rne(acc),  acc = fma(topk_weights[t][k], v(cell(t, k)), acc)
+ * over k ascending, valid non-dropped slots, from acc = +0.
+ *   packed_q     [epr][R][num_slots][H] e4m3 codes (bytes), 8-byte aligned
+ *   packed_scale [epr][R][num_slots][H/128] fp32
+ * hidden must be a multiple of 128 (EP_ERR_ALIGN).  A NaN code gives NaN
+ * terms.  rank_mask as for ep_ll_combine.  No host sync.
+ */
+int ep_ll_combine_fp8(const ep_dims *dims, int32_t num_slots, const void *packed_q,
+                      const float *packed_scale, const int64_t *topk_idx,
+                      const float *topk_weights, const int32_t *topk_slot,
+                      const int32_t *rank_mask, void *out, ep_stream_t stream);
+
 /* [P1] "Dynamic Rank Masking" on a caller-owned device mask rank_mask[R]
  * (0 active, 1 masked), stream-ordered like the other calls:
  *   ep_mask_update  set rank `rank` to masked (nonzero) or active (0)
@@ -336,7 +354,7 @@ const char *ep_status_str(int status);
 const char *ep_last_hip_error(void);
 
 /* ABI version: (major << 16) | minor.  2.0: rank_mask arguments of
- * ep_get_dispatch_layout, ep_dispatch and ep_combine. */
+ * ep_get_dispatch_layout, ep_dispatch and ep_combine; 2.1: ep_ll_combine_fp8. */
 int ep_version(void);
 
 #ifdef __cplusplus

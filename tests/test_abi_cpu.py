@@ -60,7 +60,7 @@ def test_product_package_never_touches_the_oracle():
 
 
 def test_version_and_status_text():
-    assert abi.version() == (2, 0)
+    assert abi.version() == (2, 1)
     for code in range(7):
         assert L.ep_status_str(code)
     assert L.ep_status_str(99) == b"unknown status"

@@ -275,3 +275,48 @@ def test_lb_ops_many_replicas():
     egd = dev_bf16(ew)
     buf.lb_reduce_grads(dev_bf16(rg), egd, mp)
     assert_bf16_close(host_bits(egd), oracle.lb_reduce_grads(rg, ew, mapping), what="many replicas")
+
+
+# ------------------------------------------------------------ FP8 LL combine
+
+
+@pytest.mark.parametrize("case", ["decode", "random_codes", "masked", "nonfinite"])
+def test_ll_combine_fp8(case, ll_mode):
+    """The FP8 payload decoded with its scales inside the LL combine, against
+    the oracle: the FP8 dispatch's own output, and random codes with
+    power-of-two scales; a rank masked at combine time; non-finite blocks
+    (NaN outputs compared as NaN)."""
+    if case == "decode":
+        inp, m = config_inputs(3), None
+    elif case == "random_codes":
+        inp, m = random_case(13, 40, 384, 16, 4, 4, 1, mask=0.1, dup=0.2, slots=40), None
+    elif case == "masked":
+        inp = random_case(14, 40, 512, 16, 4, 4, 1, mask=0.1, slots=40)
+        m = np.array([0, 1, 0, 0], np.int32)
+    else:
+        inp, m = pinlib.fp8_nonfinite_case(), None
+    E, R, S = inp.E, inp.R, inp.slots
+    buf = epm.Buffer(R, E)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+    (q, sc), _, hdl, _, _ = buf.low_latency_dispatch(x, topk, S, E, use_fp8=True)
+    if case == "random_codes":
+        rng = np.random.default_rng(5)
+        qh = rng.integers(0, 256, tuple(q.shape)).astype(np.uint8)
+        qh[(qh & 0x7F) == 0x7F] = 0x21
+        sh = np.ldexp(np.ones(tuple(sc.shape)), rng.integers(-4, 5, tuple(sc.shape))).astype(np.float32)
+        q = torch.from_numpy(qh).cuda().view(torch.float8_e4m3fn)
+        sc = torch.from_numpy(sh).cuda()
+    else:
+        qh = q.view(torch.uint8).cpu().numpy()
+        sh = sc.cpu().numpy()
+    if m is not None:
+        buf.low_latency_update_mask_buffer(int(np.nonzero(m)[0][0]), mask=True)
+    out, _, _ = buf.low_latency_combine((q, sc), topk, w, hdl)
+    # the oracle combines the same codes and scales (unused cells never read)
+    exp = oracle.ll_combine_fp8(qh, sh, inp.topk_idx, inp.topk_weights, E, R, combine_mask=m)
+    got = host_bits(out)
+    nan_e = (exp & 0x7FFF) > 0x7F80
+    np.testing.assert_array_equal((got & 0x7FFF) > 0x7F80, nan_e)
+    assert_bf16_close(np.where(nan_e, 0, got), np.where(nan_e, 0, exp), what=f"fp8 combine {case}")
+    if case != "nonfinite":
+        assert not nan_e.any()
