@@ -10,6 +10,7 @@
 // caller asks for it or when a buffer is smaller than the worst case).
 
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -181,10 +182,23 @@ struct ep_handle {
     LayoutBufs bufs;
     std::atomic<int64_t> num_recv{-1};  // N on the host once read back
     std::atomic<bool> dispatched{false};
+    bool hashed = false;  // topk_hash[0] holds the hash of the layout's table
     std::atomic<hipStream_t> last_stream{nullptr};
 };
 
 namespace {
+
+// EP_CHECK=1: keep a hash of each layout's top-k table and compare it when a
+// layout handle comes back with a table (read at every call).
+bool check_enabled()
+{
+    const char *v = std::getenv("EP_CHECK");
+    return v != nullptr && v[0] == '1';
+}
+
+// Does topk_idx hash to what the handle's layout was made from?  Reads both
+// hashes back (synchronizes the stream): a debug check only.
+int same_table(ep_handle *h, const int64_t *topk_idx, hipStream_t stream, bool *same);
 
 int create_handle(const ep_dims &d, const int64_t *topk_idx, const int32_t *rank_mask,
                   hipStream_t stream, ep_handle **out)
@@ -208,12 +222,32 @@ int create_handle(const ep_dims &d, const int64_t *topk_idx, const int32_t *rank
     }
     h->bufs = layout_bufs_at(h->arena.ptr, off);
     e = launch_layout(h->shape, topk_idx, rank_mask, h->bufs, stream);
+    if (e == hipSuccess && check_enabled() && topk_idx != nullptr) {
+        e = launch_topk_hash(topk_idx, int64_t(d.num_tokens) * d.num_topk, h->bufs.topk_hash,
+                             stream);
+        h->hashed = e == hipSuccess;
+    }
     h->last_stream = stream;
     if (e != hipSuccess) {
         ep_handle_free(h);
         return hip_fail(e);
     }
     *out = h;
+    return EP_OK;
+}
+
+int same_table(ep_handle *h, const int64_t *topk_idx, hipStream_t stream, bool *same)
+{
+    const int64_t n = int64_t(h->dims.num_tokens) * h->dims.num_topk;
+    hipError_t e = launch_topk_hash(topk_idx, n, h->bufs.topk_hash + 1, stream);
+    uint64_t v[2] = {0, 0};
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(v, h->bufs.topk_hash, sizeof v, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    *same = v[0] == v[1];
     return EP_OK;
 }
 
@@ -382,6 +416,16 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
             // layout is known, so new routing is refused.
             if (h->dispatched.load() && (topk_idx != nullptr || topk_weights != nullptr))
                 return EP_ERR_INVALID;
+            // A layout handle with its table: under EP_CHECK=1 the table must
+            // be the one the layout came from.
+            if (topk_idx != nullptr && h->hashed && check_enabled()) {
+                bool same = false;
+                rc = same_table(h, topk_idx, static_cast<hipStream_t>(stream_), &same);
+                if (rc != EP_OK)
+                    return rc;
+                if (!same)
+                    return EP_ERR_INVALID;
+            }
         }
         if (fresh) {
             rc = create_handle(*dims, topk_idx, rank_mask, stream, &h);

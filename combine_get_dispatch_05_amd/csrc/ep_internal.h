@@ -24,7 +24,7 @@ constexpr int64_t kMaxTokens = int64_t(1) << 24;
 constexpr int kMaxHidden = 1 << 20;
 
 // Device pointers of one layout (all inside a handle's arena).
-constexpr int kArenaFields = 15;
+constexpr int kArenaFields = 16;
 struct LayoutBufs {
     int32_t *num_tokens_per_rank;        // [R]
     int32_t *num_tokens_per_expert;      // [E]
@@ -41,6 +41,7 @@ struct LayoutBufs {
     int32_t *blk_count;                  // [nB][R] block totals (exclusive bases after a scan kernel)
     int32_t *blk_ecount;                 // [nB][E] per-block expert counts (512-token blocks)
     int64_t *num_recv;                   // [1] N
+    uint64_t *topk_hash;                 // [2] hash of the layout's topk_idx, and of a later one
 };
 
 struct LayoutShape {
@@ -81,6 +82,9 @@ hipError_t launch_ll_combine_fp8(const ep_dims &d, int num_slots, const void *pa
                                  const float *packed_scale, const int64_t *topk_idx,
                                  const float *topk_weights, const int32_t *topk_slot,
                                  const int32_t *rank_mask, void *out, hipStream_t stream);
+
+// Order-independent 64-bit hash of n top-k ids into *out (debug check).
+hipError_t launch_topk_hash(const int64_t *topk_idx, int64_t n, uint64_t *out, hipStream_t stream);
 
 hipError_t launch_mask_set(int32_t *mask, int num_ranks, int rank, int value, hipStream_t stream);
 

@@ -607,6 +607,7 @@ size_t layout_arena_bytes(const LayoutShape &s, size_t off[kArenaFields])
     const size_t sizes[kArenaFields] = {
         R * 4,      E * 4,      T * R,      R * 4,      R * C * 4,  R * C * 4,  T * R * 4,
         T * km * 4, T * km * 4, T * km * 4, nW * R * 8, nW * R * 4, nB * R * 4, nB * E * 4, 8,
+        16,
     };
     size_t cur = 0;
     for (int i = 0; i < kArenaFields; ++i) {
@@ -635,6 +636,7 @@ LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields])
     b.blk_count = reinterpret_cast<int32_t *>(p + off[12]);
     b.blk_ecount = reinterpret_cast<int32_t *>(p + off[13]);
     b.num_recv = reinterpret_cast<int64_t *>(p + off[14]);
+    b.topk_hash = reinterpret_cast<uint64_t *>(p + off[15]);
     return b;
 }
 

@@ -163,6 +163,12 @@ int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, const i
  *   is needed to check it.
  * num_recv (HOST pointer, nullable): receives N; asking for it synchronizes
  *   the stream once per handle (later calls use the cached value).
+ * Debug check ([P4] "Performance Contract and Constraints": a layout is only
+ *   valid for the table it came from): with EP_CHECK=1 in the environment,
+ *   ep_get_dispatch_layout stores a 64-bit hash of topk_idx in the handle,
+ *   and a dispatch given that handle together with a topk_idx hashes it and
+ *   reads both hashes back (one stream synchronization); a different table
+ *   returns EP_ERR_INVALID before anything is packed.
  * rank_mask [R] int32 (nullable): as for ep_get_dispatch_layout; used only
  *   by a fresh dispatch (the layout it computes).  A handle already holds
  *   its layout, so a non-NULL rank_mask with *handle != NULL returns

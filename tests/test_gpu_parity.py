@@ -231,6 +231,28 @@ def test_layout_handle_accepts_its_topk_once():
         buf.dispatch(x, topk, w, handle=h)
 
 
+def test_ep_check_refuses_another_table(monkeypatch):
+    """EP_CHECK=1: a layout handle passed to a dispatch with a different
+    top-k table (two slots of one token swapped) is refused before anything
+    is packed; with its own table the dispatch goes through."""
+    monkeypatch.setenv("EP_CHECK", "1")
+    inp = config_inputs(0)
+    buf = epm.Buffer(inp.R, inp.E, inp.C)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+    _, _, _, h = buf.get_dispatch_layout(topk, keep_handle=True)
+    other = inp.topk_idx.copy()
+    other[5, [0, 1]] = other[5, [1, 0]]
+    with pytest.raises(abi.EpError) as ei:
+        buf.dispatch(x, dev(other), w, handle=h)
+    assert ei.value.code == abi.EP_ERR_INVALID
+    rx, rti, _, _, _, _ = buf.dispatch(x, topk, w, handle=h)
+    ora = oracle.layout(inp.topk_idx, inp.E, inp.R, inp.C)
+    o_rx, o_rti, _ = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, inp.E, inp.R, ora)
+    np.testing.assert_array_equal(host_bits(rx), o_rx)
+    np.testing.assert_array_equal(host(rti), o_rti)
+    h.free()
+
+
 def test_layout_capacity_out():
     inp = config_inputs(0)
     d = abi.dims(inp.T, 8, inp.K, inp.E, inp.R, inp.C)
