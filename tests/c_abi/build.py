@@ -21,12 +21,14 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 def build() -> str:
     pkg = os.path.join(ROOT, "combine_get_dispatch_05_amd")
-    cmd = ["gcc", "-std=c11", "-O1", "-Wall", "-Wextra", "-Werror", "-o", BIN, SRC,
+    tmp = BIN + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-std=c11", "-O1", "-Wall", "-Wextra", "-Werror", "-o", tmp, SRC,
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROCM, "include"),
            "-L", pkg, "-lep", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
            "-Wl,-rpath,$ORIGIN/../../combine_get_dispatch_05_amd",
            "-Wl,-rpath," + os.path.join(ROCM, "lib")]
     subprocess.check_call(cmd)
+    os.replace(tmp, BIN)  # a reader never sees a half-written binary
     return BIN
 
 
