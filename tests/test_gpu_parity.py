@@ -253,6 +253,34 @@ def test_ep_check_refuses_another_table(monkeypatch):
     h.free()
 
 
+def test_two_streams_at_once():
+    """Two independent layout -> dispatch -> combine pipelines on two streams,
+    enqueued interleaved so that they run concurrently; handles are freed and
+    new ones made on each stream again (the pool hands an arena back only to
+    the stream that freed it).  Both results against the oracle."""
+    cases = [random_case(61, 700, 264, 48, 6, 12, 5, mask=0.1, dup=0.1),
+             random_case(62, 900, 136, 64, 4, 16, 3, mask=0.05)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    bufs = [epm.Buffer(c.R, c.E, c.C) for c in cases]
+    for _round in range(2):
+        outs = []
+        for c, st, b in zip(cases, streams, bufs):
+            with torch.cuda.stream(st):
+                x, topk, w = dev_bf16(c.x), dev(c.topk_idx), dev(c.topk_weights)
+                rx, _, rtw, _, h, _ = b.dispatch(x, topk, w)
+                out, cw, _ = b.combine(rx, h, rtw)
+                outs.append((rx, out, cw, h))
+        torch.cuda.synchronize()
+        for c, (rx, out, cw, h) in zip(cases, outs):
+            ora = oracle.layout(c.topk_idx, c.E, c.R, c.C)
+            o_rx, _, o_rtw = oracle.dispatch(c.x, c.topk_idx, c.topk_weights, c.E, c.R, ora)
+            np.testing.assert_array_equal(host_bits(rx), o_rx)
+            o_out, o_cw = oracle.combine(o_rx, ora, o_rtw)
+            assert_bf16_close(host_bits(out), o_out, what="two streams")
+            np.testing.assert_array_equal(f32_bits(host(cw)), f32_bits(o_cw))
+            h.free()
+
+
 def test_layout_capacity_out():
     inp = config_inputs(0)
     d = abi.dims(inp.T, 8, inp.K, inp.E, inp.R, inp.C)
