@@ -177,6 +177,35 @@ def test_ll_random(case, ll_mode):
     run_ll(random_case(3 + T, T, H, E, K, R, 1, mask=mask, dup=dup, slots=S), seed=T)
 
 
+def _sweep_cases(n=40, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        R = int(rng.choice([1, 2, 3, 5, 8, 13, 64, 65, 130, 200]))
+        epr = int(rng.integers(1, 5))
+        E = R * epr
+        K = int(rng.integers(1, min(16, E) + 1))
+        T = int(rng.integers(0, 700))
+        H = 8 * int(rng.integers(1, 40))
+        C = int(rng.integers(1, 20))
+        mask = float(rng.choice([0.0, 0.1, 0.5]))
+        dup = float(rng.choice([0.0, 0.2]))
+        out.append((i, T, H, E, K, R, C, mask, dup))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "s%d_T%d_H%d_E%d_K%d_R%d_C%d" % c[:7])
+def test_random_sweep(case):
+    """Seeded random shapes (odd row lengths, R up to 200, masks, repeated
+    experts): the normal path end to end, and the low-latency path when the
+    batch fits its slots, against the oracle."""
+    i, T, H, E, K, R, C, mask, dup = case
+    inp = random_case(1000 + i, T, H, E, K, R, C, mask=mask, dup=dup, slots=max(T, 1))
+    run_normal_path(inp, seed=i)
+    if T <= 4096:
+        run_ll(inp, seed=i)
+
+
 # ----------------------------------------------------------- boundary / errors
 
 
