@@ -282,6 +282,10 @@ hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const
     if (c.P > 0 && c.P < blocks)
         blocks = c.P;
     const bool bias = bias0 != nullptr || bias1 != nullptr;
+    if (log_enabled())
+        log_launch("combine T=%d H=%d K=%d R=%d: G=%d VPT=%d S=%d U=%d NTL=%d blocks=%d%s%s", s.T,
+                   hidden, s.K, s.R, c.G, c.VPT, c.S, c.U, c.NTL, blocks, bias ? " +bias" : "",
+                   rank_mask != nullptr ? " +mask" : "");
     hipLaunchKernelGGL(bias ? c.fn_bias : c.fn, dim3(blocks), dim3(kCombineBlock), 0, stream,
                        static_cast<const u32x4 *>(y), s.T, V, s.K, s.kmax, c.S, b.dst_row,
                        b.dst_rank, rank_mask, recv_topk_weights, static_cast<const u32x4 *>(bias0),

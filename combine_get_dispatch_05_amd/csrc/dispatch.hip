@@ -226,6 +226,10 @@ hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, cons
     int blocks = int((groups + per_block - 1) / per_block);
     if (c.P > 0 && c.P < blocks)
         blocks = c.P;
+    if (log_enabled())
+        log_launch("dispatch_pack T=%d H=%d K=%d R=%d: G=%d VPT=%d S=%d NTS=%d NTL=%d blocks=%d%s",
+                   s.T, hidden, s.K, s.R, c.G, c.VPT, c.S, c.NTS, c.NTL, blocks,
+                   topk ? " +topk" : "");
     hipLaunchKernelGGL(topk ? c.topk : c.plain, dim3(blocks), dim3(kPackBlock), 0, stream,
                        static_cast<const u32x4 *>(x), s.T, V, s.K, s.E, s.epr, s.kmax, c.S,
                        b.dst_row,

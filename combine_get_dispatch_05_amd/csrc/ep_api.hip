@@ -10,6 +10,9 @@
 // caller asks for it or when a buffer is smaller than the worst case).
 
 #include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <dlfcn.h>
 #include <cstdlib>
 #include <cstring>
 #include <map>
@@ -21,9 +24,75 @@
 
 using namespace ep;
 
+namespace ep {
+
+bool log_enabled()
+{
+    const char *v = std::getenv("EP_LOG");
+    return v != nullptr && v[0] == '1';
+}
+
+void log_launch(const char *fmt, ...)
+{
+    char line[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(line, sizeof line, fmt, ap);
+    va_end(ap);
+    std::fprintf(stderr, "[ep] %s\n", line);
+}
+
+}  // namespace ep
+
 namespace {
 
 thread_local std::string g_last_hip;
+
+// EP_TRACE=1: a roctx range around every entry point, so rocprofv3's marker
+// trace shows the calls over their kernels.  The roctx library is opened on
+// first use only when the variable is set; without it nothing changes.
+typedef int (*RangePushFn)(const char *);
+typedef int (*RangePopFn)();
+
+struct Roctx {
+    RangePushFn push = nullptr;
+    RangePopFn pop = nullptr;
+};
+
+const Roctx &roctx()
+{
+    static const Roctx r = [] {
+        Roctx x;
+        const char *v = std::getenv("EP_TRACE");
+        if (v == nullptr || v[0] != '1')
+            return x;
+        void *h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+        if (h == nullptr)
+            h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+        if (h == nullptr)
+            return x;
+        x.push = reinterpret_cast<RangePushFn>(dlsym(h, "roctxRangePushA"));
+        x.pop = reinterpret_cast<RangePopFn>(dlsym(h, "roctxRangePop"));
+        if (x.push == nullptr || x.pop == nullptr)
+            x.push = nullptr, x.pop = nullptr;
+        return x;
+    }();
+    return r;
+}
+
+struct TraceRange {
+    bool on;
+    explicit TraceRange(const char *name) : on(roctx().push != nullptr)
+    {
+        if (on)
+            roctx().push(name);
+    }
+    ~TraceRange()
+    {
+        if (on)
+            roctx().pop();
+    }
+};
 
 int hip_fail(hipError_t e)
 {
@@ -346,6 +415,7 @@ int64_t ep_max_recv_rows(const ep_dims *dims)
 int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, const int32_t *rank_mask,
                            ep_layout_out *out, ep_handle **handle_out, ep_stream_t stream_)
 {
+    TraceRange trace_range("ep_get_dispatch_layout");
     try {
         int rc = check_dims(dims);
         if (rc != EP_OK)
@@ -380,6 +450,7 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
                 void *recv_x, int64_t *recv_topk_idx, float *recv_topk_weights, int64_t recv_cap,
                 int64_t *num_recv, ep_stream_t stream_)
 {
+    TraceRange trace_range("ep_dispatch");
     try {
         int rc = check_dims(dims);
         if (rc != EP_OK)
@@ -464,6 +535,7 @@ int ep_combine(ep_handle *h, int32_t hidden, const void *y, int64_t y_rows,
                const int32_t *rank_mask, void *out, float *combined_topk_weights,
                ep_stream_t stream_)
 {
+    TraceRange trace_range("ep_combine");
     try {
         if (h == nullptr)
             return EP_ERR_HANDLE;
@@ -559,6 +631,7 @@ int ep_ll_dispatch(const ep_dims *dims, int32_t num_slots, const void *x,
                    int32_t *packed_count, int32_t *src_info, int32_t *topk_slot,
                    ep_stream_t stream)
 {
+    TraceRange trace_range("ep_ll_dispatch");
     return ll_dispatch_common(dims, num_slots, x, topk_idx, rank_mask, packed_x, nullptr, nullptr,
                               packed_count, src_info, topk_slot, stream);
 }
@@ -568,6 +641,7 @@ int ep_ll_dispatch_fp8(const ep_dims *dims, int32_t num_slots, const void *x,
                        float *packed_scale, int32_t *packed_count, int32_t *src_info,
                        int32_t *topk_slot, ep_stream_t stream)
 {
+    TraceRange trace_range("ep_ll_dispatch_fp8");
     if (packed_q == nullptr || packed_scale == nullptr)
         return EP_ERR_INVALID;
     return ll_dispatch_common(dims, num_slots, x, topk_idx, rank_mask, nullptr, packed_q,
@@ -579,6 +653,7 @@ int ep_ll_combine(const ep_dims *dims, int32_t num_slots, const void *packed_y,
                   const int32_t *topk_slot, const int32_t *rank_mask, void *out,
                   ep_stream_t stream_)
 {
+    TraceRange trace_range("ep_ll_combine");
     if (dims == nullptr)
         return EP_ERR_INVALID;
     ep_dims d = *dims;
@@ -606,6 +681,7 @@ int ep_ll_combine_fp8(const ep_dims *dims, int32_t num_slots, const void *packed
                       const float *topk_weights, const int32_t *topk_slot,
                       const int32_t *rank_mask, void *out, ep_stream_t stream_)
 {
+    TraceRange trace_range("ep_ll_combine_fp8");
     if (dims == nullptr)
         return EP_ERR_INVALID;
     ep_dims d = *dims;
@@ -675,6 +751,7 @@ int ep_lb_reduce_grads(const void *redundant_grads, void *expert_grads, const in
                        int32_t num_replicas, int32_t num_experts, int64_t elems_per_expert,
                        ep_stream_t stream)
 {
+    TraceRange trace_range("ep_lb_reduce_grads");
     int rc = check_lb(redundant_grads, expert_grads, mapping, num_replicas, num_experts,
                       elems_per_expert);
     if (rc != EP_OK)
@@ -689,6 +766,7 @@ int ep_lb_prefetch_weights(const void *expert_weights, void *redundant_weights,
                            const int64_t *mapping, int32_t num_replicas, int32_t num_experts,
                            int64_t elems_per_expert, ep_stream_t stream)
 {
+    TraceRange trace_range("ep_lb_prefetch_weights");
     int rc = check_lb(expert_weights, redundant_weights, mapping, num_replicas, num_experts,
                       elems_per_expert);
     if (rc != EP_OK)

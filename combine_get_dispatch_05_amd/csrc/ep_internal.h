@@ -53,6 +53,11 @@ LayoutShape layout_shape(const ep_dims &d);
 size_t layout_arena_bytes(const LayoutShape &s, size_t off[kArenaFields]);
 LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields]);
 
+// EP_LOG=1 in the environment: one line per kernel launch on stderr with its
+// launch geometry (read at every call).
+bool log_enabled();
+void log_launch(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+
 // rank_mask [R] int32 (nullable): nonzero ranks are masked.
 hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const int32_t *rank_mask,
                          const LayoutBufs &b, hipStream_t stream);

@@ -643,6 +643,10 @@ LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields])
 hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const int32_t *rank_mask,
                          const LayoutBufs &b, hipStream_t stream)
 {
+    if (log_enabled())
+        log_launch("layout T=%d K=%d E=%d R=%d C=%d: count blocks=%d pos blocks=%d%s%s", s.T, s.K,
+                   s.E, s.R, s.C, s.nB, s.nW, s.nB > kSelfScanBlocks ? " +scan" : "",
+                   rank_mask != nullptr ? " +mask" : "");
     switch ((s.R + kWave - 1) / kWave) {
     case 1: return launch_layout_nw<1>(s, topk_idx, rank_mask, b, stream);
     case 2: return launch_layout_nw<2>(s, topk_idx, rank_mask, b, stream);

@@ -654,6 +654,10 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
         if (rows)
             ny = fp8 ? (V / 16 + 15) / 16 : (V + kLLBlock - 1) / kLLBlock;
         const int64_t blocks = int64_t(d.num_tokens) * ny + (E + kLLWaves - 1) / kLLWaves;
+        if (log_enabled())
+            log_launch("ll_dispatch token-major T=%d H=%d K=%d E=%d: slices=%d blocks=%lld%s",
+                       d.num_tokens, d.hidden, d.num_topk, E, ny, (long long)blocks,
+                       fp8 ? " fp8" : "");
         auto tk = fp8 ? ll_dispatch_tok_kernel<true> : ll_dispatch_tok_kernel<false>;
         hipLaunchKernelGGL(tk, dim3(unsigned(blocks)), dim3(kLLBlock), 0, stream,
                            static_cast<const u32x4 *>(x), d.num_tokens, V, d.num_topk, E, R,
@@ -670,6 +674,9 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
     const int64_t per = fp8 ? 64 : 2048;
     int ny = int((work + per - 1) / per);
     ny = ny < 1 ? 1 : (ny > 8 ? 8 : ny);
+    if (log_enabled())
+        log_launch("ll_dispatch expert-major T=%d H=%d K=%d E=%d: grid=%dx%d%s", d.num_tokens,
+                   d.hidden, d.num_topk, E, E, ny, fp8 ? " fp8" : "");
     hipLaunchKernelGGL(kernel, dim3(E, ny), dim3(kLLBlock), 0, stream,
                        static_cast<const u32x4 *>(x), d.num_tokens, d.hidden / 8, d.num_topk, E,
                        R, E / R, num_slots, topk_idx, rank_mask, static_cast<u32x4 *>(packed_x),
@@ -688,6 +695,9 @@ hipError_t launch_ll_combine_fp8(const ep_dims &d, int num_slots, const void *pa
     const int E = d.num_experts, R = d.num_ranks;
     const int V = d.hidden / 8;
     const int chunks = (V + kLLBlock - 1) / kLLBlock;
+    if (log_enabled())
+        log_launch("ll_combine fp8 T=%d H=%d K=%d: grid=%dx%d", d.num_tokens, d.hidden,
+                   d.num_topk, d.num_tokens, chunks);
     hipLaunchKernelGGL(ll_combine_fp8_kernel, dim3(d.num_tokens, chunks), dim3(kLLBlock), 0,
                        stream, static_cast<const uint2 *>(packed_q), packed_scale, V, d.num_topk,
                        E, R, E / R, num_slots, topk_idx, topk_weights, topk_slot, rank_mask,
@@ -706,6 +716,9 @@ hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed
     const int V = d.hidden / 8;
     constexpr int VPT = 1;
     const int chunks = (V + kLLBlock * VPT - 1) / (kLLBlock * VPT);
+    if (log_enabled())
+        log_launch("ll_combine T=%d H=%d K=%d: grid=%dx%d", d.num_tokens, d.hidden, d.num_topk,
+                   d.num_tokens, chunks);
     hipLaunchKernelGGL((ll_combine_kernel<VPT>), dim3(d.num_tokens, chunks), dim3(kLLBlock), 0,
                        stream, static_cast<const u32x4 *>(packed_y), V, d.num_topk, E, R, E / R,
                        num_slots, topk_idx, topk_weights, topk_slot, rank_mask,

@@ -39,6 +39,11 @@
  *   - Errors: every int-returning call returns an ep_status.  On any error no
  *     work has been enqueued and no output pointer argument was written,
  *     except as noted.  Host-side errors never throw across the ABI.
+ *   - Environment (read by the library, never required):
+ *       EP_LOG=1     one line per kernel launch on stderr with its launch geometry;
+ *       EP_TRACE=1   a roctx range around every entry point (rocprofv3 marker trace);
+ *       EP_CHECK=1   the handle-reuse table check of ep_dispatch;
+ *       EP_TUNE_DISPATCH / EP_TUNE_COMBINE   initial launch-shape overrides (ep_set_tuning).
  *   - Concurrency: calls may run on different streams concurrently as long
  *     as they do not write the same caller memory.  One handle may be read by
  *     several calls at once; it must not be freed while they are in flight

@@ -12,6 +12,7 @@ experts inside a token, masked slots, empty inputs).
 from __future__ import annotations
 
 import ctypes
+import os
 import sys
 
 import numpy as np
@@ -308,6 +309,52 @@ def test_two_streams_at_once():
             assert_bf16_close(host_bits(out), o_out, what="two streams")
             np.testing.assert_array_equal(f32_bits(host(cw)), f32_bits(o_cw))
             h.free()
+
+
+def test_ep_log_lines(monkeypatch, capfd):
+    """EP_LOG=1: one stderr line per launch with its geometry; silent without."""
+    monkeypatch.setenv("EP_LOG", "1")
+    inp = config_inputs(0)
+    buf = epm.Buffer(inp.R, inp.E, inp.C)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+    rx, _, rtw, _, h, _ = buf.dispatch(x, topk, w)
+    buf.combine(rx, h, rtw)
+    torch.cuda.synchronize()
+    err = capfd.readouterr().err
+    for tag in ("[ep] layout T=128", "[ep] dispatch_pack T=128", "[ep] combine T=128"):
+        assert tag in err, err
+    h.free()
+    monkeypatch.delenv("EP_LOG")
+    _, _, _, _, h2, _ = buf.dispatch(x, topk, w)
+    torch.cuda.synchronize()
+    assert "[ep]" not in capfd.readouterr().err
+    h2.free()
+
+
+def test_ep_trace_ranges_in_a_fresh_process():
+    """EP_TRACE=1 (read once per process, so in a child process): the roctx
+    ranges around the calls change no result."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = "\n".join([
+        "import sys",
+        f"sys.path[:0] = [{root!r}, {os.path.join(root, 'tests')!r}]",
+        "import numpy as np, torch",
+        "import combine_get_dispatch_05_amd as epm, oracle",
+        "from gen import config_inputs",
+        "from gpu_util import dev, dev_bf16, host_bits",
+        "inp = config_inputs(0)",
+        "buf = epm.Buffer(inp.R, inp.E, inp.C)",
+        "rx, _, rtw, _, h, _ = buf.dispatch(dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights))",
+        "ora = oracle.layout(inp.topk_idx, inp.E, inp.R, inp.C)",
+        "o_rx, _, _ = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, inp.E, inp.R, ora)",
+        "assert (host_bits(rx) == o_rx).all()",
+        "print('trace ok')",
+    ])
+    r = subprocess.run([sys.executable, "-c", code], env={**os.environ, "EP_TRACE": "1"},
+                       capture_output=True, text=True, timeout=150)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "trace ok" in r.stdout
 
 
 def test_layout_capacity_out():
