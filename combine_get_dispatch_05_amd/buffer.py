@@ -36,6 +36,19 @@ def _need(t: torch.Tensor, dtype, name: str, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _shape(t: torch.Tensor, shape, name: str):
+    # The C ABI takes bare pointers, so every extent the kernels will index
+    # is checked here, before a launch could read or write past a tensor.
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(map(str, devs))}")
+
+
 @dataclass
 class Layout:
     """Device copies of a dispatch layout ("What the Handle Contains")."""
@@ -212,10 +225,16 @@ class Buffer:
             if topk_idx.shape[0] != T:
                 raise ValueError("topk_idx and x disagree on the number of tokens")
         if topk_weights is not None:
+            if topk_idx is None:
+                raise ValueError("topk_weights needs topk_idx")
             _need(topk_weights, torch.float32, "topk_weights", 2)
+            _shape(topk_weights, topk_idx.shape, "topk_weights")
+        _same_device(x, topk_idx, topk_weights)
         K = topk_idx.shape[1] if topk_idx is not None else handle.dims.num_topk
         d = self._dims(T, H, K)
         dev = x.device
+        if handle is not None and handle.device != dev:
+            raise ValueError("handle was made on another device")
         raw = ctypes.c_void_p(handle.raw.value if handle is not None else None)
         if handle is not None and handle.dims.num_tokens != T:
             raise ValueError("handle was made for another number of tokens")
@@ -257,9 +276,12 @@ class Buffer:
         two), added before the single rounding.  Ranks masked in the mask
         buffer now are left out of the sums."""
         _need(x, torch.bfloat16, "x", 2)
+        d = handle.dims
         if topk_weights is not None:
             _need(topk_weights, torch.float32, "topk_weights", 2)
-        d = handle.dims
+            _shape(topk_weights, (x.shape[0], d.num_topk), "topk_weights")
+        if handle.device != x.device:
+            raise ValueError("handle was made on another device")
         T, H = d.num_tokens, x.shape[1]
         biases = [] if bias is None else ([bias] if isinstance(bias, torch.Tensor) else list(bias))
         if len(biases) > 2:
@@ -268,6 +290,7 @@ class Buffer:
             _need(b, torch.bfloat16, "bias", 2)
             if tuple(b.shape) != (T, H):
                 raise ValueError("bias must be [num_tokens, hidden]")
+        _same_device(x, topk_weights, *biases)
         b0 = biases[0] if len(biases) > 0 else None
         b1 = biases[1] if len(biases) > 1 else None
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
@@ -296,6 +319,9 @@ class Buffer:
         _need(topk_idx, torch.int64, "topk_idx", 2)
         T, H = x.shape
         K = topk_idx.shape[1]
+        if topk_idx.shape[0] != T:
+            raise ValueError("topk_idx and x disagree on the number of tokens")
+        _same_device(x, topk_idx)
         S = int(num_max_dispatch_tokens_per_rank)
         d = self._dims(T, H, K)
         dev = x.device
@@ -330,6 +356,11 @@ class Buffer:
         _need(topk_idx, torch.int64, "topk_idx", 2)
         _need(topk_weights, torch.float32, "topk_weights", 2)
         T, K = topk_idx.shape
+        _shape(topk_weights, (T, K), "topk_weights")
+        _shape(handle.topk_slot, (T, K), "the handle's topk_slot")
+        if handle.num_experts != self.num_experts:
+            raise ValueError("handle was made for another number of experts")
+        cells = (self.num_local_experts, self.num_ranks, handle.num_slots)
         if isinstance(x, (tuple, list)):
             q, sc = x
             if q.dtype == torch.float8_e4m3fn:
@@ -337,8 +368,10 @@ class Buffer:
             _need(q, torch.uint8, "codes", 4)
             _need(sc, torch.float32, "scales", 4)
             H = q.shape[3]
+            _shape(q, cells + (H,), "codes")
             if tuple(sc.shape) != tuple(q.shape[:3]) + (H // 128,):
                 raise ValueError("scales must be [E/R, R, slots, H/128]")
+            _same_device(q, sc, topk_idx, topk_weights, handle.topk_slot)
             d = self._dims(T, H, K)
             out = torch.empty((T, H), dtype=torch.bfloat16, device=q.device)
             abi.check(abi.lib().ep_ll_combine_fp8(ctypes.byref(d), handle.num_slots, abi.ptr(q),
@@ -350,6 +383,8 @@ class Buffer:
             return out, None, None
         _need(x, torch.bfloat16, "x", 4)
         H = x.shape[3]
+        _shape(x, cells + (H,), "x")
+        _same_device(x, topk_idx, topk_weights, handle.topk_slot)
         d = self._dims(T, H, K)
         out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
         abi.check(abi.lib().ep_ll_combine(ctypes.byref(d), handle.num_slots, abi.ptr(x),
@@ -361,12 +396,20 @@ class Buffer:
 
     # ------------------------------------------------------ load balancing
     @staticmethod
-    def _lb_args(a: torch.Tensor, b: torch.Tensor, mapping: torch.Tensor):
-        for t, n in ((a, "weights"), (b, "weights")):
+    def _lb_args(redundant: torch.Tensor, expert: torch.Tensor, mapping: torch.Tensor):
+        """Rows per replica / expert; one replica row per mapping entry, and
+        replica rows the size of expert rows."""
+        for t, n in ((redundant, "redundant tensor"), (expert, "expert tensor")):
             _need(t, torch.bfloat16, n, t.dim())
+            if t.dim() < 1:
+                raise ValueError(f"{n} needs a leading [rows] dimension")
         _need(mapping, torch.int64, "redundancy_mapping", 1)
-        P = a[0].numel() if a.shape[0] > 0 else (b[0].numel() if b.shape[0] > 0 else 0)
-        return P
+        _same_device(redundant, expert, mapping)
+        if redundant.shape[0] != mapping.numel():
+            raise ValueError("the redundant tensor needs one row per redundancy_mapping entry")
+        if tuple(redundant.shape[1:]) != tuple(expert.shape[1:]):
+            raise ValueError("replica rows and expert rows must have the same shape")
+        return int(torch.Size(expert.shape[1:]).numel())
 
     def lb_prefetch_weights(self, redundant_expert_weights: torch.Tensor,
                             expert_weights: torch.Tensor, redundancy_mapping: torch.Tensor,
