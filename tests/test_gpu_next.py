@@ -182,10 +182,15 @@ def test_combine_bias(cfg):
 # ------------------------------------------------------------------- FP8 LL
 
 
-@pytest.mark.parametrize("case", ["decode", "edge", "nonfinite", "masked"])
+@pytest.mark.parametrize("case", ["decode", "edge", "nonfinite", "masked", "max_slots",
+                                  "long_row"])
 def test_ll_dispatch_fp8(case, ll_mode):
     if case == "decode":
         inp, m = config_inputs(3), None
+    elif case == "max_slots":  # the largest slot count the library accepts
+        inp, m = random_case(6, 4096, 128, 8, 1, 4, 1, slots=4096), None
+    elif case == "long_row":  # the longest row (H = 2^20: 8192 scale blocks)
+        inp, m = random_case(9, 3, 1 << 20, 8, 2, 4, 1, slots=3), None
     elif case == "edge":
         inp, m = pinlib.fp8_edge_case(), None
     elif case == "nonfinite":

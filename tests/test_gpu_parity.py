@@ -114,6 +114,8 @@ RANDOM_CASES = [
     (65537, 16, 130, 3, 65, 33, 0.05, 0.0),
     # the largest expert count, top-k and rank count the library accepts
     (100, 64, 8192, 64, 512, 4096, 0.05, 0.05),
+    # the longest row the library accepts (H = 2^20, 2 MiB per row)
+    (5, 1 << 20, 8, 2, 4, 2, 0.0, 0.0),
 ]
 
 
@@ -169,6 +171,8 @@ LL_CASES = [
     (600, 256, 64, 8, 16, 640, 0.05, 0.1),    # T*K = 4800: expert-major in every mode
     (64, 128, 8192, 64, 512, 64, 0.05, 0.05),  # the largest expert count, top-k, ranks
     (32, 64, 8, 8, 4, 32, 0.0, 0.9),     # repeated experts overflow the slots: 39 pairs dropped
+    (4096, 64, 8, 1, 4, 4096, 0.0, 0.0),  # the largest slot count the library accepts
+    (4, 1 << 20, 8, 2, 4, 4, 0.0, 0.0),   # the longest row (H = 2^20)
 ]
 
 
