@@ -380,9 +380,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
 // pack and reduce kernels read.
 template <int NW, bool kSelfScan>
 __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
-    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
-    int E, int R, int C, int epr, int epr_shift, int kmax,
-    int nB, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
+    int T, int E, int R, int C, int kmax, int nB, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
     const int32_t *__restrict__ blk_count, const int32_t *__restrict__ blk_ecount,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
     int32_t *__restrict__ recv_src_idx, int32_t *__restrict__ dst_row,
@@ -396,7 +394,6 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     __shared__ int32_t s_off[NW * kWave];  // position of this tile's first hit inside segment r
     __shared__ int32_t s_tot[NW * kWave];
     __shared__ int32_t s_wsum[kPosBlock / kWave];
-    __shared__ uint64_t s_live[NW];
     __shared__ uint64_t s_tokm[NW][kWave];  // live-rank bitmask of each token of the tile
     const int tid = threadIdx.x;
     const int wg = blockIdx.x;
@@ -404,41 +401,38 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     const int64_t t0 = int64_t(wg) * kWave;
     const int ntok = int(T - t0 < kWave ? T - t0 : kWave);
 
-    uint64_t m[NW];
-    if (tid < ntok) {
-        int64_t ids0[kIdChunk];
-        token_rank_mask<NW>(topk_idx + (t0 + tid) * K, K, E, epr, epr_shift, m, ids0);
-    }
-    build_live<NW>(rank_mask, R, s_live);
-    for (int r = tid; r < R; r += kPosBlock) {
-        s_mask[r] = wave_mask[size_t(wg) * R + r];
-        int before = 0, tot = 0;
-        if (kSelfScan) {
-            for (int b0 = 0; b0 < nB; b0 += kBatch) {
-                int c[kBatch];
+    // Per-rank state of the tile.  The count kernel stored, for each rank, the
+    // mask of the tile's tokens that hit it (ranks masked at the time already
+    // cleared).  The loop runs over whole 64-rank words, so each wave also
+    // transposes the words it loaded: that gives every token its mask of
+    // ranks, without reading the top-k ids again.
+    for (int r = tid; r < NW * kWave; r += kPosBlock) {
+        uint64_t bm = 0;
+        if (r < R) {
+            bm = wave_mask[size_t(wg) * R + r];
+            s_mask[r] = bm;
+            int before = 0, tot = 0;
+            if (kSelfScan) {
+                for (int b0 = 0; b0 < nB; b0 += kBatch) {
+                    int c[kBatch];
 #pragma unroll
-                for (int i = 0; i < kBatch; ++i)
-                    c[i] = b0 + i < nB ? blk_count[size_t(b0 + i) * R + r] : 0;
+                    for (int i = 0; i < kBatch; ++i)
+                        c[i] = b0 + i < nB ? blk_count[size_t(b0 + i) * R + r] : 0;
 #pragma unroll
-                for (int i = 0; i < kBatch; ++i) {
-                    before += b0 + i < blk ? c[i] : 0;
-                    tot += c[i];
+                    for (int i = 0; i < kBatch; ++i) {
+                        before += b0 + i < blk ? c[i] : 0;
+                        tot += c[i];
+                    }
                 }
+                s_tot[r] = tot;
+            } else {
+                before = blk_count[size_t(blk) * R + r];
             }
-            s_tot[r] = tot;
-        } else {
-            before = blk_count[size_t(blk) * R + r];
+            s_off[r] = before + wave_base[size_t(wg) * R + r];
         }
-        s_off[r] = before + wave_base[size_t(wg) * R + r];
+        s_tokm[r >> 6][r & (kWave - 1)] = wave_transpose64(bm);
     }
     __syncthreads();
-    if (tid < kWave) {
-        if (tid < ntok)
-            keep_live<NW>(s_live, m);
-#pragma unroll
-        for (int w = 0; w < NW; ++w)
-            s_tokm[w][tid] = tid < ntok ? m[w] : 0;
-    }
     if (kSelfScan) {
         const int N = rank_exclusive_scan(s_tot, s_seg, R, s_wsum);
         __syncthreads();
@@ -573,9 +567,8 @@ hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
                            b.recv_channel_prefix_matrix, b.num_recv);
     auto pos_kernel = self_scan ? layout_pos_kernel<NW, true> : layout_pos_kernel<NW, false>;
     if (s.T > 0)
-        hipLaunchKernelGGL(pos_kernel, dim3(s.nW), dim3(kPosBlock), 0, stream, topk_idx, rank_mask,
-                           s.T, s.K, s.E, s.R,
-                           s.C, s.epr, epr_shift, s.kmax, s.nB, b.wave_mask, b.wave_base, b.blk_count,
+        hipLaunchKernelGGL(pos_kernel, dim3(s.nW), dim3(kPosBlock), 0, stream, s.T, s.E, s.R,
+                           s.C, s.kmax, s.nB, b.wave_mask, b.wave_base, b.blk_count,
                            b.blk_ecount, b.is_token_in_rank, b.send_head, b.recv_src_idx,
                            b.dst_row, b.dst_rank, b.num_tokens_per_rank, b.num_tokens_per_expert,
                            b.rank_prefix_matrix, b.channel_prefix_matrix,
