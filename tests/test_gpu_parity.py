@@ -37,13 +37,14 @@ def _announce(request):
     torch.cuda.synchronize()
 
 
-def run_normal_path(inp, seed=0):
-    """Fresh dispatch, handle-reuse dispatch and combine against the oracle."""
+def run_normal_path(inp, seed=0, gpu_topk=None):
+    """Fresh dispatch, handle-reuse dispatch and combine against the oracle.
+    gpu_topk: another table for the library (the oracle keeps inp.topk_idx)."""
     E, R, C = inp.E, inp.R, inp.C
     ora = oracle.layout(inp.topk_idx, E, R, C)
     buf = epm.Buffer(R, E, C)
     x = dev_bf16(inp.x)
-    topk = dev(inp.topk_idx)
+    topk = dev(inp.topk_idx if gpu_topk is None else gpu_topk)
     w = dev(inp.topk_weights)
 
     # layout alone
@@ -125,13 +126,13 @@ def test_normal_path_random(case):
     run_normal_path(random_case(7 + T, T, H, E, K, R, C, mask=mask, dup=dup), seed=T)
 
 
-def run_ll(inp, seed=0):
+def run_ll(inp, seed=0, gpu_topk=None):
     E, R, S = inp.E, inp.R, inp.slots
     T, K = inp.topk_idx.shape
     o_buf, o_cnt, o_src, o_slot = oracle.ll_dispatch(inp.x, inp.topk_idx, E, R, S)
     buf = epm.Buffer(R, E)
     x = dev_bf16(inp.x)
-    topk = dev(inp.topk_idx)
+    topk = dev(inp.topk_idx if gpu_topk is None else gpu_topk)
     packed, count, hdl, ev, hook = buf.low_latency_dispatch(x, topk, S, E)
     assert ev is None and hook is None
     np.testing.assert_array_equal(host(count), o_cnt)
@@ -209,6 +210,23 @@ def test_random_sweep(case):
     run_normal_path(inp, seed=i)
     if T <= 4096:
         run_ll(inp, seed=i)
+
+
+def test_out_of_range_ids_act_as_masked(ll_mode):
+    """Expert ids outside [-1, E) are invalid input, which the library ignores
+    (as masked slots) so that no access leaves its buffer.  Both paths on a
+    table salted with such ids (E, E + 1, 2^40, -2, -2^40) equal the oracle on
+    the same table with those slots set to -1."""
+    inp = random_case(77, 300, 136, 32, 6, 8, 5, mask=0.1, dup=0.2, slots=300)
+    rng = np.random.default_rng(77)
+    bad = rng.random(inp.topk_idx.shape) < 0.15
+    junk = rng.choice(np.array([inp.E, inp.E + 1, 1 << 40, -2, -(1 << 40)], np.int64),
+                      size=inp.topk_idx.shape)
+    dirty = np.ascontiguousarray(np.where(bad, junk, inp.topk_idx))
+    inp.topk_idx = np.ascontiguousarray(np.where(bad, np.int64(-1), inp.topk_idx))
+    assert bad.sum() > 100
+    run_normal_path(inp, seed=77, gpu_topk=dirty)
+    run_ll(inp, seed=77, gpu_topk=dirty)
 
 
 # ----------------------------------------------------------- boundary / errors
