@@ -1,0 +1,130 @@
+"""A small mixture-of-experts layer through the library, end to end.
+
+"DeepEP Buffer Class API for Expert Parallel Communication" shows the calls in
+their setting: dispatch the tokens to the ranks that hold their experts, run
+each expert on the rows it received, and combine the results back into token
+order.  Here every expert is a linear map W[e] of the hidden vector.  Each
+received row is multiplied by the weighted sum of its local experts' maps, and
+the result is combined.  That must equal the dense definition
+out[t] = sum over valid slots k of w[t, k] * W[e(t, k)] x[t].  Both passes
+are checked, the fresh dispatch and the handle-reuse dispatch of a second
+batch with the same routing ("How DeepEP Optimizes Handle Reuse for Repeated
+Dispatches")."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gen import random_case, random_rows
+from gpu_util import dev, dev_bf16, host
+
+pytestmark = pytest.mark.gpu
+
+import combine_get_dispatch_05_amd as epm  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu-test] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bf16_values(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _experts(recv_x, rti, rtw, seg_start, epr, W):
+    """Every received row times the weighted sum of its local experts' maps,
+    in fp32 on the device, rounded once to bf16 (the expert output)."""
+    N = recv_x.shape[0]
+    rank = torch.searchsorted(seg_start, torch.arange(N, device=recv_x.device, dtype=torch.int32),
+                              right=True) - 1
+    y = torch.zeros(recv_x.shape, dtype=torch.float32, device=recv_x.device)
+    xf = recv_x.float()
+    for k in range(rti.shape[1]):
+        ok = rti[:, k] >= 0
+        if not bool(ok.any()):
+            continue
+        e = rank[ok].long() * epr + rti[ok, k]
+        prod = torch.bmm(W[e].contiguous(), xf[ok].unsqueeze(-1)).squeeze(-1)
+        y[ok] += rtw[ok, k].unsqueeze(-1) * prod
+    return y.to(torch.bfloat16)
+
+
+def _dense_reference(x_bits, topk_idx, w, W64, R, epr):
+    """In fp64: out[t]; per token the sum over ranks of |that rank's share|;
+    and sum_k |w| |W_e| |x|, which bounds the fp32 product errors."""
+    x = _bf16_values(x_bits)
+    T, K = topk_idx.shape
+    share = np.zeros((T, R, x.shape[1]))
+    amag = np.zeros(x.shape)
+    for t in range(T):
+        for k in range(K):
+            e = int(topk_idx[t, k])
+            if e < 0:
+                continue
+            share[t, e // epr] += float(w[t, k]) * (W64[e] @ x[t])
+            amag[t] += abs(float(w[t, k])) * (np.abs(W64[e]) @ np.abs(x[t]))
+    return share.sum(axis=1), np.abs(share).sum(axis=1), amag
+
+
+def _check(out_bf16, ref, mag, amag, H, R):
+    # Error sources, each bounded (unit roundoff: 2^-24 for fp32, 2^-8 for
+    # bf16, whose significand has 8 bits): the fp32 expert products (W rounded
+    # to fp32, H products and adds: recursive summation,
+    # (H + 8) * 2^-24 * sum |w||W||x|); the expert output rounded to bf16 once
+    # per (token, rank) row (2^-8 of its size); the fp32 sum over at most R
+    # rows ((R + 1) * 2^-24 of the summed sizes); and the final rounding to
+    # bf16 (2^-8 of the total).
+    got = _bf16_values(host(out_bf16.contiguous().view(torch.int16)).view(np.uint16))
+    tol = ((H + 8) * 2.0 ** -24 * amag * (1 + 2.0 ** -7) + 2.0 ** -8 * mag * (1 + 2.0 ** -7)
+           + (R + 1) * 2.0 ** -24 * mag * 1.01 + 2.0 ** -8 * np.abs(ref) * 1.02 + 2.0 ** -40)
+    err = np.abs(got - ref)
+    assert (err <= tol).all(), f"max excess {float((err - tol).max()):.3g}"
+
+
+@pytest.mark.parametrize("shape", [(256, 128, 16, 4, 4, 3), (600, 256, 64, 6, 16, 5)],
+                         ids=["T256_E16_R4", "T600_E64_R16"])
+def test_moe_layer_matches_dense_definition(shape):
+    T, H, E, K, R, C = shape
+    # the error bound below assumes full fp32 products
+    torch.backends.cuda.matmul.allow_tf32 = False
+    inp = random_case(41 + T, T, H, E, K, R, C, mask=0.1, dup=0.0)
+    epr = E // R
+    g = torch.Generator().manual_seed(T)
+    W = (torch.randn(E, H, H, generator=g, dtype=torch.float64) / np.sqrt(H))
+    W64 = W.numpy()
+    Wd = W.float().cuda()
+    buf = epm.Buffer(R, E, C)
+    x = dev_bf16(inp.x)
+    topk = dev(inp.topk_idx)
+    w = dev(inp.topk_weights)
+
+    recv_x, rti, rtw, counts, h, _ = buf.dispatch(x, topk, w)
+    lay = h.layout()
+    seg_start = torch.cat([torch.zeros(1, dtype=torch.int32, device="cuda"),
+                           lay.rank_prefix_matrix[:-1]])
+    assert int(counts.sum()) == int((inp.topk_idx >= 0).sum())
+    y = _experts(recv_x, rti, rtw, seg_start, epr, Wd)
+    out, cw, _ = buf.combine(y, h, rtw)
+    ref, mag, amag = _dense_reference(inp.x, inp.topk_idx, inp.topk_weights, W64, R, epr)
+    _check(out, ref, mag, amag, H, R)
+    # the reduced weights are the token's valid weights, summed per rank and
+    # then over ranks: for distinct experts, each weight lands once
+    valid = inp.topk_idx >= 0
+    np.testing.assert_allclose(host(cw), np.where(valid, inp.topk_weights, 0.0), rtol=0, atol=0)
+
+    # a second batch with the same routing, through the cached handle
+    x2 = random_rows(T, H, T, tag=21)
+    recv_x2, _, _, _, _, _ = buf.dispatch(dev_bf16(x2), handle=h)
+    y2 = _experts(recv_x2, rti, rtw, seg_start, epr, Wd)
+    out2, _, _ = buf.combine(y2, h)
+    ref2, mag2, amag2 = _dense_reference(x2, inp.topk_idx, inp.topk_weights, W64, R, epr)
+    _check(out2, ref2, mag2, amag2, H, R)
+    h.free()
