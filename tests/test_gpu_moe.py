@@ -128,3 +128,44 @@ def test_moe_layer_matches_dense_definition(shape):
     ref2, mag2, amag2 = _dense_reference(x2, inp.topk_idx, inp.topk_weights, W64, R, epr)
     _check(out2, ref2, mag2, amag2, H, R)
     h.free()
+
+
+@pytest.mark.parametrize("ll_shape", [(64, 256, 32, 4, 8, 64), (100, 128, 64, 6, 16, 128)],
+                         ids=["T64_E32_R8", "T100_E64_R16"])
+def test_low_latency_moe_layer_matches_dense_definition(ll_shape, ll_mode):
+    """The decode path: low-latency dispatch into per-expert slots, each
+    expert's linear map on its slots, and the low-latency combine, which
+    weights and sums the slots of every token.  Same dense definition."""
+    T, H, E, K, R, S = ll_shape
+    torch.backends.cuda.matmul.allow_tf32 = False
+    inp = random_case(43 + T, T, H, E, K, R, 1, mask=0.1, dup=0.0, slots=S)
+    epr = E // R
+    g = torch.Generator().manual_seed(1000 + T)
+    W = (torch.randn(E, H, H, generator=g, dtype=torch.float64) / np.sqrt(H))
+    W64 = W.numpy()
+    buf = epm.Buffer(R, E)
+    topk = dev(inp.topk_idx)
+    packed, count, hdl, _, _ = buf.low_latency_dispatch(dev_bf16(inp.x), topk, S, E)
+    assert int(count.sum()) == int((inp.topk_idx >= 0).sum())
+    # cell (le, r) holds the rows for expert r * epr + le
+    e_of_cell = (torch.arange(R).view(1, R) * epr + torch.arange(epr).view(epr, 1)).reshape(-1)
+    Wt = W.float()[e_of_cell].transpose(1, 2).contiguous().cuda()
+    y = torch.bmm(packed.view(epr * R, S, H).float(), Wt).to(torch.bfloat16).view(packed.shape)
+    out, _, _ = buf.low_latency_combine(y.contiguous(), topk, dev(inp.topk_weights), hdl)
+
+    x = _bf16_values(inp.x)
+    ref = np.zeros(x.shape)
+    mag = np.zeros(x.shape)
+    amag = np.zeros(x.shape)
+    for t in range(T):
+        for k in range(K):
+            e = int(inp.topk_idx[t, k])
+            if e < 0:
+                continue
+            wk = float(inp.topk_weights[t, k])
+            v = W64[e] @ x[t]
+            ref[t] += wk * v
+            mag[t] += abs(wk) * np.abs(v)
+            amag[t] += abs(wk) * (np.abs(W64[e]) @ np.abs(x[t]))
+    # mag here already carries the weights, and the sum runs over K slots
+    _check(out, ref, mag, amag, H, K)
