@@ -333,6 +333,56 @@ def test_two_streams_at_once():
             h.free()
 
 
+def test_host_threads_at_once():
+    """Four host threads, each with its own stream and inputs, call layout ->
+    dispatch -> combine -> free three times over.  ctypes drops the
+    interpreter lock during the calls, so the library's handle pool and error
+    state are used from several threads at once.  Every result matches the
+    oracle (computed beforehand on the main thread)."""
+    import threading
+    cases = [random_case(70 + i, 300 + 97 * i, 136 + 64 * i, 32, 4 + i, 8, 3 + i, mask=0.1,
+                         dup=0.1) for i in range(4)]
+    expect = []
+    for c in cases:
+        ora = oracle.layout(c.topk_idx, c.E, c.R, c.C)
+        o_rx, _, o_rtw = oracle.dispatch(c.x, c.topk_idx, c.topk_weights, c.E, c.R, ora)
+        o_out, o_cw = oracle.combine(o_rx, ora, o_rtw)
+        expect.append((o_rx, o_out, o_cw))
+    results = [None] * len(cases)
+
+    def work(i):
+        try:
+            c = cases[i]
+            st = torch.cuda.Stream()
+            got = []
+            with torch.cuda.stream(st):
+                b = epm.Buffer(c.R, c.E, c.C)
+                x, topk, w = dev_bf16(c.x), dev(c.topk_idx), dev(c.topk_weights)
+                for _ in range(3):
+                    rx, _, rtw, _, h, _ = b.dispatch(x, topk, w)
+                    out, cw, _ = b.combine(rx, h, rtw)
+                    h.free()
+                    st.synchronize()
+                    got.append((host_bits(rx), host_bits(out), f32_bits(host(cw))))
+            results[i] = got
+        except Exception as exc:  # reported on the main thread
+            results[i] = exc
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=100)
+        assert not t.is_alive(), "a worker thread did not finish"
+    for i, got in enumerate(results):
+        assert not isinstance(got, Exception), f"thread {i}: {got!r}"
+        o_rx, o_out, o_cw = expect[i]
+        for rx, out, cw in got:
+            np.testing.assert_array_equal(rx, o_rx)
+            assert_bf16_close(out, o_out, what=f"thread {i}")
+            np.testing.assert_array_equal(cw, f32_bits(o_cw))
+
+
 def test_ep_log_lines(monkeypatch, capfd):
     """EP_LOG=1: one stderr line per launch with its geometry; silent without."""
     monkeypatch.setenv("EP_LOG", "1")
