@@ -867,6 +867,41 @@ def check_tie_rounding():
     np.testing.assert_array_equal(got, np.array([[1.0, -3.03125]], np.float32))
 
 
+def check_sum_order():
+    """Every sum's order is fixed by a reading: the combine adds ranks in
+    ascending order, the LL combine slots k in ascending order, and
+    lb_reduce_grads the expert's own gradient and then its replicas in
+    ascending order.  fp32 sums depend on that order when small terms land on
+    ties.  With the terms 1, 2^-8, 2^-24, 2^-24 in that order, each 2^-24 is
+    exactly half an fp32 ulp of 1 + 2^-8 and is dropped (ties to even).  That
+    leaves 1 + 2^-8, a bf16 tie that rounds to 1.0.  In the opposite order the
+    two 2^-24 first make 2^-23, the total 1 + 2^-8 + 2^-23 is exact and above
+    the tie, and it rounds to 1 + 2^-7.  Each case checks both orders of the
+    input, so the pin also shows that the order matters."""
+    terms = np.array([1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24], np.float32)
+    fwd, rev = np.float32(1.0), np.float32(1.0 + 2.0 ** -7)
+    # normal combine: one token on experts 0..3, one expert per rank (R = 4);
+    # the packed row of rank r holds terms[r]
+    L = O.layout(np.array([[0, 1, 2, 3]], np.int64), 4, 4, 1)
+    for t, want in ((terms, fwd), (terms[::-1], rev)):
+        rows = np.repeat(np.ascontiguousarray(t)[:, None], 8, axis=1)
+        out, _ = O.combine(bits_from_f32_exact(rows), L)
+        assert (f32_from_bits(out) == want).all(), "combine rank order"
+    # LL combine: one token, experts 0..3 on one rank, one slot each, unit weights
+    idx = np.array([[0, 1, 2, 3]], np.int64)
+    w = np.ones((1, 4), np.float32)
+    for t, want in ((terms, fwd), (terms[::-1], rev)):
+        b = np.repeat(np.ascontiguousarray(t)[:, None], 8, axis=1).reshape(4, 1, 1, 8)
+        out = f32_from_bits(O.ll_combine(bits_from_f32_exact(b), idx, w, 4, 1))
+        assert (out == want).all(), "LL combine slot order"
+    # lb_reduce_grads: own gradient 0, then four replicas of expert 0
+    for t, want in ((terms, fwd), (terms[::-1], rev)):
+        rg = bits_from_f32_exact(np.repeat(np.ascontiguousarray(t)[:, None], 8, axis=1))
+        eg = bits_from_f32_exact(np.zeros((1, 8), np.float32))
+        got = f32_from_bits(O.lb_reduce_grads(rg, eg, np.zeros(4, np.int64)))
+        assert (got == want).all(), "lb_reduce_grads replica order"
+
+
 def fp8_edge_case(seed=4):
     """A decode batch whose rows hold an all-zero block and a block of values
     far below the amax floor, next to ordinary blocks."""

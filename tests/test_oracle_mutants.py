@@ -28,6 +28,15 @@ _LL_FP8_TAIL = ("            float w = topk_weights[t * K + k];\n"
                 "            for (int64_t h = 0; h < H; ++h) {\n"
                 "                float v = oracle_e4m3_to_f32")
 
+# The head of the bf16 LL combine's slot loop (shared with the FP8 one).
+_LL_BF16_HEAD = ("        for (int64_t k = 0; k < K; ++k) {\n"
+                 "            int64_t e = topk_idx[t * K + k];\n"
+                 "            int64_t s = slot[t * K + k];\n"
+                 "            if (e < 0 || s < 0 || s >= num_slots)\n"
+                 "                continue;\n"
+                 "            if (combine_mask != NULL && combine_mask[e / epr] != 0)\n"
+                 "                continue;\n")
+
 # (name, original text, planted text): each original must occur exactly once.
 MUTANTS = [
     ("bf16 ties away from zero", "u += 0x7fffu + lsb;", "u += 0x8000u;"),
@@ -101,6 +110,29 @@ MUTANTS = [
      "float v = oracle_e4m3_to_f32(q[cell * H + h]) * scale[cell * nb];"),
     ("prefetch ignores mapping", "memcpy(redundant_weights + j * P, expert_weights + e * P,",
      "memcpy(redundant_weights + j * P, expert_weights + j % E * P,"),
+    ("recv_src_idx without the segment base",
+     "recv_src_idx[base + send_head[t * R + r]] = (int32_t)t;",
+     "recv_src_idx[send_head[t * R + r]] = (int32_t)t;"),
+    ("exclusive rank prefix", "        acc += num_tokens_per_rank[r];\n        rank_prefix_matrix[r] = acc;",
+     "        rank_prefix_matrix[r] = acc;\n        acc += num_tokens_per_rank[r];"),
+    ("membership counted per slot", "is_token_in_rank[t * R + e / epr] = 1;",
+     "is_token_in_rank[t * R + e / epr] += 1;"),
+    ("combine sums ranks in descending order",
+     "        for (int64_t r = 0; r < R; ++r) {\n            int32_t p = send_head[t * R + r];\n"
+     "            if (rank_masked(rank_mask, r))",
+     "        for (int64_t r = R - 1; r >= 0; --r) {\n            int32_t p = send_head[t * R + r];\n"
+     "            if (rank_masked(rank_mask, r))"),
+    ("LL combine sums slots in descending order", _LL_BF16_HEAD + _LL_BF16_TAIL,
+     _LL_BF16_HEAD.replace("for (int64_t k = 0; k < K; ++k)", "for (int64_t k = K - 1; k >= 0; --k)")
+     + _LL_BF16_TAIL),
+    ("reduce grads sums replicas in descending order",
+     "        for (int64_t j = 0; j < n_rep; ++j)\n            if (mapping[j] == e)\n",
+     "        for (int64_t j = n_rep - 1; j >= 0; --j)\n            if (mapping[j] == e)\n"),
+    ("LL src_info holds the slot", "            src_info[cell] = (int32_t)t;",
+     "            src_info[cell] = (int32_t)s;"),
+    ("LL counts capped at capacity", "        counts[(e % epr) * R + e / epr] = cnt[e];",
+     "        counts[(e % epr) * R + e / epr] = cnt[e] < num_slots ? cnt[e] : (int32_t)num_slots;"),
+    ("e4m3 sign dropped", "    uint8_t sign = signbit(f) ? 0x80 : 0;", "    uint8_t sign = 0;"),
 ]
 
 
@@ -130,6 +162,7 @@ def quick_pins():
     pinlib.check_ll_fp8(random_case(4, 40, 256, 16, 4, 4, 1, mask=0.2, slots=40))
     pinlib.check_ll_fp8(pinlib.fp8_edge_case())
     pinlib.check_tie_rounding()
+    pinlib.check_sum_order()
     pinlib.check_ll_combine_fp8(random_case(12, 40, 384, 16, 4, 4, 1, mask=0.2, dup=0.2, slots=40),
                                 rank_mask=np.array([0, 0, 1, 0], np.int32), seed=1)
 

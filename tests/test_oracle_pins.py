@@ -136,6 +136,10 @@ def test_tie_rounding():
     pinlib.check_tie_rounding()
 
 
+def test_sum_order():
+    pinlib.check_sum_order()
+
+
 def test_ll_fp8_zero_and_tiny_blocks():
     pinlib.check_ll_fp8(pinlib.fp8_edge_case())
 
