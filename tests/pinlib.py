@@ -902,6 +902,42 @@ def check_sum_order():
         assert (got == want).all(), "lb_reduce_grads replica order"
 
 
+def check_fma_and_bias_order():
+    """Two more fixed roundings.  The LL combines add each weighted term with
+    one fused multiply-add: with slot 0 holding -(1 + 2^-7) at weight 1 and
+    slot 1 holding 1 + 2^-7 at weight 1 + 2^-17, the exact product of slot 1
+    is 1 + 2^-7 + 2^-17 + 2^-24, so the fused sum is 2^-17 + 2^-24 (exact in
+    bf16).  A separate product would first round the 2^-24 away (an fp32 tie)
+    and give 2^-17.  The FP8 combine gets the same terms from the codes of
+    -1 and 1 with the block scale 1 + 2^-7, whose product is exact in fp32.
+    The normal combine adds the bias terms after the rank sum: rank rows 1 and
+    2^-8 then two biases of 2^-24 give 1 + 2^-8 (each bias lost at a tie), so
+    bf16 1.0.  Biases added first would make 2^-23 and give 1 + 2^-7."""
+    fused = np.float32(2.0 ** -17 + 2.0 ** -24)
+    idx = np.array([[0, 1]], np.int64)
+    w = np.array([[1.0, 1.0 + 2.0 ** -17]], np.float32)
+    # bf16 LL combine: experts 0, 1 on one rank, one slot each
+    b = np.zeros((2, 1, 1, 8), np.float32)
+    b[0] = -(1.0 + 2.0 ** -7)
+    b[1] = 1.0 + 2.0 ** -7
+    out = f32_from_bits(O.ll_combine(bits_from_f32_exact(b), idx, w, 2, 1))
+    assert (out == fused).all(), "LL combine fma"
+    # FP8 LL combine: codes of -1 (0xB8) and 1 (0x38), scale 1 + 2^-7
+    assert O.e4m3_to_f32(0x38) == 1.0 and O.e4m3_to_f32(0xB8) == -1.0
+    q = np.zeros((2, 1, 1, 128), np.uint8)
+    q[0] = 0xB8
+    q[1] = 0x38
+    sc = np.full((2, 1, 1, 1), 1.0 + 2.0 ** -7, np.float32)
+    out = f32_from_bits(O.ll_combine_fp8(q, sc, idx, w, 2, 1))
+    assert (out == fused).all(), "FP8 LL combine fma"
+    # normal combine: one token on experts 0, 1 (ranks 0, 1), two biases
+    L = O.layout(idx, 2, 2, 1)
+    rows = bits_from_f32_exact(np.repeat(np.array([[1.0], [2.0 ** -8]], np.float32), 8, axis=1))
+    bias = bits_from_f32_exact(np.full((1, 8), 2.0 ** -24, np.float32))
+    out, _ = O.combine(rows, L, bias0=bias, bias1=bias)
+    assert (f32_from_bits(out) == np.float32(1.0)).all(), "bias after the rank sum"
+
+
 def fp8_edge_case(seed=4):
     """A decode batch whose rows hold an all-zero block and a block of values
     far below the amax floor, next to ordinary blocks."""

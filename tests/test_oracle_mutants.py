@@ -37,6 +37,25 @@ _LL_BF16_HEAD = ("        for (int64_t k = 0; k < K; ++k) {\n"
                  "            if (combine_mask != NULL && combine_mask[e / epr] != 0)\n"
                  "                continue;\n")
 
+# The LL slot assignment's loops, token-major as the reading fixes.
+_LL_SLOT_LOOPS = ("    for (int64_t t = 0; t < T; ++t) {\n        for (int64_t k = 0; k < K; ++k) {\n"
+                  "            int64_t e = topk_idx[t * K + k];\n"
+                  "            if (!ll_live(e, E, epr, rank_mask)) {")
+
+
+def _biases_first():
+    """The combine's rank sum followed by its bias additions, and the same
+    code with the bias additions moved before the rank sum."""
+    src = open(SRC).read()
+    zero = "        for (int64_t h = 0; h < H; ++h)\n            acc[h] = 0.0f;\n"
+    i0 = src.index(zero + "        for (int64_t r = 0; r < R; ++r) {")
+    tail = "                acc[h] += bf16_to_f32(bias1[t * H + h]);\n"
+    i1 = src.index(tail, i0) + len(tail)
+    block = src[i0:i1]
+    cut = block.index("        if (bias0 != NULL)")
+    return block, zero + block[cut:] + block[len(zero):cut]
+
+
 # (name, original text, planted text): each original must occur exactly once.
 MUTANTS = [
     ("bf16 ties away from zero", "u += 0x7fffu + lsb;", "u += 0x8000u;"),
@@ -133,6 +152,15 @@ MUTANTS = [
     ("LL counts capped at capacity", "        counts[(e % epr) * R + e / epr] = cnt[e];",
      "        counts[(e % epr) * R + e / epr] = cnt[e] < num_slots ? cnt[e] : (int32_t)num_slots;"),
     ("e4m3 sign dropped", "    uint8_t sign = signbit(f) ? 0x80 : 0;", "    uint8_t sign = 0;"),
+    ("LL combine without fma", "acc[h] = fmaf(w, bf16_to_f32(buf[cell * H + h]), acc[h]);",
+     "acc[h] = acc[h] + w * bf16_to_f32(buf[cell * H + h]);"),
+    ("fp8 LL combine without fma", "acc[h] = fmaf(w, v, acc[h]);", "acc[h] = acc[h] + w * v;"),
+    ("biases before the rank sum",) + _biases_first(),
+    ("LL slots in slot-major order", _LL_SLOT_LOOPS,
+     _LL_SLOT_LOOPS.replace("    for (int64_t t = 0; t < T; ++t) {\n        for (int64_t k = 0; k < K; ++k) {",
+                            "    for (int64_t k = 0; k < K; ++k) {\n        for (int64_t t = 0; t < T; ++t) {")),
+    ("channel size rounded down", "    int64_t per = (T + C - 1) / C;",
+     "    int64_t per = T / C > 0 ? T / C : 1;"),
 ]
 
 
@@ -163,6 +191,7 @@ def quick_pins():
     pinlib.check_ll_fp8(pinlib.fp8_edge_case())
     pinlib.check_tie_rounding()
     pinlib.check_sum_order()
+    pinlib.check_fma_and_bias_order()
     pinlib.check_ll_combine_fp8(random_case(12, 40, 384, 16, 4, 4, 1, mask=0.2, dup=0.2, slots=40),
                                 rank_mask=np.array([0, 0, 1, 0], np.int32), seed=1)
 

@@ -140,6 +140,10 @@ def test_sum_order():
     pinlib.check_sum_order()
 
 
+def test_fma_and_bias_order():
+    pinlib.check_fma_and_bias_order()
+
+
 def test_ll_fp8_zero_and_tiny_blocks():
     pinlib.check_ll_fp8(pinlib.fp8_edge_case())
 
