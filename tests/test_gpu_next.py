@@ -325,3 +325,70 @@ def test_ll_combine_fp8(case, ll_mode):
     assert_bf16_close(np.where(nan_e, 0, got), np.where(nan_e, 0, exp), what=f"fp8 combine {case}")
     if case != "nonfinite":
         assert not nan_e.any()
+
+
+# ---------------------------------------------------- crafted rounding cases
+
+
+def _rows_f32(values, H=8):
+    return pinlib.bits_from_f32_exact(np.repeat(np.asarray(values, np.float32)[:, None], H, axis=1))
+
+
+def test_crafted_sum_order_and_fma_on_gpu():
+    """The crafted cases the oracle is pinned with, through the HIP kernels:
+    summation order (ranks, slots, replicas ascending), the fused
+    multiply-add of the LL combines and the bias order of the combine.  Each
+    case has one right answer, and the wrong orders or an unfused product give
+    another."""
+    terms = np.array([1.0, 2.0 ** -8, 2.0 ** -24, 2.0 ** -24], np.float32)
+    fwd, rev = np.float32(1.0), np.float32(1.0 + 2.0 ** -7)
+    fused = np.float32(2.0 ** -17 + 2.0 ** -24)
+
+    def values(t):
+        return pinlib.f32_from_bits(host_bits(t))
+
+    # normal combine: one token on experts 0..3, one per rank
+    buf = epm.Buffer(4, 4, 1)
+    idx = dev(np.array([[0, 1, 2, 3]], np.int64))
+    x = dev_bf16(_rows_f32([1.0]))
+    _, _, _, _, h, _ = buf.dispatch(x, idx)
+    for t, want in ((terms, fwd), (terms[::-1].copy(), rev)):
+        out, _, _ = buf.combine(dev_bf16(_rows_f32(t)), h)
+        assert (values(out) == want).all(), "combine rank order"
+    h.free()
+    # bias after the rank sum: ranks 0, 1 hold 1 and 2^-8, two biases of 2^-24
+    buf = epm.Buffer(2, 2, 1)
+    _, _, _, _, h, _ = buf.dispatch(x, dev(np.array([[0, 1]], np.int64)))
+    bias = dev_bf16(_rows_f32([2.0 ** -24]))
+    out, _, _ = buf.combine(dev_bf16(_rows_f32([1.0, 2.0 ** -8])), h, bias=(bias, bias))
+    assert (values(out) == fwd).all(), "bias after the rank sum"
+    h.free()
+
+    # LL combines: experts 0, 1 on one rank, one slot each
+    buf = epm.Buffer(1, 2)
+    lidx = dev(np.array([[0, 1]], np.int64))
+    w = dev(np.array([[1.0, 1.0 + 2.0 ** -17]], np.float32))
+    _, _, hdl, _, _ = buf.low_latency_dispatch(dev_bf16(_rows_f32([1.0], H=128)), lidx, 1, 2)
+    y = _rows_f32([-(1.0 + 2.0 ** -7), 1.0 + 2.0 ** -7], H=128).reshape(2, 1, 1, 128)
+    out, _, _ = buf.low_latency_combine(dev_bf16(y), lidx, w, hdl)
+    assert (values(out) == fused).all(), "LL combine fma"
+    q = np.zeros((2, 1, 1, 128), np.uint8)
+    q[0], q[1] = 0xB8, 0x38  # e4m3 codes of -1 and 1
+    sc = np.full((2, 1, 1, 1), 1.0 + 2.0 ** -7, np.float32)
+    out, _, _ = buf.low_latency_combine((dev(q), dev(sc)), lidx, w, hdl)
+    assert (values(out) == fused).all(), "FP8 LL combine fma"
+    # and the slot order: unit weights over four slots
+    buf = epm.Buffer(1, 4)
+    lidx = dev(np.array([[0, 1, 2, 3]], np.int64))
+    ones = dev(np.ones((1, 4), np.float32))
+    _, _, hdl, _, _ = buf.low_latency_dispatch(x, lidx, 1, 4)
+    for t, want in ((terms, fwd), (terms[::-1].copy(), rev)):
+        out, _, _ = buf.low_latency_combine(dev_bf16(_rows_f32(t).reshape(4, 1, 1, 8)), lidx, ones,
+                                            hdl)
+        assert (values(out) == want).all(), "LL combine slot order"
+
+    # lb_reduce_grads: own gradient 0, four replicas of expert 0
+    for t, want in ((terms, fwd), (terms[::-1].copy(), rev)):
+        eg = dev_bf16(_rows_f32([0.0]))
+        buf.lb_reduce_grads(dev_bf16(_rows_f32(t)), eg, dev(np.zeros(4, np.int64)))
+        assert (values(eg) == want).all(), "lb_reduce_grads replica order"
