@@ -683,6 +683,13 @@ def check_e4m3(seed=0):
     inr = pts[np.abs(pts) <= 448]
     tq = torch.from_numpy(inr).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     np.testing.assert_array_equal(O.f32_to_e4m3(inr), tq)
+    # the format has no infinity: NaN encodes to a NaN code (0x7F or 0xFF, the
+    # sign is left open), and infinities saturate to +-448 like any value
+    # past the largest finite one
+    nan_codes = O.f32_to_e4m3(np.array([np.nan, -np.nan], np.float32))
+    assert all(int(c) & 0x7F == 0x7F for c in nan_codes), nan_codes
+    np.testing.assert_array_equal(O.f32_to_e4m3(np.array([np.inf, -np.inf], np.float32)),
+                                  np.array([0x7E, 0xFE], np.uint8))
 
 
 def check_ll_fp8(inp, rank_mask=None):

@@ -161,6 +161,17 @@ MUTANTS = [
                             "    for (int64_t k = 0; k < K; ++k) {\n        for (int64_t t = 0; t < T; ++t) {")),
     ("channel size rounded down", "    int64_t per = (T + C - 1) / C;",
      "    int64_t per = T / C > 0 ? T / C : 1;"),
+    ("e4m3 NaN saturates", "    if (isnan(f))\n        return 0x7F;", "    if (isnan(f))\n        return 0x7E;"),
+    ("bf16 NaN not special-cased",
+     "    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)\n",
+     "    if (0)\n"),
+    ("expert counts ignore the rank mask",
+     "            if (rank_masked(rank_mask, e / epr))\n"
+     "                continue; /* expert on a masked rank: as a masked slot */\n"
+     "            num_tokens_per_expert[e] += 1;",
+     "            num_tokens_per_expert[e] += 1;\n"
+     "            if (rank_masked(rank_mask, e / epr))\n"
+     "                continue; /* expert on a masked rank: as a masked slot */"),
 ]
 
 
