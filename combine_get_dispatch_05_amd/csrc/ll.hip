@@ -331,14 +331,18 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
 }
 
 constexpr int kLLTokPairs = 4096;  // token-major path for T*K up to this (ids held in LDS)
+constexpr int kSlotChunk = 8;      // a token's experts matched per pass of the slot scan
 
 // Token-major variant for small batches (T*K <= kLLTokPairs), same results
 // as ll_dispatch_kernel.  Every workgroup first loads the whole [T][K] id
-// table into LDS.  Workgroups [0, T*ny) are token workgroups: (t, slice y);
-// one wave per own pair (t, k) counts the earlier pairs (in (token, slot)
-// order) that name the same expert, which is the pair's slot; the slice of
-// x[t] is then read once and stored to all K destination cells (for FP8 each
-// 128-element block is quantized once).  The remaining workgroups handle
+// table into LDS.  Workgroups [0, T*ny) are token workgroups: (t, slice y).
+// The slot of an own pair (t, k) is the number of earlier pairs (in (token,
+// slot) order) that name the same expert: all lanes of the workgroup scan the
+// earlier tokens' pairs once, each entry compared with up to kSlotChunk of
+// the token's experts, the counts are summed over the workgroup, and thread
+// k adds the token's own earlier slots.  The slice of x[t] is then read once
+// and stored to all K destination cells (for FP8 each 128-element block is
+// quantized once).  The remaining workgroups handle
 // four experts each (one per wave): the expert's count and the -1 entries
 // of its unused src_info cells.
 template <bool kFP8>
@@ -351,6 +355,7 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_tok_kernel(
 {
     __shared__ int32_t s_ids[kLLTokPairs];
     __shared__ int64_t s_cell[kMaxTopk];
+    __shared__ int32_t s_cnt[kMaxTopk];  // earlier tokens' pairs naming pair k's expert
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
@@ -381,6 +386,8 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_tok_kernel(
         }
     }
 
+    if (tid < kMaxTopk)
+        s_cnt[tid] = 0;
     // expert id of every pair; -1 for masked slots and invalid ids
     constexpr int kU = 4;
     for (int i0 = 0; i0 < TK; i0 += kLLBlock * kU) {
@@ -418,34 +425,57 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_tok_kernel(
         return;
     }
 
-    for (int k = wid; k < K; k += kLLWaves) {
-        const int e = s_ids[t * K + k];
-        int64_t cell = -1;
-        int slot = -1;
-        if (e >= 0) {
-            const int r = e / epr;
-            if (rank_mask == nullptr || rank_mask[r] == 0) {
-                const int lim = t * K + k;
-                int cnt = 0;
-                for (int i = lane; i < lim; i += kWave)
-                    cnt += s_ids[i] == e ? 1 : 0;
-                cnt = wave_sum(cnt);
-                if (cnt < S) {
-                    slot = cnt;
-                    cell = (int64_t(e - r * epr) * R + r) * S + cnt;
-                }
-            }
+    // Thread k < K owns pair (t, k); its rank-mask load is issued before the
+    // scan so that the scan hides its latency.
+    const int base = t * K;
+    int e_mine = -1;
+    bool live_mine = false;
+    if (tid < K) {
+        e_mine = s_ids[base + tid];
+        live_mine = e_mine >= 0 && (rank_mask == nullptr || rank_mask[e_mine / epr] == 0);
+    }
+    // An expert occurs only a few times among the earlier pairs, so the few
+    // nonzero per-lane counts go to LDS with atomic adds.
+    for (int k0 = 0; k0 < K; k0 += kSlotChunk) {
+        int ek[kSlotChunk], c[kSlotChunk];
+#pragma unroll
+        for (int q = 0; q < kSlotChunk; ++q) {
+            ek[q] = k0 + q < K ? s_ids[base + k0 + q] : -2;  // -2 matches no entry
+            c[q] = 0;
         }
-        if (lane == 0) {
-            s_cell[k] = cell;
-            if (yb == 0) {
-                topk_slot[t * K + k] = slot;
-                if (cell >= 0)
-                    src_info[cell] = t;
-            }
+        for (int i = tid; i < base; i += kLLBlock) {
+            const int v = s_ids[i];
+#pragma unroll
+            for (int q = 0; q < kSlotChunk; ++q)
+                c[q] += v == ek[q] ? 1 : 0;
         }
+#pragma unroll
+        for (int q = 0; q < kSlotChunk; ++q)
+            if (c[q] != 0)
+                atomicAdd(&s_cnt[k0 + q], c[q]);
     }
     __syncthreads();
+    if (tid < K) {
+        int64_t cell = -1;
+        int slot = -1;
+        if (live_mine) {
+            int cnt = s_cnt[tid];
+            for (int j = 0; j < tid; ++j)
+                cnt += s_ids[base + j] == e_mine ? 1 : 0;
+            if (cnt < S) {
+                const int r = e_mine / epr;
+                slot = cnt;
+                cell = (int64_t(e_mine - r * epr) * R + r) * S + cnt;
+            }
+        }
+        s_cell[tid] = cell;
+        if (yb == 0) {
+            topk_slot[base + tid] = slot;
+            if (cell >= 0)
+                src_info[cell] = t;
+        }
+    }
+    __syncthreads();  // s_cell is read by the copy below
 
     if (!kFP8) {
         if (packed_x == nullptr)
