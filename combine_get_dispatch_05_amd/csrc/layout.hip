@@ -252,6 +252,7 @@ __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
 }
 
 constexpr int kPosBlock = 256;
+constexpr int kPosGrid = 512;   // split tiles while the grid stays within this
 constexpr int kSelfScanBlocks = 32;  // up to this many count blocks, pos blocks scan for themselves
 constexpr int kBatch = 8;
 
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
 // pack and reduce kernels read.
 template <int NW, bool kSelfScan>
 __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
-    int T, int E, int R, int C, int kmax, int nB, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
+    int T, int E, int R, int C, int kmax, int nB, int sub_shift, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
     const int32_t *__restrict__ blk_count, const int32_t *__restrict__ blk_ecount,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
     int32_t *__restrict__ recv_src_idx, int32_t *__restrict__ dst_row,
@@ -396,10 +397,19 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     __shared__ int32_t s_wsum[kPosBlock / kWave];
     __shared__ uint64_t s_tokm[NW][kWave];  // live-rank bitmask of each token of the tile
     const int tid = threadIdx.x;
-    const int wg = blockIdx.x;
+    // 2^sub_shift workgroups (1, 2 or 4) share a tile, sub_tok tokens each
+    // (powers of two throughout: shifts and masks, no integer division)
+    const int wg = blockIdx.x >> sub_shift;  // the 64-token tile
+    const int sub = blockIdx.x & ((1 << sub_shift) - 1);
+    const int sub_tok = kWave >> sub_shift;
     const int blk = wg / (kCountBlock / kWave);
     const int64_t t0 = int64_t(wg) * kWave;
     const int ntok = int(T - t0 < kWave ? T - t0 : kWave);
+    // this workgroup's tokens of the tile: [lo, hi)
+    const int lo = sub * sub_tok;
+    const int hi = lo + sub_tok < ntok ? lo + sub_tok : ntok;
+    if (lo >= hi)
+        return;  // uniform over the workgroup, before any barrier
 
     // Per-rank state of the tile.  The count kernel stored, for each rank, the
     // mask of the tile's tokens that hit it (ranks masked at the time already
@@ -436,7 +446,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     if (kSelfScan) {
         const int N = rank_exclusive_scan(s_tot, s_seg, R, s_wsum);
         __syncthreads();
-        if (blockIdx.x == 0)
+        if (wg == 0 && sub == 0)
             write_totals(T, E, R, C, nB, s_tot, s_seg, blk_ecount, num_tokens_per_rank,
                          num_tokens_per_expert, rank_prefix_matrix, channel_prefix_matrix,
                          recv_channel_prefix_matrix, num_recv, N, kPosBlock);
@@ -452,9 +462,9 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     // one 4-byte is_token_in_rank store.
     if ((R & 3) == 0) {
         const int G = R >> 2;
-        const int items = ntok * G;
+        const int items = (hi - lo) * G;
         const int dt = kPosBlock / G, dg = kPosBlock % G;
-        int tl = tid / G, g = tid % G;
+        int tl = lo + tid / G, g = tid % G;
         for (int i = tid; i < items; i += kPosBlock) {
             const int64_t t = t0 + tl;
             const uint64_t below = (1ull << tl) - 1ull;
@@ -479,9 +489,9 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
             }
         }
     } else {
-        const int cells = ntok * R;
+        const int cells = (hi - lo) * R;
         const int dt = kPosBlock / R, dr = kPosBlock % R;
-        int tl = tid / R, r = tid % R;
+        int tl = lo + tid / R, r = tid % R;
         for (int i = tid; i < cells; i += kPosBlock) {
             const uint64_t b = s_mask[r];
             const bool hit = (b >> tl) & 1ull;
@@ -498,12 +508,13 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
         }
     }
 
-    // Channel ends inside the tile: hits of rank r before the boundary token.
+    // Channel ends at this workgroup's tokens: hits of rank r before the
+    // boundary token.
     const int per = (T + C - 1) / C;
-    int64_t boundary = ((t0 + per - 1) / per) * per;  // smallest multiple of per >= t0
+    int64_t boundary = ((t0 + lo + per - 1) / per) * per;  // smallest multiple of per >= t0 + lo
     if (boundary == 0)
         boundary = per;
-    for (; boundary < t0 + ntok; boundary += per) {
+    for (; boundary < t0 + hi; boundary += per) {
         const int bl = int(boundary - t0);
         const int64_t c = boundary / per - 1;
         for (int rr = tid; rr < R; rr += kPosBlock) {
@@ -514,12 +525,13 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     }
 
     // Each token's destination rows in ascending rank order (and the inverse
-    // map recv_src_idx): lane = token, and wave p of the block writes the
-    // entries j with j % 4 == p.
+    // map recv_src_idx): sub_tok lanes per token group, and group p of the
+    // workgroup writes the entries j with j % parts == p.
     {
-        const int tl = tid & (kWave - 1);
-        const int part = tid >> 6;
-        if (tl < ntok) {
+        const int parts = (kPosBlock / kWave) << sub_shift;  // kPosBlock / sub_tok
+        const int tl = lo + (tid & (sub_tok - 1));
+        const int part = tid >> (6 - sub_shift);
+        if (tl < hi) {
             const int64_t t = t0 + tl;
             const uint64_t below = (1ull << tl) - 1ull;
             int j = 0;
@@ -529,7 +541,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
                 while (mm) {
                     const int bit = __ffsll((unsigned long long)mm) - 1;
                     mm &= mm - 1;
-                    if ((j & 3) == part) {
+                    if ((j & (parts - 1)) == part) {
                         const int rr = w * kWave + bit;
                         const int row = s_seg[rr] + s_off[rr] + __popcll(s_mask[rr] & below);
                         dst_row[size_t(t) * kmax + j] = row;
@@ -540,13 +552,24 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
                 }
             }
             for (; j < kmax; ++j) {
-                if ((j & 3) == part) {
+                if ((j & (parts - 1)) == part) {
                     dst_row[size_t(t) * kmax + j] = -1;
                     dst_rank[size_t(t) * kmax + j] = -1;
                 }
             }
         }
     }
+}
+
+// log2 of the workgroups per tile of the position kernel: a small grid
+// leaves most of the chip idle, so its tiles are split (each part repeats
+// the tile's cheap per-rank setup); a grid that already fills the chip is not.
+int pos_split_shift(int nW)
+{
+    int sh = 2;  // at most 4 workgroups per tile
+    while (sh > 0 && (int64_t(nW) << sh) > kPosGrid)
+        --sh;
+    return sh;
 }
 
 template <int NW>
@@ -566,9 +589,10 @@ hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
                            b.num_tokens_per_expert, b.rank_prefix_matrix, b.channel_prefix_matrix,
                            b.recv_channel_prefix_matrix, b.num_recv);
     auto pos_kernel = self_scan ? layout_pos_kernel<NW, true> : layout_pos_kernel<NW, false>;
+    const int sub_shift = pos_split_shift(s.nW);
     if (s.T > 0)
-        hipLaunchKernelGGL(pos_kernel, dim3(s.nW), dim3(kPosBlock), 0, stream, s.T, s.E, s.R,
-                           s.C, s.kmax, s.nB, b.wave_mask, b.wave_base, b.blk_count,
+        hipLaunchKernelGGL(pos_kernel, dim3(unsigned(s.nW) << sub_shift), dim3(kPosBlock), 0, stream,
+                           s.T, s.E, s.R, s.C, s.kmax, s.nB, sub_shift, b.wave_mask, b.wave_base, b.blk_count,
                            b.blk_ecount, b.is_token_in_rank, b.send_head, b.recv_src_idx,
                            b.dst_row, b.dst_rank, b.num_tokens_per_rank, b.num_tokens_per_expert,
                            b.rank_prefix_matrix, b.channel_prefix_matrix,
