@@ -366,22 +366,25 @@ __global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
                  recv_channel_prefix_matrix, num_recv, N, kPosBlock);
 }
 
-// Positions of one 64-token tile.  With kSelfScan the block first sums the
-// count blocks' per-rank totals itself (all loads of a batch issued before
-// any add): those before its own block give its bases, all of them give the
-// segment starts S[r]; block 0 also writes the totals.  Otherwise the bases
-// were made by layout_scan_kernel.
+// Positions of one 64-token tile, or of a 2^sub_shift-th part of it (small
+// grids split their tiles so that more of the chip works).  With kSelfScan
+// the workgroup first sums the count blocks' per-rank totals itself (all
+// loads of a batch issued before any add): those before its own block give
+// its bases, all of them give the segment starts S[r]; the first workgroup
+// also writes the totals.  Otherwise the bases were made by
+// layout_scan_kernel.
 //
-// The (token, rank) cells of the tile are then spread flat over the block:
-// each cell's position is its tile base plus a popcount of the rank's
-// membership mask below the token, so there is no loop-carried dependence,
-// and consecutive lanes write consecutive entries of every [T][R] row
-// (send_head, is_token_in_rank).  Finally the first wave takes the tokens and
-// emits each token's destination rows in ascending rank order, the list the
-// pack and reduce kernels read.
+// The (token, rank) cells of the workgroup's tokens are then spread flat over
+// its lanes: each cell's position is its tile base plus a popcount of the
+// rank's membership mask below the token, so there is no loop-carried
+// dependence, and consecutive lanes write consecutive entries of every [T][R]
+// row (send_head, is_token_in_rank).  Finally groups of lanes emit each
+// token's destination rows in ascending rank order, the list the pack and
+// reduce kernels read.
 template <int NW, bool kSelfScan>
 __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
-    int T, int E, int R, int C, int kmax, int nB, int sub_shift, const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
+    int T, int E, int R, int C, int kmax, int nB, int sub_shift,
+    const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
     const int32_t *__restrict__ blk_count, const int32_t *__restrict__ blk_ecount,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
     int32_t *__restrict__ recv_src_idx, int32_t *__restrict__ dst_row,

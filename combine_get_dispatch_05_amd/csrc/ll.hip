@@ -339,12 +339,12 @@ constexpr int kSlotChunk = 8;      // a token's experts matched per pass of the 
 // The slot of an own pair (t, k) is the number of earlier pairs (in (token,
 // slot) order) that name the same expert: all lanes of the workgroup scan the
 // earlier tokens' pairs once, each entry compared with up to kSlotChunk of
-// the token's experts, the counts are summed over the workgroup, and thread
-// k adds the token's own earlier slots.  The slice of x[t] is then read once
+// the token's experts, the per-lane counts are added up in LDS, and thread k
+// adds the token's own earlier slots.  The slice of x[t] is then read once
 // and stored to all K destination cells (for FP8 each 128-element block is
-// quantized once).  The remaining workgroups handle
-// four experts each (one per wave): the expert's count and the -1 entries
-// of its unused src_info cells.
+// quantized once).  The remaining workgroups handle four experts each (one
+// per wave): the expert's count and the -1 entries of its unused src_info
+// cells.
 template <bool kFP8>
 __global__ __launch_bounds__(kLLBlock) void ll_dispatch_tok_kernel(
     const u32x4 *__restrict__ x, int T, int V, int K, int E, int R, int epr, int S, int ny,
