@@ -299,6 +299,8 @@ def main():
                                out, cw, packed, lcount, lsrc, lslot, lout, lx, ltopk, lw, dd, S,
                                epr)
 
+    workloads = measure_workloads(args, L, abi)
+
     # ---------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline and args.cpu_seconds > 0:
@@ -330,6 +332,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "next": next_report,
+        "workloads": workloads,
         "copy_ceiling": {"bytes_read_plus_written": 2 * copy_bytes, "avg_us": round(copy_us, 2),
                          "gbs": round(copy_gbs, 1),
                          "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
@@ -365,6 +368,23 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     rep = {}
     T, H, K = tr.T, tr.H, tr.K
     s = abi.current_stream()
+    # the layout with the N readback a fresh dispatch of unknown size needs
+    # (one host sync per call), host wall time per call
+    def layout_and_n():
+        hl = ctypes.c_void_p()
+        abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, None, ctypes.byref(hl),
+                                           s), "layout")
+        nn = ctypes.c_int64()
+        abi.check(L.ep_handle_num_recv(hl, ctypes.byref(nn)), "num_recv")
+        L.ep_handle_free(hl)
+    for _ in range(max(args.warmup, 2)):
+        layout_and_n()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layout_and_n()
+    us = (time.perf_counter() - t0) * 1e6 / args.steps
+    rep["layout_with_n_readback"] = {"avg_us": round(us, 2), "mtok_s": round(T / us, 2)}
     # combine with two bias rows
     h = ctypes.c_void_p()
     abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), None, ctypes.byref(h),
@@ -459,13 +479,98 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     return rep
 
 
-def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int, op_bytes=None):
+def measure_workloads(args, L, abi):
+    """The skewed (Zipf 1.2, 10 % masked, R=32) and large (R=144, 32 redundant
+    experts) workloads: layout, fresh dispatch (layout + pack with top-k),
+    cached dispatch and combine, each timed over back-to-back calls with HIP
+    events at the ends (not in ``value``)."""
+    import numpy as np
+    import torch
+    from gen import config_inputs
+
+    P = abi.ptr
+    dev = torch.device("cuda", 0)
+    s = abi.current_stream()
+    n = max(args.steps // 2, 3)
+
+    def timed(fn):
+        for _ in range(max(args.warmup, 2)):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(n):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / n
+
+    rep = {}
+    for cfg in (2, 4):
+        inp = config_inputs(cfg)
+        T, H, E, K, R, C = inp.T, inp.H, inp.E, inp.K, inp.R, inp.C
+        d = abi.dims(T, H, K, E, R, C)
+        cap = int(L.ep_max_recv_rows(ctypes.byref(d)))
+        x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).to(dev)
+        topk = torch.from_numpy(inp.topk_idx).to(dev)
+        w = torch.from_numpy(inp.topk_weights).to(dev)
+        recv = torch.empty((cap, H), dtype=torch.int16, device=dev)
+        rti = torch.empty((cap, K), dtype=torch.int64, device=dev)
+        rtw = torch.empty((cap, K), dtype=torch.float32, device=dev)
+        out = torch.empty((T, H), dtype=torch.int16, device=dev)
+        cw = torch.empty((T, K), dtype=torch.float32, device=dev)
+
+        def layout():
+            h = ctypes.c_void_p()
+            abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, None,
+                                               ctypes.byref(h), s), "layout")
+            L.ep_handle_free(h)
+
+        def fresh():
+            h = ctypes.c_void_p()
+            abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), None, ctypes.byref(h),
+                                    P(recv), P(rti), P(rtw), cap, None, s), "dispatch")
+            L.ep_handle_free(h)
+
+        h = ctypes.c_void_p()
+        abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), None, ctypes.byref(h),
+                                P(recv), P(rti), P(rtw), cap, None, s), "dispatch")
+        nn = ctypes.c_int64()
+        abi.check(L.ep_handle_num_recv(h, ctypes.byref(nn)), "num_recv")
+        N = int(nn.value)
+        us_lay = timed(layout)
+        us_fresh = timed(fresh)
+        us_cached = timed(lambda: abi.check(L.ep_dispatch(
+            ctypes.byref(d), P(x), None, None, None, ctypes.byref(h), P(recv), None, None, cap,
+            None, s), "cached dispatch"))
+        us_comb = timed(lambda: abi.check(L.ep_combine(h, H, P(recv), cap, P(rtw), None, None,
+                                                       None, P(out), P(cw), s), "combine"))
+        L.ep_handle_free(h)
+        b_cached = (T + N) * H * 2 + N * 4
+        b_comb = (N + T) * H * 2 + N * 4 + N * K * 4 + T * K * 4
+        rep[inp.name] = {
+            "T": T, "H": H, "E": E, "K": K, "R": R, "C": C, "N": N,
+            "layout_us": round(us_lay, 2), "layout_mtok_s": round(T / us_lay, 2),
+            "dispatch_fresh_us": round(us_fresh, 2),
+            "dispatch_cached_us": round(us_cached, 2),
+            "dispatch_cached_gbs": round(b_cached / (us_cached * 1e-6) / 1e9, 1),
+            "combine_us": round(us_comb, 2),
+            "combine_gbs": round(b_comb / (us_comb * 1e-6) / 1e9, 1),
+        }
+        del x, recv, rti, rtw, out, cw
+    return rep
+
+
+def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int, op_bytes=None,
+                 workloads=(0, 2, 4)):
     """The oracle, as it stands, on the same rows of the same workload:
     whole passes (layout, dispatch, cached dispatch, combine, LL dispatch,
     LL combine) until ``budget`` seconds of CPU work are spent, with the
     process pinned to one core.  Also the median time of each operation over
-    the passes (and its rate on the same algorithmic bytes)."""
+    the passes (and its rate on the same algorithmic bytes), and the median
+    of three runs of layout, dispatch and combine on each of ``workloads``
+    (workload ids of the input generator)."""
     import oracle
+    from gen import config_inputs
     pinned = None
     old_aff = None
     if hasattr(os, "sched_setaffinity"):
@@ -501,6 +606,25 @@ def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int, op_bytes=None)
             el = time.perf_counter() - t0
             if el >= budget:
                 break
+        per_workload = {}
+        for cfg in workloads:
+            inp = config_inputs(cfg)
+            tl, td, tc = [], [], []
+            for _ in range(3):
+                c0 = time.perf_counter()
+                lay = oracle.layout(inp.topk_idx, inp.E, inp.R, inp.C)
+                c1 = time.perf_counter()
+                rx, _, rtw = oracle.dispatch(inp.x, inp.topk_idx, inp.topk_weights, inp.E, inp.R,
+                                             lay)
+                c2 = time.perf_counter()
+                oracle.combine(rx, lay, rtw)
+                c3 = time.perf_counter()
+                tl.append(c1 - c0)
+                td.append(c2 - c1)
+                tc.append(c3 - c2)
+            per_workload[inp.name] = {"layout_ms": round(1e3 * sorted(tl)[1], 3),
+                                      "dispatch_ms": round(1e3 * sorted(td)[1], 3),
+                                      "combine_ms": round(1e3 * sorted(tc)[1], 3)}
     finally:
         if old_aff is not None and pinned is not None:
             os.sched_setaffinity(0, old_aff)
@@ -523,7 +647,7 @@ def cpu_baseline(tr, dc, x2_bits, budget: float, step_bytes: int, op_bytes=None)
             "sample": f"{passes} whole passes of the benchmark step (same workload, same rows) "
                       f"in {el:.1f} s, single-threaded C oracle"
                       + (f" pinned to CPU {pinned}" if pinned is not None else ""),
-            "per_op": per_op,
+            "per_op": per_op, "per_workload": per_workload,
             "host_cpu": model or platform.processor(), "host_nproc": os.cpu_count()}
 
 

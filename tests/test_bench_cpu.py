@@ -47,11 +47,14 @@ def test_cpu_baseline_leg():
     # bytes of the size the bench uses: the rates are rounded to 1 MB/s, and
     # parallel test workers share the one core every leg pins itself to
     out = bench.cpu_baseline(tr, dc, x2_bits=random_rows(tr.T, tr.H, 0, tag=11), budget=0.01,
-                             step_bytes=10**12, op_bytes={n: 10**12 for n in names})
+                             step_bytes=10**12, op_bytes={n: 10**12 for n in names},
+                             workloads=(0,))
     assert out["kind"] == "oracle" and out["cores"] == 1 and out["unit"] == "GB/s"
     assert out["value"] > 0 and "whole passes" in out["sample"]
     assert np.isfinite(out["value"])
     assert sorted(out["per_op"]) == sorted(names)
     assert all(v["median_ms"] > 0 and v["gbs"] > 0 for v in out["per_op"].values())
+    assert list(out["per_workload"]) == ["tiny"]
+    assert all(v > 0 for v in out["per_workload"]["tiny"].values())
     if hasattr(os, "sched_getaffinity"):
         assert len(os.sched_getaffinity(0)) >= 1  # the affinity is restored

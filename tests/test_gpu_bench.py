@@ -50,6 +50,13 @@ def test_bench_line_keeps_the_contract():
     if roof["traffic"] is not None:  # counters taken on the current pack source
         assert abs(roof["traffic"] - algo) <= 0.02 * algo
 
+    # informational parts: the layout with its N readback, the other workloads
+    assert b["next"]["layout_with_n_readback"]["avg_us"] > 0
+    for name in ("skewed", "large"):
+        wl = b["workloads"][name]
+        assert wl["N"] > 0 and wl["combine_gbs"] > 0 and wl["dispatch_cached_gbs"] > 0
+
     cpu = b["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["cores"] == 1
     assert cpu["value"] > 0 and cpu["sample"]
+    assert sorted(cpu["per_workload"]) == ["large", "skewed", "tiny"]
