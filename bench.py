@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU work budget of the oracle baseline leg (0 = skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the skewed and large workloads (profiling runs: their launches "
+                        "would mix into the per-kernel figures of the training-scale batch)")
     return p.parse_args()
 
 
@@ -299,7 +302,7 @@ def main():
                                out, cw, packed, lcount, lsrc, lslot, lout, lx, ltopk, lw, dd, S,
                                epr)
 
-    workloads = measure_workloads(args, L, abi)
+    workloads = None if args.no_workloads else measure_workloads(args, L, abi)
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None
