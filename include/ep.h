@@ -31,9 +31,10 @@
  *     is int64 with -1 for a masked slot; weights are fp32.
  *   - Expert e belongs to rank e / (E/R) as local expert e % (E/R).
  *   - Alignment ([P3]): token-row pointers (x, recv_x, y, out, bias0, bias1,
- *     packed_x, packed_y, load-balance tensors) must be 16-byte aligned and hidden*2 must be a multiple of 16
- *     (rows are whole int4 vectors); int64 arrays 8-byte, others 4-byte
- *     aligned.  Violations return EP_ERR_ALIGN before any work is enqueued.
+ *     packed_x, packed_y, load-balance tensors) must be 16-byte aligned, and
+ *     hidden*2 must be a multiple of 16 (rows are whole int4 vectors); int64
+ *     arrays 8-byte, others 4-byte aligned.  Violations return EP_ERR_ALIGN
+ *     before any work is enqueued.
  *   - Expert ids outside [-1, E) are invalid input.  The kernels ignore such
  *     slots (treat them as masked) so that no access leaves its buffer.
  *   - Errors: every int-returning call returns an ep_status.  On any error no
