@@ -14,6 +14,8 @@
  * Prints one line and exits 0 on success; on a failed check prints it and
  * exits 1.
  */
+/* Built by gcc, not hipcc: the HIP runtime header needs its platform named
+ * (hipcc would define this itself).  There is no other platform here. */
 #define __HIP_PLATFORM_AMD__ 1
 #include <hip/hip_runtime_api.h>
 
