@@ -48,12 +48,52 @@ __device__ __forceinline__ u32x4 load_x_vec(const u32x4 *p)
     return *p;
 }
 
+// One pass of a group over the chunk [base, base + G*VPT) of a token's row:
+// VPT loads, all issued before the row list is consulted (rowv's own load
+// was issued earlier; only its ballot waits for it), then the chunk is
+// stored to each of the token's nhit destination rows.  Loads past the end
+// of the row read its last vector again (in bounds, never stored), so no
+// load sits behind a branch.
+template <int G, int VPT, bool NTS, bool NTL>
+__device__ __forceinline__ void pack_pass(const u32x4 *__restrict__ src, u32x4 *__restrict__ recv_x,
+                                          int V, int base, int gt, int rowv)
+{
+    u32x4 v[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int idx = base + i * G + gt;
+        v[i] = load_x_vec<NTL>(src + (idx < V ? idx : V - 1));
+    }
+    // The loaded vectors feed only the stores below, which run nhit times;
+    // without this the compiler moves the loads under "nhit > 0", i.e.
+    // behind the wait for the row list.  Empty and volatile, it keeps them
+    // here, all in flight together with the row list's load.
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+        asm volatile("" : "+v"(v[i]));
+    asm volatile("" : "+v"(rowv));  // (nor may the row list's test move above them)
+    const int nhit = __popcll(wave_ballot(rowv >= 0));  // rows are packed first
+    for (int j = 0; j < nhit; ++j) {
+        const int row = __builtin_amdgcn_readlane(rowv, j);
+        u32x4 *dst = recv_x + int64_t(row) * V;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int idx = base + i * G + gt;
+            if (idx < V)
+                store_row_vec<NTS>(v[i], dst + idx);
+        }
+    }
+}
+
 // A group of G lanes packs one slice of one token's row at a time: the row's
 // chunks of G*VPT vectors are dealt round-robin to S groups (S = 1: one group
 // per token), so more, shorter-lived wavefronts share the stores.  With a
 // persistent grid (fewer groups than token slices) each group walks them with
 // a grid stride.  NTS / NTL: packed rows are stored / token rows loaded
-// nontemporally.  The slice-0 group writes the top-k outputs.
+// nontemporally.  The slice-0 group writes the top-k outputs.  A row that
+// one chunk covers (the usual shape: 7168 = 128 lanes x 7 vectors x 8) takes
+// a loop-free path, so that the compiler need not wait for the previous
+// chunk's stores before it issues the loads.
 template <int G, int VPT, bool NTS, bool NTL, bool kTopk>
 __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
     const u32x4 *__restrict__ x, int T, int V, int K, int E, int epr, int kmax, int S,
@@ -67,41 +107,41 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
     const int gt = threadIdx.x % G;
     const int first = __builtin_amdgcn_readfirstlane(blockIdx.x * kGroups + threadIdx.x / G);
     const int stride = gridDim.x * kGroups;
-    for (int ts = first; ts < T * S; ts += stride) {
+    const bool one_pass = S == 1 && V <= G * VPT;
+    auto slice_work = [&](int ts) {
         const int t = ts / S;
         const int slice = ts - t * S;
         const u32x4 *src = x + int64_t(t) * V;
         const int rowv = lane < kmax ? dst_row[int64_t(t) * kmax + lane] : -1;
-        const int nhit = __popcll(wave_ballot(rowv >= 0));  // rows are packed first
-
-        if (recv_x != nullptr) {
-            for (int base = slice * G * VPT; base < V; base += S * G * VPT) {
-                u32x4 v[VPT];
-#pragma unroll
-                for (int i = 0; i < VPT; ++i) {
-                    const int idx = base + i * G + gt;
-                    if (idx < V)
-                        v[i] = load_x_vec<NTL>(src + idx);
-                }
-                for (int j = 0; j < nhit; ++j) {
-                    const int row = __builtin_amdgcn_readlane(rowv, j);
-                    u32x4 *dst = recv_x + int64_t(row) * V;
-#pragma unroll
-                    for (int i = 0; i < VPT; ++i) {
-                        const int idx = base + i * G + gt;
-                        if (idx < V)
-                            store_row_vec<NTS>(v[i], dst + idx);
-                    }
-                }
+        // The top-k inputs of the slice-0 group are loaded up front, so that
+        // their latency overlaps the row's (K <= 64 <= G: one slot per lane).
+        const bool topk = kTopk && slice == 0;
+        int rankv = -1;
+        int64_t e = -1;
+        float w = 0.0f;
+        if (topk) {
+            rankv = lane < kmax ? dst_rank[int64_t(t) * kmax + lane] : -1;
+            if (gt < K) {
+                e = topk_idx[int64_t(t) * K + gt];
+                if (recv_topk_weights != nullptr)
+                    w = topk_weights[int64_t(t) * K + gt];
             }
         }
 
-        if (kTopk && slice == 0) {
-            const int rankv = lane < kmax ? dst_rank[int64_t(t) * kmax + lane] : -1;
-            for (int k = gt; k < K; k += G) {
-                const int64_t e = topk_idx[int64_t(t) * K + k];
-                const float w =
-                    recv_topk_weights != nullptr ? topk_weights[int64_t(t) * K + k] : 0.0f;
+        if (recv_x != nullptr) {
+            if (one_pass)
+                pack_pass<G, VPT, NTS, NTL>(src, recv_x, V, 0, gt, rowv);
+            else
+                for (int base = slice * G * VPT; base < V; base += S * G * VPT)
+                    pack_pass<G, VPT, NTS, NTL>(src, recv_x, V, base, gt, rowv);
+        }
+
+        if (topk) {
+            // (their uses stay here: hoisted above the row's loads, they
+            // would make those wait for the top-k loads)
+            asm volatile("" : "+v"(e), "+v"(w), "+v"(rankv));
+            const int nhit = __popcll(wave_ballot(rowv >= 0));
+            if (gt < K) {
                 const bool valid = e >= 0 && e < E;
                 const int er = valid ? int(e) / epr : -1;
                 for (int j = 0; j < nhit; ++j) {
@@ -109,12 +149,21 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
                     const int r = __builtin_amdgcn_readlane(rankv, j);
                     const bool mine = er == r;
                     if (recv_topk_idx != nullptr)
-                        recv_topk_idx[row * K + k] = mine ? e - int64_t(r) * epr : -1;
+                        recv_topk_idx[row * K + gt] = mine ? e - int64_t(r) * epr : -1;
                     if (recv_topk_weights != nullptr)
-                        recv_topk_weights[row * K + k] = mine ? w : 0.0f;
+                        recv_topk_weights[row * K + gt] = mine ? w : 0.0f;
                 }
             }
         }
+    };
+    if (stride >= T * S) {
+        // one token slice per group (the usual launch): no loop around the
+        // slice, so nothing makes its loads wait for earlier stores
+        if (first < T * S)
+            slice_work(first);
+    } else {
+        for (int ts = first; ts < T * S; ts += stride)
+            slice_work(ts);
     }
 }
 

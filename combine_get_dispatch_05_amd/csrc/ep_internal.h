@@ -19,13 +19,17 @@ constexpr int kMaxRanks = 512;     // NW <= 8 64-bit rank-mask words
 constexpr int kMaxTopk = 64;
 constexpr int kMaxExperts = 8192;  // per-block expert histogram lives in LDS
 constexpr int kMaxChannels = 4096;
-constexpr int kMaxLLSlots = 4096;  // LL slot list lives in LDS
+constexpr int kMaxLLSlots = 4096;  // slots per low-latency expert cell list
 constexpr int64_t kMaxTokens = int64_t(1) << 24;
 constexpr int kMaxHidden = 1 << 20;
 
-// Device pointers of one layout (all inside a handle's arena).
-constexpr int kArenaFields = 16;
+// Device pointers of one layout (all inside a handle's arena).  The first
+// kLayoutCtrBytes of every arena hold the one-launch layout's counters,
+// zeroed when the arena is allocated and only ever increased after that.
+constexpr int kArenaFields = 17;
+constexpr size_t kLayoutCtrBytes = 256;
 struct LayoutBufs {
+    uint64_t *layout_ctr;                // [4] tickets, count units done, -, wait-timeout flag
     int32_t *num_tokens_per_rank;        // [R]
     int32_t *num_tokens_per_expert;      // [E]
     uint8_t *is_token_in_rank;           // [T][R]
@@ -39,13 +43,14 @@ struct LayoutBufs {
     uint64_t *wave_mask;                 // [nW][R] ballot of "token hits r" per 64-token wave
     int32_t *wave_base;                  // [nW][R] hits of r in earlier waves of the same block
     int32_t *blk_count;                  // [nB][R] block totals (exclusive bases after a scan kernel)
-    int32_t *blk_ecount;                 // [nB][E] per-block expert counts (512-token blocks)
+    int32_t *blk_ecount;                 // [nB][E] per-block expert counts
     int64_t *num_recv;                   // [1] N
     uint64_t *topk_hash;                 // [2] hash of the layout's topk_idx, and of a later one
 };
 
 struct LayoutShape {
     int T, K, E, R, C, epr, kmax, nW, nB;
+    bool fused;  // one-launch layout (count blocks of 256 tokens), else two kernels (512)
 };
 
 LayoutShape layout_shape(const ep_dims &d);
@@ -58,9 +63,20 @@ LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields]);
 bool log_enabled();
 void log_launch(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
 
-// rank_mask [R] int32 (nullable): nonzero ranks are masked.
+// How far an arena's one-launch layout counters have advanced: the tickets
+// and done marks of every layout launched in it so far (host-side, kept with
+// the arena; stream order makes each launch start where the last one ended).
+struct LayoutCounters {
+    uint64_t tickets = 0;
+    uint64_t done = 0;
+};
+
+// rank_mask [R] int32 (nullable): nonzero ranks are masked.  num_recv_host
+// (nullable): pinned, coherent host memory that also receives N, so that a
+// caller waiting for N can poll it instead of copying it back.
 hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const int32_t *rank_mask,
-                         const LayoutBufs &b, hipStream_t stream);
+                         const LayoutBufs &b, int64_t *num_recv_host, LayoutCounters &lc,
+                         hipStream_t stream);
 
 hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, const LayoutBufs &b,
                            const int64_t *topk_idx, const float *topk_weights, void *recv_x,
@@ -105,9 +121,14 @@ hipError_t launch_lb_prefetch_weights(const void *expert_weights, void *redundan
 // default choice.  Return false for a shape that is not compiled in.
 bool set_dispatch_tuning(int g, int vpt, int code);
 bool set_combine_tuning(int g, int vpt, int u);
-// Low-latency dispatch variant: 0 automatic (token-major for T*K <= 4096),
-// 1 expert-major always, 2 token-major whenever T*K allows.
+// Low-latency dispatch variant: 0 automatic (one launch for T*K <= 4096,
+// else slot scan + token-major copy), 1 slot scan + copy always, 2 one
+// launch whenever T*K allows.
 bool set_ll_tuning(int mode);
+// Layout: 0 automatic (the count and position kernels), 1 those kernels
+// always, 2 one launch whenever it fits (up to 8192 tokens).  Read when a
+// handle is made.
+bool set_layout_tuning(int mode);
 int dispatch_tuning_count();
 void dispatch_tuning_at(int i, int *g, int *vpt, int *code);
 int combine_tuning_count();

@@ -33,6 +33,8 @@
 // tokens' rank bitmasks with the live ranks, and the expert histogram skips
 // slots on masked ranks, so a masked rank's slots act as masked slots.
 
+#include <atomic>
+
 #include "ep_internal.h"
 
 namespace ep {
@@ -154,22 +156,24 @@ __device__ __forceinline__ int wave_inclusive_scan(int v)
 // wave's membership mask of that rank; the block turns the 8 waves'
 // popcounts into within-block offsets (LDS) and publishes masks, offsets,
 // its per-rank totals and its LDS expert histogram.
-template <int NW>
-__global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
-    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
-    int E, int R, int epr, int epr_shift, int nW, uint64_t *__restrict__ wave_mask,
+// The count of block `blk` (BC tokens, BC threads); the body of
+// layout_count_kernel and of the count units of layout_fused_kernel.
+template <int NW, int BC>
+__device__ __forceinline__ void count_body(
+    int blk, const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T,
+    int K, int E, int R, int epr, int epr_shift, int nW, uint64_t *__restrict__ wave_mask,
     int32_t *__restrict__ wave_base, int32_t *__restrict__ blk_count,
     int32_t *__restrict__ blk_ecount)
 {
-    constexpr int kWaves = kCountBlock / kWave;
+    constexpr int kWaves = BC / kWave;
     extern __shared__ int32_t s_ecount[];  // [E]
     __shared__ int32_t s_wcnt[kWaves][kMaxRanks];
     __shared__ uint64_t s_live[NW];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
-    const int wg = blockIdx.x * kWaves + wid;
-    const int64_t t = int64_t(blockIdx.x) * kCountBlock + tid;
+    const int wg = blk * kWaves + wid;
+    const int64_t t = int64_t(blk) * BC + tid;
 
     uint64_t m[NW];
     int64_t ids0[kIdChunk];
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
     const int64_t *row = topk_idx + t * K;
     if (t < T)
         token_rank_mask<NW>(row, K, E, epr, epr_shift, m, ids0);
-    for (int i = tid; i < E; i += kCountBlock)
+    for (int i = tid; i < E; i += BC)
         s_ecount[i] = 0;
     build_live<NW>(rank_mask, R, s_live);
     __syncthreads();
@@ -235,20 +239,31 @@ __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
     }
     __syncthreads();
 
-    for (int r = tid; r < R; r += kCountBlock) {
+    for (int r = tid; r < R; r += BC) {
         int acc = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const int c = s_wcnt[w][r];
-            const int g = blockIdx.x * kWaves + w;
+            const int g = blk * kWaves + w;
             if (g < nW)
                 wave_base[size_t(g) * R + r] = acc;
             acc += c;
         }
-        blk_count[size_t(blockIdx.x) * R + r] = acc;
+        blk_count[size_t(blk) * R + r] = acc;
     }
-    for (int i = tid; i < E; i += kCountBlock)
-        blk_ecount[size_t(blockIdx.x) * E + i] = s_ecount[i];
+    for (int i = tid; i < E; i += BC)
+        blk_ecount[size_t(blk) * E + i] = s_ecount[i];
+}
+
+template <int NW>
+__global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
+    int E, int R, int epr, int epr_shift, int nW, uint64_t *__restrict__ wave_mask,
+    int32_t *__restrict__ wave_base, int32_t *__restrict__ blk_count,
+    int32_t *__restrict__ blk_ecount)
+{
+    count_body<NW, kCountBlock>(blockIdx.x, topk_idx, rank_mask, T, K, E, R, epr, epr_shift, nW,
+                                wave_mask, wave_base, blk_count, blk_ecount);
 }
 
 constexpr int kPosBlock = 256;
@@ -294,7 +309,8 @@ __device__ void write_totals(int T, int E, int R, int C, int nB, const int32_t *
                              int32_t *__restrict__ rank_prefix_matrix,
                              int32_t *__restrict__ channel_prefix_matrix,
                              int32_t *__restrict__ recv_channel_prefix_matrix,
-                             int64_t *__restrict__ num_recv, int N, int nthreads)
+                             int64_t *__restrict__ num_recv, int64_t *num_recv_host, int N,
+                             int nthreads)
 {
     const int tid = threadIdx.x;
     for (int r = tid; r < R; r += nthreads) {
@@ -302,8 +318,13 @@ __device__ void write_totals(int T, int E, int R, int C, int nB, const int32_t *
         rank_prefix_matrix[r] = s_seg[r] + s_tot[r];
         recv_channel_prefix_matrix[size_t(r) * C] = 0;
     }
-    if (tid == 0)
+    if (tid == 0) {
         *num_recv = N;
+        // the host copy (pinned, coherent) that a caller waiting for N polls
+        if (num_recv_host != nullptr)
+            __hip_atomic_store(num_recv_host, int64_t(N), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     for (int e = tid; e < E; e += nthreads) {
         int sum = 0;
         for (int b0 = 0; b0 < nB; b0 += kBatch) {
@@ -337,7 +358,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
     const int32_t *__restrict__ blk_ecount, int32_t *__restrict__ num_tokens_per_rank,
     int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ rank_prefix_matrix,
     int32_t *__restrict__ channel_prefix_matrix, int32_t *__restrict__ recv_channel_prefix_matrix,
-    int64_t *__restrict__ num_recv)
+    int64_t *__restrict__ num_recv, int64_t *num_recv_host)
 {
     __shared__ int32_t s_tot[kMaxRanks];
     __shared__ int32_t s_seg[kMaxRanks];
@@ -363,7 +384,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
     __syncthreads();
     write_totals(T, E, R, C, T > 0 ? nB : 0, s_tot, s_seg, blk_ecount, num_tokens_per_rank,
                  num_tokens_per_expert, rank_prefix_matrix, channel_prefix_matrix,
-                 recv_channel_prefix_matrix, num_recv, N, kPosBlock);
+                 recv_channel_prefix_matrix, num_recv, num_recv_host, N, kPosBlock);
 }
 
 // Positions of one 64-token tile, or of a 2^sub_shift-th part of it (small
@@ -381,9 +402,9 @@ __global__ __launch_bounds__(kPosBlock) void layout_scan_kernel(
 // row (send_head, is_token_in_rank).  Finally groups of lanes emit each
 // token's destination rows in ascending rank order, the list the pack and
 // reduce kernels read.
-template <int NW, bool kSelfScan>
-__global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
-    int T, int E, int R, int C, int kmax, int nB, int sub_shift,
+template <int NW, bool kSelfScan, int BC>
+__device__ __forceinline__ void pos_body(
+    int vb, int T, int E, int R, int C, int kmax, int nB, int sub_shift,
     const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
     const int32_t *__restrict__ blk_count, const int32_t *__restrict__ blk_ecount,
     uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
@@ -391,7 +412,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     int32_t *__restrict__ dst_rank, int32_t *__restrict__ num_tokens_per_rank,
     int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ rank_prefix_matrix,
     int32_t *__restrict__ channel_prefix_matrix, int32_t *__restrict__ recv_channel_prefix_matrix,
-    int64_t *__restrict__ num_recv)
+    int64_t *__restrict__ num_recv, int64_t *num_recv_host)
 {
     __shared__ uint64_t s_mask[NW * kWave];
     __shared__ int32_t s_seg[NW * kWave];  // S[r]
@@ -402,10 +423,10 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     const int tid = threadIdx.x;
     // 2^sub_shift workgroups (1, 2 or 4) share a tile, sub_tok tokens each
     // (powers of two throughout: shifts and masks, no integer division)
-    const int wg = blockIdx.x >> sub_shift;  // the 64-token tile
-    const int sub = blockIdx.x & ((1 << sub_shift) - 1);
+    const int wg = vb >> sub_shift;  // the 64-token tile
+    const int sub = vb & ((1 << sub_shift) - 1);
     const int sub_tok = kWave >> sub_shift;
-    const int blk = wg / (kCountBlock / kWave);
+    const int blk = wg / (BC / kWave);  // its count block
     const int64_t t0 = int64_t(wg) * kWave;
     const int ntok = int(T - t0 < kWave ? T - t0 : kWave);
     // this workgroup's tokens of the tile: [lo, hi)
@@ -452,7 +473,7 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
         if (wg == 0 && sub == 0)
             write_totals(T, E, R, C, nB, s_tot, s_seg, blk_ecount, num_tokens_per_rank,
                          num_tokens_per_expert, rank_prefix_matrix, channel_prefix_matrix,
-                         recv_channel_prefix_matrix, num_recv, N, kPosBlock);
+                         recv_channel_prefix_matrix, num_recv, num_recv_host, N, kPosBlock);
     } else {
         for (int r = tid; r < R; r += kPosBlock)
             s_seg[r] = r > 0 ? rank_prefix_matrix[r - 1] : 0;
@@ -564,6 +585,105 @@ __global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
     }
 }
 
+template <int NW, bool kSelfScan>
+__global__ __launch_bounds__(kPosBlock) void layout_pos_kernel(
+    int T, int E, int R, int C, int kmax, int nB, int sub_shift,
+    const uint64_t *__restrict__ wave_mask, const int32_t *__restrict__ wave_base,
+    const int32_t *__restrict__ blk_count, const int32_t *__restrict__ blk_ecount,
+    uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
+    int32_t *__restrict__ recv_src_idx, int32_t *__restrict__ dst_row,
+    int32_t *__restrict__ dst_rank, int32_t *__restrict__ num_tokens_per_rank,
+    int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ rank_prefix_matrix,
+    int32_t *__restrict__ channel_prefix_matrix, int32_t *__restrict__ recv_channel_prefix_matrix,
+    int64_t *__restrict__ num_recv, int64_t *num_recv_host)
+{
+    pos_body<NW, kSelfScan, kCountBlock>(
+        blockIdx.x, T, E, R, C, kmax, nB, sub_shift, wave_mask, wave_base, blk_count, blk_ecount,
+        is_token_in_rank, send_head, recv_src_idx, dst_row, dst_rank, num_tokens_per_rank,
+        num_tokens_per_expert, rank_prefix_matrix, channel_prefix_matrix,
+        recv_channel_prefix_matrix, num_recv, num_recv_host);
+}
+
+// One-launch layout for up to kSelfScanBlocks count blocks of kFusedCount
+// tokens.  Every workgroup first takes a ticket from a counter in the
+// handle's arena: the first nB tickets of this launch are count units, the
+// rest position units, so work is handed out in the order workgroups start,
+// whatever order the hardware starts them in.  A count unit publishes its
+// block (one device-scope release) and bumps the done counter; a position
+// unit polls that counter with relaxed loads (an acquire at every poll would
+// invalidate this XCD's L2 under the count units still running) until all
+// nB count units of this launch are done, then takes one device-scope
+// acquire and runs as layout_pos_kernel would.  Count units never wait, and
+// a ticket is only taken by a workgroup that is running, so the wait always
+// ends however few workgroups fit on the chip at once.  (A bound on the
+// wait, seconds, far beyond any real layout, sets a sticky flag and skips
+// the unit's writes rather than hang.)
+// The counters only grow: the host keeps, per arena, how many tickets and
+// done marks earlier launches used and passes those bases in, so nothing
+// has to reset them (and no workgroup has to fence on its way out).
+constexpr int kFusedCount = 256;  // tokens (and threads) of a fused count unit
+constexpr unsigned kFusedMaxPolls = 1u << 22;
+
+template <int NW>
+__global__ __launch_bounds__(kPosBlock) void layout_fused_kernel(
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
+    int E, int R, int C, int epr, int epr_shift, int kmax, int nW, int nB, int sub_shift,
+    uint64_t *__restrict__ ctr, uint64_t ticket_base, uint64_t done_base,
+    uint64_t *__restrict__ wave_mask, int32_t *__restrict__ wave_base,
+    int32_t *__restrict__ blk_count, int32_t *__restrict__ blk_ecount,
+    uint8_t *__restrict__ is_token_in_rank, int32_t *__restrict__ send_head,
+    int32_t *__restrict__ recv_src_idx, int32_t *__restrict__ dst_row,
+    int32_t *__restrict__ dst_rank, int32_t *__restrict__ num_tokens_per_rank,
+    int32_t *__restrict__ num_tokens_per_expert, int32_t *__restrict__ rank_prefix_matrix,
+    int32_t *__restrict__ channel_prefix_matrix, int32_t *__restrict__ recv_channel_prefix_matrix,
+    int64_t *__restrict__ num_recv, int64_t *num_recv_host)
+{
+    static_assert(kFusedCount == kPosBlock, "one workgroup shape for both unit kinds");
+    __shared__ int s_ticket;
+    __shared__ int s_ready;
+    const int tid = threadIdx.x;
+    if (tid == 0)
+        s_ticket = int(__hip_atomic_fetch_add(&ctr[0], uint64_t(1), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) -
+                       ticket_base);
+    __syncthreads();
+    const int ticket = s_ticket;
+    if (ticket < nB) {
+        count_body<NW, kFusedCount>(ticket, topk_idx, rank_mask, T, K, E, R, epr, epr_shift, nW,
+                                    wave_mask, wave_base, blk_count, blk_ecount);
+        __syncthreads();  // every wave's stores have reached L2
+        if (tid == 0)
+            __hip_atomic_fetch_add(&ctr[1], uint64_t(1), __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    } else if (ticket < int(gridDim.x)) {
+        if (tid == 0) {
+            unsigned polls = 0;
+            int ready = 1;
+            while (__hip_atomic_load(&ctr[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                       done_base <
+                   uint64_t(nB)) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++polls == kFusedMaxPolls) {
+                    __hip_atomic_store(&ctr[3], uint64_t(1), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    ready = 0;
+                    break;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_ready = ready;
+        }
+        __syncthreads();
+        // without all counts the positions could point anywhere: write none
+        if (s_ready)
+            pos_body<NW, true, kFusedCount>(
+                ticket - nB, T, E, R, C, kmax, nB, sub_shift, wave_mask, wave_base, blk_count,
+                blk_ecount, is_token_in_rank, send_head, recv_src_idx, dst_row, dst_rank,
+                num_tokens_per_rank, num_tokens_per_expert, rank_prefix_matrix,
+                channel_prefix_matrix, recv_channel_prefix_matrix, num_recv, num_recv_host);
+    }
+}
+
 // log2 of the workgroups per tile of the position kernel: a small grid
 // leaves most of the chip idle, so its tiles are split (each part repeats
 // the tile's cheap per-rank setup); a grid that already fills the chip is not.
@@ -577,9 +697,28 @@ int pos_split_shift(int nW)
 
 template <int NW>
 hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
-                            const int32_t *rank_mask, const LayoutBufs &b, hipStream_t stream)
+                            const int32_t *rank_mask, const LayoutBufs &b,
+                            int64_t *num_recv_host, LayoutCounters &lc, hipStream_t stream)
 {
     const int epr_shift = (s.epr & (s.epr - 1)) == 0 ? __builtin_ctz(unsigned(s.epr)) : -1;
+    const int sub_shift = pos_split_shift(s.nW);
+    if (s.fused) {
+        const unsigned grid = unsigned(s.nB) + (unsigned(s.nW) << sub_shift);
+        hipLaunchKernelGGL(layout_fused_kernel<NW>, dim3(grid), dim3(kPosBlock),
+                           size_t(s.E) * sizeof(int32_t), stream, topk_idx, rank_mask, s.T, s.K,
+                           s.E, s.R, s.C, s.epr, epr_shift, s.kmax, s.nW, s.nB, sub_shift,
+                           b.layout_ctr, lc.tickets, lc.done, b.wave_mask, b.wave_base,
+                           b.blk_count, b.blk_ecount, b.is_token_in_rank, b.send_head,
+                           b.recv_src_idx, b.dst_row, b.dst_rank, b.num_tokens_per_rank,
+                           b.num_tokens_per_expert, b.rank_prefix_matrix, b.channel_prefix_matrix,
+                           b.recv_channel_prefix_matrix, b.num_recv, num_recv_host);
+        const hipError_t e = hipGetLastError();
+        if (e == hipSuccess) {
+            lc.tickets += grid;
+            lc.done += unsigned(s.nB);
+        }
+        return e;
+    }
     if (s.T > 0)
         hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(s.nB), dim3(kCountBlock),
                            size_t(s.E) * sizeof(int32_t), stream, topk_idx, rank_mask, s.T, s.K, s.E, s.R,
@@ -590,20 +729,29 @@ hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
         hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kPosBlock), 0, stream, s.T, s.E, s.R,
                            s.C, s.nB, b.blk_count, b.blk_ecount, b.num_tokens_per_rank,
                            b.num_tokens_per_expert, b.rank_prefix_matrix, b.channel_prefix_matrix,
-                           b.recv_channel_prefix_matrix, b.num_recv);
+                           b.recv_channel_prefix_matrix, b.num_recv, num_recv_host);
     auto pos_kernel = self_scan ? layout_pos_kernel<NW, true> : layout_pos_kernel<NW, false>;
-    const int sub_shift = pos_split_shift(s.nW);
     if (s.T > 0)
         hipLaunchKernelGGL(pos_kernel, dim3(unsigned(s.nW) << sub_shift), dim3(kPosBlock), 0, stream,
                            s.T, s.E, s.R, s.C, s.kmax, s.nB, sub_shift, b.wave_mask, b.wave_base, b.blk_count,
                            b.blk_ecount, b.is_token_in_rank, b.send_head, b.recv_src_idx,
                            b.dst_row, b.dst_rank, b.num_tokens_per_rank, b.num_tokens_per_expert,
                            b.rank_prefix_matrix, b.channel_prefix_matrix,
-                           b.recv_channel_prefix_matrix, b.num_recv);
+                           b.recv_channel_prefix_matrix, b.num_recv, num_recv_host);
     return hipGetLastError();
 }
 
+std::atomic<int> g_layout_mode{0};  // 0 automatic (= 1), 1 two kernels, 2 one launch when it fits
+
 }  // namespace
+
+bool set_layout_tuning(int mode)
+{
+    if (mode < 0 || mode > 2)
+        return false;
+    g_layout_mode = mode;
+    return true;
+}
 
 LayoutShape layout_shape(const ep_dims &d)
 {
@@ -616,7 +764,13 @@ LayoutShape layout_shape(const ep_dims &d)
     s.epr = s.E / s.R;
     s.kmax = s.K < s.R ? s.K : s.R;
     s.nW = (s.T + kWave - 1) / kWave;
-    s.nB = s.T > 0 ? (s.T + kCountBlock - 1) / kCountBlock : 1;
+    // One launch only when asked for (and while its position units can sum
+    // all count blocks themselves): its grid-wide wait costs more than the
+    // second launch it saves (13.4 against 4.2 + 5.9 us at 4096 tokens).
+    const int64_t fused_blocks = (int64_t(s.T) + kFusedCount - 1) / kFusedCount;
+    s.fused = g_layout_mode.load() == 2 && s.T > 0 && fused_blocks <= kSelfScanBlocks;
+    const int cb = s.fused ? kFusedCount : kCountBlock;
+    s.nB = s.T > 0 ? (s.T + cb - 1) / cb : 1;
     return s;
 }
 
@@ -624,10 +778,12 @@ size_t layout_arena_bytes(const LayoutShape &s, size_t off[kArenaFields])
 {
     const size_t T = size_t(s.T), R = size_t(s.R), E = size_t(s.E), C = size_t(s.C);
     const size_t km = size_t(s.kmax), nW = size_t(s.nW), nB = size_t(s.nB);
+    // field 0, the one-launch layout's counters, is first so that it sits at
+    // the same place for every shape that reuses the arena
     const size_t sizes[kArenaFields] = {
-        R * 4,      E * 4,      T * R,      R * 4,      R * C * 4,  R * C * 4,  T * R * 4,
-        T * km * 4, T * km * 4, T * km * 4, nW * R * 8, nW * R * 4, nB * R * 4, nB * E * 4, 8,
-        16,
+        kLayoutCtrBytes, R * 4,      E * 4,      T * R,      R * 4,      R * C * 4,
+        R * C * 4,       T * R * 4,  T * km * 4, T * km * 4, T * km * 4, nW * R * 8,
+        nW * R * 4,      nB * R * 4, nB * E * 4, 8,          16,
     };
     size_t cur = 0;
     for (int i = 0; i < kArenaFields; ++i) {
@@ -641,41 +797,44 @@ LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields])
 {
     char *p = static_cast<char *>(base);
     LayoutBufs b;
-    b.num_tokens_per_rank = reinterpret_cast<int32_t *>(p + off[0]);
-    b.num_tokens_per_expert = reinterpret_cast<int32_t *>(p + off[1]);
-    b.is_token_in_rank = reinterpret_cast<uint8_t *>(p + off[2]);
-    b.rank_prefix_matrix = reinterpret_cast<int32_t *>(p + off[3]);
-    b.channel_prefix_matrix = reinterpret_cast<int32_t *>(p + off[4]);
-    b.recv_channel_prefix_matrix = reinterpret_cast<int32_t *>(p + off[5]);
-    b.send_head = reinterpret_cast<int32_t *>(p + off[6]);
-    b.recv_src_idx = reinterpret_cast<int32_t *>(p + off[7]);
-    b.dst_row = reinterpret_cast<int32_t *>(p + off[8]);
-    b.dst_rank = reinterpret_cast<int32_t *>(p + off[9]);
-    b.wave_mask = reinterpret_cast<uint64_t *>(p + off[10]);
-    b.wave_base = reinterpret_cast<int32_t *>(p + off[11]);
-    b.blk_count = reinterpret_cast<int32_t *>(p + off[12]);
-    b.blk_ecount = reinterpret_cast<int32_t *>(p + off[13]);
-    b.num_recv = reinterpret_cast<int64_t *>(p + off[14]);
-    b.topk_hash = reinterpret_cast<uint64_t *>(p + off[15]);
+    b.layout_ctr = reinterpret_cast<uint64_t *>(p + off[0]);
+    b.num_tokens_per_rank = reinterpret_cast<int32_t *>(p + off[1]);
+    b.num_tokens_per_expert = reinterpret_cast<int32_t *>(p + off[2]);
+    b.is_token_in_rank = reinterpret_cast<uint8_t *>(p + off[3]);
+    b.rank_prefix_matrix = reinterpret_cast<int32_t *>(p + off[4]);
+    b.channel_prefix_matrix = reinterpret_cast<int32_t *>(p + off[5]);
+    b.recv_channel_prefix_matrix = reinterpret_cast<int32_t *>(p + off[6]);
+    b.send_head = reinterpret_cast<int32_t *>(p + off[7]);
+    b.recv_src_idx = reinterpret_cast<int32_t *>(p + off[8]);
+    b.dst_row = reinterpret_cast<int32_t *>(p + off[9]);
+    b.dst_rank = reinterpret_cast<int32_t *>(p + off[10]);
+    b.wave_mask = reinterpret_cast<uint64_t *>(p + off[11]);
+    b.wave_base = reinterpret_cast<int32_t *>(p + off[12]);
+    b.blk_count = reinterpret_cast<int32_t *>(p + off[13]);
+    b.blk_ecount = reinterpret_cast<int32_t *>(p + off[14]);
+    b.num_recv = reinterpret_cast<int64_t *>(p + off[15]);
+    b.topk_hash = reinterpret_cast<uint64_t *>(p + off[16]);
     return b;
 }
 
 hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const int32_t *rank_mask,
-                         const LayoutBufs &b, hipStream_t stream)
+                         const LayoutBufs &b, int64_t *num_recv_host, LayoutCounters &lc,
+                         hipStream_t stream)
 {
     if (log_enabled())
-        log_launch("layout T=%d K=%d E=%d R=%d C=%d: count blocks=%d pos blocks=%d%s%s", s.T, s.K,
-                   s.E, s.R, s.C, s.nB, s.nW, s.nB > kSelfScanBlocks ? " +scan" : "",
+        log_launch("layout T=%d K=%d E=%d R=%d C=%d: count blocks=%d pos blocks=%d%s%s%s", s.T,
+                   s.K, s.E, s.R, s.C, s.nB, s.nW, s.fused ? " one-launch" : "",
+                   !s.fused && s.nB > kSelfScanBlocks ? " +scan" : "",
                    rank_mask != nullptr ? " +mask" : "");
     switch ((s.R + kWave - 1) / kWave) {
-    case 1: return launch_layout_nw<1>(s, topk_idx, rank_mask, b, stream);
-    case 2: return launch_layout_nw<2>(s, topk_idx, rank_mask, b, stream);
-    case 3: return launch_layout_nw<3>(s, topk_idx, rank_mask, b, stream);
-    case 4: return launch_layout_nw<4>(s, topk_idx, rank_mask, b, stream);
+    case 1: return launch_layout_nw<1>(s, topk_idx, rank_mask, b, num_recv_host, lc, stream);
+    case 2: return launch_layout_nw<2>(s, topk_idx, rank_mask, b, num_recv_host, lc, stream);
+    case 3: return launch_layout_nw<3>(s, topk_idx, rank_mask, b, num_recv_host, lc, stream);
+    case 4: return launch_layout_nw<4>(s, topk_idx, rank_mask, b, num_recv_host, lc, stream);
     case 5:
-    case 6: return launch_layout_nw<6>(s, topk_idx, rank_mask, b, stream);
+    case 6: return launch_layout_nw<6>(s, topk_idx, rank_mask, b, num_recv_host, lc, stream);
     case 7:
-    case 8: return launch_layout_nw<8>(s, topk_idx, rank_mask, b, stream);
+    case 8: return launch_layout_nw<8>(s, topk_idx, rank_mask, b, num_recv_host, lc, stream);
     default: return hipErrorInvalidValue;
     }
 }

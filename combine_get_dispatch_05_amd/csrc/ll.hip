@@ -6,15 +6,16 @@
 // per-expert counts; low_latency_combine reduces the expert results back to
 // the tokens' positions, weighted by the top-k weights.
 //
-// Dispatch is one fused launch with one workgroup per expert: the workgroup
-// scans the [T][K] table, turns "names my expert" into slots with one
-// block-wide prefix scan (so slots follow (token, slot) order), records the
-// token of each slot, and then copies those token rows into the expert's
-// area [le][r][slot][:] with every lane issuing independent 16-byte loads and
-// stores.  No layout pass, no second launch, no host sync.
+// Dispatch of a decode-sized batch (T*K <= 4096) is one launch: each
+// workgroup owns one slice of one token's row, finds the slots of the
+// token's K pairs (the number of earlier pairs naming the same expert) with
+// wave ballots over top-k ids held in registers, and stores the slice, read
+// once, to the K destination cells [le][r][slot][:].  Larger batches take
+// two launches: a per-expert slot scan, then the same token-major copy.  No
+// layout pass and no host sync either way.
 //
-// Combine: one workgroup per (token, row chunk).  All K cell addresses of the
-// token are resolved once into LDS; each lane then issues its K loads before
+// Combine: one workgroup per (token, row chunk).  Every wave resolves the
+// token's K cell addresses in its first K lanes; each lane then issues its K loads before
 // the fused multiply-adds, which run in ascending slot order from +0.  A rank
 // masked at combine time contributes nothing.
 //
@@ -161,30 +162,136 @@ __device__ __forceinline__ int wave_sum(int v)
     return v;
 }
 
-// One workgroup per expert.  Each thread owns a contiguous chunk of the
-// flattened [T][K] table (held in registers when it is short), counts the
-// pairs naming its expert, and one block-wide exclusive scan of those counts
-// gives every thread the first slot of its chunk, so slots follow (token,
-// slot) order.  The rows are then copied with the (row, vector) pairs spread
-// flat over the block, kUnroll independent 16-byte loads in flight per lane.
-// A masked rank ("Dynamic Rank Masking") takes part in nothing: its experts'
-// pairs get no slot and its counts are 0.
-// kFP8: instead of bf16 rows, each 128-element block of a sent row is scaled
-// by 448 / max(amax, 1e-4) and stored as e4m3 codes, with its scale
-// amax / 448; a 16-lane group handles one block (8 elements per lane).
-// The copy of one expert's rows is split over gridDim.y workgroups; each
-// recomputes the (cheap, cached) slot scan, and only the y = 0 workgroup
-// writes the metadata.
-template <bool kFP8>
-__global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
-    const u32x4 *__restrict__ x, int T, int V, int K, int E, int R, int epr, int S,
-    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask,
-    u32x4 *__restrict__ packed_x, uint2 *__restrict__ packed_q, float *__restrict__ packed_scale,
-    int32_t *__restrict__ packed_count, int32_t *__restrict__ src_info,
-    int32_t *__restrict__ topk_slot)
+// Expert id of one top-k entry: -1 for a masked slot or an id outside [0, E).
+__device__ __forceinline__ int ll_valid_id(int64_t v, int E)
 {
-    constexpr int kHold = 8;
-    __shared__ int32_t s_tok[kMaxLLSlots];
+    return (v >= 0 && v < E) ? int(v) : -1;
+}
+
+// Entry i of the flattened top-k table as ll_valid_id, for i < n; the index
+// is clamped to n - 1 (n >= 1), so the load is unconditional and a batch of
+// these calls keeps all of its loads in flight.  Callers exclude i >= n
+// where they use the value.
+__device__ __forceinline__ int ll_id_at(const int64_t *__restrict__ topk_idx, int i, int n, int E)
+{
+    return ll_valid_id(topk_idx[i < n ? i : n - 1], E);
+}
+
+// Index of cell (le, r, s) of expert e in the [E/R][R][S] receive layout.
+// E * S <= 8192 * 4096, so it fits an int.
+__device__ __forceinline__ int ll_cell(int e, int epr, int R, int S, int s)
+{
+    const int r = e / epr;
+    return ((e - r * epr) * R + r) * S + s;
+}
+
+__device__ __forceinline__ int ll_readlane(int v, int lane)
+{
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+// Packed rows are read again soon (by the expert computation and the
+// combine): plain stores leave them in the caches.  Nontemporal stores made
+// the dispatch 0.3 us faster and the combine after it 2.4 us slower.
+__device__ __forceinline__ void ll_store(u32x4 v, u32x4 *p) { *p = v; }
+
+// This workgroup's slice of token t's row, stored to the cells of the
+// token's K pairs (lane k of every wave holds pair k's cell, -1 for none).
+// bf16: vectors [c0, c1) of the row, the lane's first one already loaded
+// in `first`.  FP8: 128-element blocks [b0, b1), one per 16-lane group (a
+// DPP row, so a block's loop bounds are the same for all of its lanes),
+// each quantized once and stored K times.
+template <bool kFP8, int BT>
+__device__ __forceinline__ void ll_store_slice(const u32x4 *__restrict__ x, int64_t t, int V,
+                                               int K, int cell, u32x4 first, int c0, int c1,
+                                               int b0, int b1, u32x4 *__restrict__ packed_x,
+                                               uint2 *__restrict__ packed_q,
+                                               float *__restrict__ packed_scale)
+{
+    const int tid = threadIdx.x;
+    if (!kFP8) {
+        for (int c = c0 + tid; c < c1; c += BT) {
+            const u32x4 v = c == c0 + tid ? first : x[t * V + c];
+            for (int k = 0; k < K; ++k) {
+                const int ck = ll_readlane(cell, k);
+                if (ck >= 0)
+                    ll_store(v, packed_x + int64_t(ck) * V + c);
+            }
+        }
+    } else {
+        const int nb = V / 16;
+        const int g = tid >> 4;
+        const int l16 = tid & 15;
+        for (int bb = b0 + g; bb < b1; bb += BT / 16) {
+            const u32x4 v = bb == b0 + g ? first : x[t * V + int64_t(bb) * 16 + l16];
+            float amax;
+            const uint2 codes = fp8_block(v, amax);
+            for (int k = 0; k < K; ++k) {
+                const int ck = ll_readlane(cell, k);
+                if (ck >= 0) {
+                    packed_q[int64_t(ck) * V + int64_t(bb) * 16 + l16] = codes;
+                    if (l16 == 0)
+                        packed_scale[int64_t(ck) * nb + bb] = amax / 448.0f;
+                }
+            }
+        }
+    }
+}
+
+// Row slice of workgroup `yb` of ny: vectors [c0, c1) (bf16, about 256
+// vectors) or 128-element blocks [b0, b1) (FP8, about 16 blocks).
+template <bool kFP8>
+__device__ __forceinline__ void ll_slice(int V, int ny, int yb, int &c0, int &c1, int &b0, int &b1)
+{
+    if (!kFP8) {
+        const int per = (V + ny - 1) / ny;
+        c0 = yb * per;
+        c1 = c0 + per < V ? c0 + per : V;
+        b0 = b1 = 0;
+    } else {
+        const int nb = V / 16;
+        const int per = (nb + ny - 1) / ny;
+        b0 = yb * per;
+        b1 = b0 + per < nb ? b0 + per : nb;
+        c0 = c1 = 0;
+    }
+}
+
+// The first vector of this lane's share of the slice (its load does not
+// depend on the slots, so it is issued before they are known).
+template <bool kFP8>
+__device__ __forceinline__ u32x4 ll_first(const u32x4 *__restrict__ x, int64_t t, int V, int c0,
+                                          int c1, int b0, int b1, bool rows)
+{
+    const int tid = threadIdx.x;
+    u32x4 v = {0, 0, 0, 0};
+    if (!kFP8) {
+        if (rows && c0 + tid < c1)
+            v = x[t * V + c0 + tid];
+    } else {
+        if (b0 + (tid >> 4) < b1)
+            v = x[t * V + int64_t(b0 + (tid >> 4)) * 16 + (tid & 15)];
+    }
+    return v;
+}
+
+constexpr int kSlotHold = 32;  // top-k entries a thread of the slot scan keeps in registers
+
+// Slot scan for batches of any size, one workgroup per expert: each thread
+// owns a contiguous chunk of the flattened [T][K] table, counts the pairs
+// naming the workgroup's expert, and one block-wide exclusive scan of those
+// counts gives every thread the first slot of its chunk, so slots follow
+// (token, slot) order.  Writes the expert's count, src_info (-1 in unused
+// cells) and topk_slot of its pairs; workgroup 0 also marks masked and
+// invalid slots.  A masked rank ("Dynamic Rank Masking") takes part in
+// nothing: its experts' pairs get no slot and its counts are 0.  The rows
+// are copied afterwards by ll_copy_kernel, token-major, so each token row is
+// read once.
+__global__ __launch_bounds__(kLLBlock) void ll_slot_kernel(
+    int T, int K, int E, int R, int epr, int S, const int64_t *__restrict__ topk_idx,
+    const int32_t *__restrict__ rank_mask, int32_t *__restrict__ packed_count,
+    int32_t *__restrict__ src_info, int32_t *__restrict__ topk_slot)
+{
     __shared__ int32_t s_wsum[kLLWaves];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -193,25 +300,40 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
     const int le = e % epr;
     const int r = e / epr;
     const bool masked = rank_mask != nullptr && rank_mask[r] != 0;
-    const int64_t cell0 = (int64_t(le) * R + r) * S;
+    const int cell0 = (le * R + r) * S;
     const int TK = T * K;
     const int chunk = (TK + kLLBlock - 1) / kLLBlock;
-    const int i0 = tid * chunk;
+    const int i0 = tid * chunk < TK ? tid * chunk : TK;
     const int i1 = i0 + chunk < TK ? i0 + chunk : TK;
-    const bool held = chunk <= kHold;
+    const bool held = chunk <= kSlotHold;
 
-    int64_t v[kHold];
+    // ids of the chunk: batches of 8 loads in flight
+    int v[kSlotHold];
     int mine = 0;
     if (held) {
 #pragma unroll
-        for (int q = 0; q < kHold; ++q) {
-            v[q] = i0 + q < i1 ? topk_idx[i0 + q] : -1;
-            mine += (v[q] == e && !masked) ? 1 : 0;
+        for (int q0 = 0; q0 < kSlotHold; q0 += 8) {
+            if (q0 < chunk) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    v[q0 + q] = ll_id_at(topk_idx, i0 + q0 + q, i1, E);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    mine += (v[q0 + q] == e && i0 + q0 + q < i1) ? 1 : 0;
+            }
         }
     } else {
-        for (int i = i0; i < i1; ++i)
-            mine += (topk_idx[i] == e && !masked) ? 1 : 0;
+        for (int i = i0; i < i1; i += 8) {
+            int w[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                w[q] = ll_id_at(topk_idx, i + q, i1, E);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                mine += (w[q] == e && i + q < i1) ? 1 : 0;
+        }
     }
+    mine = masked ? 0 : mine;
 
     const int incl = ll_wave_inclusive_scan(mine);
     if (lane == kWave - 1)
@@ -226,361 +348,283 @@ __global__ __launch_bounds__(kLLBlock) void ll_dispatch_kernel(
     }
     int s = before + incl - mine;  // first slot of this thread's chunk
 
-    const bool meta = blockIdx.y == 0;
-    auto place = [&](int i, int64_t val) {
+    auto place = [&](int i, int val) {
         if (val == e) {
             if (!masked && s < S) {
-                if (meta) {
-                    topk_slot[i] = s;
-                    src_info[cell0 + s] = i / K;
-                }
-                s_tok[s] = i / K;
-            } else if (meta) {
+                topk_slot[i] = s;
+                src_info[cell0 + s] = i / K;
+            } else {
                 topk_slot[i] = -1;
             }
             s += masked ? 0 : 1;
-        } else if (meta && e == 0 && !(val >= 0 && val < E)) {
+        } else if (e == 0 && val < 0) {
             topk_slot[i] = -1;  // masked or invalid slots: workgroup 0 marks them
         }
     };
     if (held) {
 #pragma unroll
-        for (int q = 0; q < kHold; ++q)
-            if (i0 + q < i1)
-                place(i0 + q, v[q]);
+        for (int q0 = 0; q0 < kSlotHold; q0 += 8)
+            if (q0 < chunk)
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (i0 + q0 + q < i1)
+                        place(i0 + q0 + q, v[q0 + q]);
     } else {
         for (int i = i0; i < i1; ++i)
-            place(i, topk_idx[i]);
+            place(i, ll_valid_id(topk_idx[i], E));
     }
 
     const int used = total < S ? total : S;
-    if (blockIdx.y == 0) {
-        if (tid == 0)
-            packed_count[int64_t(le) * R + r] = total;
-        for (int q = used + tid; q < S; q += kLLBlock)
-            src_info[cell0 + q] = -1;
-    }
-    __syncthreads();
-    const int ny = gridDim.y, yb = blockIdx.y;
-
-    if (!kFP8 && packed_x != nullptr) {
-        constexpr int kUnroll = 8;
-        const int n = used * V;
-        for (int p0 = yb * kLLBlock * kUnroll; p0 < n; p0 += ny * kLLBlock * kUnroll) {
-            u32x4 buf[kUnroll];
-            int64_t dst[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int p = p0 + u * kLLBlock + tid;
-                dst[u] = -1;
-                if (p < n) {
-                    const int row = p / V;
-                    const int col = p - row * V;
-                    buf[u] = x[int64_t(s_tok[row]) * V + col];
-                    dst[u] = (cell0 + row) * V + col;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                if (dst[u] >= 0)
-                    packed_x[dst[u]] = buf[u];
-        }
-    }
-
-    if (kFP8) {
-        // 16 vectors of 8 bf16 per 128-element block; V is a multiple of 16.
-        // A wave takes 4 blocks per round and kRounds rounds at once, so
-        // kRounds loads are in flight before any block is quantized.  Lanes
-        // past the end load row 0's block (always valid when items > 0) and
-        // store nothing.
-        constexpr int kRounds = 4;
-        const int nb = V / 16;
-        const int items = used * nb;
-        const int g16 = lane >> 4;  // group of 16 lanes inside the wave
-        const int l16 = lane & 15;
-        const int wave = yb * kLLWaves + wid;
-        const int nwaves = ny * kLLWaves;
-        for (int w0 = wave * 4 * kRounds; w0 < items; w0 += nwaves * 4 * kRounds) {
-            u32x4 vv[kRounds];
-            int row[kRounds], blk[kRounds], tok[kRounds];
-#pragma unroll
-            for (int k = 0; k < kRounds; ++k) {
-                const int item = w0 + k * 4 + g16;
-                const int it = item < items ? item : 0;
-                row[k] = item < items ? it / nb : -1;
-                blk[k] = it - (it / nb) * nb;
-                tok[k] = s_tok[it / nb];
-            }
-#pragma unroll
-            for (int k = 0; k < kRounds; ++k)
-                vv[k] = x[int64_t(tok[k]) * V + int64_t(blk[k]) * 16 + l16];
-#pragma unroll
-            for (int k = 0; k < kRounds; ++k) {
-                float amax;
-                const uint2 codes = fp8_block(vv[k], amax);
-                if (row[k] >= 0) {
-                    const int64_t cell = cell0 + row[k];
-                    const int64_t col = int64_t(blk[k]) * 16 + l16;
-                    packed_q[cell * V + col] = codes;  // 8 codes per lane
-                    if (l16 == 0)
-                        packed_scale[cell * nb + blk[k]] = amax / 448.0f;
-                }
-            }
-        }
-    }
+    if (tid == 0)
+        packed_count[le * R + r] = total;
+    for (int q = used + tid; q < S; q += kLLBlock)
+        src_info[cell0 + q] = -1;
 }
 
-constexpr int kLLTokPairs = 4096;  // token-major path for T*K up to this (ids held in LDS)
-constexpr int kSlotChunk = 8;      // a token's experts matched per pass of the slot scan
-
-// Token-major variant for small batches (T*K <= kLLTokPairs), same results
-// as ll_dispatch_kernel.  Every workgroup first loads the whole [T][K] id
-// table into LDS.  Workgroups [0, T*ny) are token workgroups: (t, slice y).
-// The slot of an own pair (t, k) is the number of earlier pairs (in (token,
-// slot) order) that name the same expert: all lanes of the workgroup scan the
-// earlier tokens' pairs once, each entry compared with up to kSlotChunk of
-// the token's experts, the per-lane counts are added up in LDS, and thread k
-// adds the token's own earlier slots.  The slice of x[t] is then read once
-// and stored to all K destination cells (for FP8 each 128-element block is
-// quantized once).  The remaining workgroups handle four experts each (one
-// per wave): the expert's count and the -1 entries of its unused src_info
-// cells.
+// Row copy after ll_slot_kernel, token-major: workgroup (t, slice) reads its
+// slice of x[t] once and stores it to the cells of the token's pairs, which
+// come from topk_slot.
 template <bool kFP8>
-__global__ __launch_bounds__(kLLBlock) void ll_dispatch_tok_kernel(
+__global__ __launch_bounds__(kLLBlock) void ll_copy_kernel(
+    const u32x4 *__restrict__ x, int V, int K, int E, int R, int epr, int S, int ny,
+    const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ topk_slot,
+    u32x4 *__restrict__ packed_x, uint2 *__restrict__ packed_q, float *__restrict__ packed_scale)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = blockIdx.x / ny;
+    const int yb = blockIdx.x - int(t) * ny;
+    int c0, c1, b0, b1;
+    ll_slice<kFP8>(V, ny, yb, c0, c1, b0, b1);
+    const u32x4 first = ll_first<kFP8>(x, t, V, c0, c1, b0, b1, true);
+    int cell = -1;
+    if (lane < K) {
+        const int e = ll_valid_id(topk_idx[t * K + lane], E);
+        const int s = topk_slot[t * K + lane];
+        if (e >= 0 && s >= 0 && s < S)
+            cell = ll_cell(e, epr, R, S, s);
+    }
+    ll_store_slice<kFP8, kLLBlock>(x, t, V, K, cell, first, c0, c1, b0, b1, packed_x, packed_q,
+                                   packed_scale);
+}
+
+constexpr int kLLTokPairs = 4096;  // one-launch path for T*K up to this
+constexpr int kTokBlock = 512;     // threads of a one-launch workgroup
+
+// One-launch dispatch for decode-sized batches (T*K <= kLLTokPairs), same
+// results as ll_slot_kernel + ll_copy_kernel.  Workgroups [0, T*ny) are
+// token workgroups (t, slice).  The slot of pair (t, k) is the number of
+// earlier pairs, in (token, slot) order, that name its expert.  Every thread
+// loads its share of those earlier entries into registers (coalesced; 4 per
+// thread for 1024 pairs); for each k one wave ballot per register gives the
+// wave's matches, and the four waves' counts meet in LDS behind the one
+// barrier.  The slice of x[t] (its first load issued before the barrier) is
+// then stored to all K destination cells; for FP8 each 128-element block is
+// quantized once.  The remaining workgroups handle four experts each (one
+// per wave), counting with the same ballots over the whole table: the
+// expert's count and the -1 entries of its unused src_info cells.
+template <bool kFP8, int BT>
+__global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
     const u32x4 *__restrict__ x, int T, int V, int K, int E, int R, int epr, int S, int ny,
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask,
     u32x4 *__restrict__ packed_x, uint2 *__restrict__ packed_q, float *__restrict__ packed_scale,
     int32_t *__restrict__ packed_count, int32_t *__restrict__ src_info,
     int32_t *__restrict__ topk_slot)
 {
-    __shared__ int32_t s_ids[kLLTokPairs];
-    __shared__ int64_t s_cell[kMaxTopk];
-    __shared__ int32_t s_cnt[kMaxTopk];  // earlier tokens' pairs naming pair k's expert
+    constexpr int kWaves = BT / kWave;
+    constexpr int kHold = kLLTokPairs / BT;  // top-k entries per thread, at most
+    __shared__ int32_t s_part[kMaxTopk][kWaves];  // per-wave match counts
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid >> 6;
     const int TK = T * K;
     const int b = blockIdx.x;
     const int ntok = T * ny;
-    const int t = b / ny;
-    const int yb = b - t * ny;
-
-    // The first vector of this lane's share of the row slice does not depend
-    // on the slots: its load is issued before anything else.
-    int c0 = 0, c1 = 0, b0 = 0, b1 = 0;
-    u32x4 first = {0, 0, 0, 0};
-    if (b < ntok) {
-        if (!kFP8) {
-            const int per = (V + ny - 1) / ny;
-            c0 = yb * per;
-            c1 = c0 + per < V ? c0 + per : V;
-            if (packed_x != nullptr && c0 + tid < c1)
-                first = x[int64_t(t) * V + c0 + tid];
-        } else {
-            const int nb = V / 16;
-            const int per = (nb + ny - 1) / ny;
-            b0 = yb * per;
-            b1 = b0 + per < nb ? b0 + per : nb;
-            if (b0 + (tid >> 4) < b1)
-                first = x[int64_t(t) * V + int64_t(b0 + (tid >> 4)) * 16 + (tid & 15)];
-        }
-    }
-
-    if (tid < kMaxTopk)
-        s_cnt[tid] = 0;
-    // expert id of every pair; -1 for masked slots and invalid ids
-    constexpr int kU = 4;
-    for (int i0 = 0; i0 < TK; i0 += kLLBlock * kU) {
-        int64_t v[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int i = i0 + u * kLLBlock + tid;
-            v[u] = i < TK ? topk_idx[i] : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int i = i0 + u * kLLBlock + tid;
-            if (i < TK)
-                s_ids[i] = (v[u] >= 0 && v[u] < E) ? int(v[u]) : -1;
-        }
-    }
-    __syncthreads();
 
     if (b >= ntok) {
-        const int e = (b - ntok) * kLLWaves + wid;
+        // experts e0 .. e0+3, one per wave: matches over the whole table
+        const int e0 = (b - ntok) * kWaves;
+        int ids[kHold];
+#pragma unroll
+        for (int u0 = 0; u0 < kHold; u0 += 4) {
+            if (u0 * BT < TK) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    ids[u0 + q] = ll_id_at(topk_idx, (u0 + q) * BT + tid, TK, E);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kWaves; ++j) {
+            int c = 0;
+#pragma unroll
+            for (int u = 0; u < kHold; ++u)
+                if (u * BT < TK)
+                    c += __popcll(wave_ballot(ids[u] == e0 + j && u * BT + tid < TK));
+            if (lane == 0)
+                s_part[j][wid] = c;
+        }
+        __syncthreads();
+        const int e = e0 + wid;
         if (e < E) {
             const int r = e / epr;
             const bool masked = rank_mask != nullptr && rank_mask[r] != 0;
             int cnt = 0;
-            if (!masked)
-                for (int i = lane; i < TK; i += kWave)
-                    cnt += s_ids[i] == e ? 1 : 0;
-            cnt = wave_sum(cnt);
-            const int64_t cell0 = (int64_t(e - r * epr) * R + r) * S;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+                cnt += s_part[wid][w];
+            cnt = masked ? 0 : cnt;
+            const int cell0 = ll_cell(e, epr, R, S, 0);
             if (lane == 0)
-                packed_count[int64_t(e - r * epr) * R + r] = cnt;
+                packed_count[(e - r * epr) * R + r] = cnt;
             for (int q = (cnt < S ? cnt : S) + lane; q < S; q += kWave)
                 src_info[cell0 + q] = -1;
         }
         return;
     }
 
-    // Thread k < K owns pair (t, k); its rank-mask load is issued before the
-    // scan so that the scan hides its latency.
+    const int t = b / ny;
+    const int yb = b - t * ny;
     const int base = t * K;
-    int e_mine = -1;
-    bool live_mine = false;
-    if (tid < K) {
-        e_mine = s_ids[base + tid];
-        live_mine = e_mine >= 0 && (rank_mask == nullptr || rank_mask[e_mine / epr] == 0);
+    // lane k < K of every wave: the expert of pair (t, k)
+    int own = -1;
+    if (lane < K)
+        own = ll_valid_id(topk_idx[base + lane], E);
+    // entries that can precede one of the token's pairs: i < base + K - 1
+    // (the count below takes entries i < base + k only, so i >= lim never
+    // counts)
+    const int lim = base + K - 1;
+    int ids[kHold];
+#pragma unroll
+    for (int u0 = 0; u0 < kHold; u0 += 4) {
+        if (u0 * BT < lim) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                ids[u0 + q] = ll_id_at(topk_idx, (u0 + q) * BT + tid, lim, E);
+        }
     }
-    // An expert occurs only a few times among the earlier pairs, so the few
-    // nonzero per-lane counts go to LDS with atomic adds.
-    for (int k0 = 0; k0 < K; k0 += kSlotChunk) {
-        int ek[kSlotChunk], c[kSlotChunk];
+    // the row slice's first load, after the table loads so that waiting for
+    // those does not wait for it
+    int c0, c1, b0, b1;
+    ll_slice<kFP8>(V, ny, yb, c0, c1, b0, b1);
+    const u32x4 first = ll_first<kFP8>(x, t, V, c0, c1, b0, b1, packed_x != nullptr);
+    bool live = own >= 0;
+    if (rank_mask != nullptr && live)
+        live = rank_mask[own / epr] == 0;
+
+    for (int k = 0; k < K; ++k) {
+        const int ek = ll_readlane(own, k);
+        int c = 0;
+        if (ek >= 0) {
+            const int lk = base + k;  // entries before pair (t, k)
 #pragma unroll
-        for (int q = 0; q < kSlotChunk; ++q) {
-            ek[q] = k0 + q < K ? s_ids[base + k0 + q] : -2;  // -2 matches no entry
-            c[q] = 0;
+            for (int u = 0; u < kHold; ++u)
+                if (u * BT < lim)
+                    c += __popcll(wave_ballot(ids[u] == ek && u * BT + tid < lk));
         }
-        for (int i = tid; i < base; i += kLLBlock) {
-            const int v = s_ids[i];
-#pragma unroll
-            for (int q = 0; q < kSlotChunk; ++q)
-                c[q] += v == ek[q] ? 1 : 0;
-        }
-#pragma unroll
-        for (int q = 0; q < kSlotChunk; ++q)
-            if (c[q] != 0)
-                atomicAdd(&s_cnt[k0 + q], c[q]);
+        if (lane == 0)
+            s_part[k][wid] = c;
     }
     __syncthreads();
-    if (tid < K) {
-        int64_t cell = -1;
-        int slot = -1;
-        if (live_mine) {
-            int cnt = s_cnt[tid];
-            for (int j = 0; j < tid; ++j)
-                cnt += s_ids[base + j] == e_mine ? 1 : 0;
-            if (cnt < S) {
-                const int r = e_mine / epr;
-                slot = cnt;
-                cell = (int64_t(e_mine - r * epr) * R + r) * S + cnt;
-            }
-        }
-        s_cell[tid] = cell;
-        if (yb == 0) {
-            topk_slot[base + tid] = slot;
-            if (cell >= 0)
-                src_info[cell] = t;
+
+    int cell = -1, slot = -1;
+    if (lane < K && live) {
+        int cnt = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            cnt += s_part[lane][w];
+        if (cnt < S) {
+            slot = cnt;
+            cell = ll_cell(own, epr, R, S, cnt);
         }
     }
-    __syncthreads();  // s_cell is read by the copy below
+    if (yb == 0 && wid == 0 && lane < K) {
+        topk_slot[base + lane] = slot;
+        if (cell >= 0)
+            src_info[cell] = t;
+    }
+    if (!kFP8 && packed_x == nullptr)
+        return;
+    ll_store_slice<kFP8, BT>(x, t, V, K, cell, first, c0, c1, b0, b1, packed_x, packed_q,
+                             packed_scale);
+}
 
-    if (!kFP8) {
-        if (packed_x == nullptr)
-            return;
-        for (int c = c0 + tid; c < c1; c += kLLBlock) {
-            const u32x4 v = c == c0 + tid ? first : x[int64_t(t) * V + c];
-            for (int k = 0; k < K; ++k) {
-                const int64_t cell = s_cell[k];
-                if (cell >= 0)
-                    packed_x[cell * V + c] = v;
-            }
-        }
-    } else {
-        // 16 lane groups, one 128-element block each; a group is a DPP row,
-        // and a block's loop bounds are the same for all of its lanes.
-        const int nb = V / 16;
-        const int g = tid >> 4;
-        const int l16 = tid & 15;
-        for (int bb = b0 + g; bb < b1; bb += kLLBlock / 16) {
-            const u32x4 v = bb == b0 + g ? first : x[int64_t(t) * V + int64_t(bb) * 16 + l16];
-            float amax;
-            const uint2 codes = fp8_block(v, amax);
-            for (int k = 0; k < K; ++k) {
-                const int64_t cell = s_cell[k];
-                if (cell >= 0) {
-                    packed_q[cell * V + int64_t(bb) * 16 + l16] = codes;
-                    if (l16 == 0)
-                        packed_scale[cell * nb + bb] = amax / 448.0f;
-                }
-            }
-        }
+// Packed rows are read once by the combine.
+__device__ __forceinline__ u32x4 ll_load_row(const u32x4 *p) { return *p; }
+
+// The pairs' cells and weights for the combines: lane k < K of every wave
+// holds pair (t, k)'s cell (-1: masked, dropped, or on a rank masked now)
+// and its weight.
+__device__ __forceinline__ void ll_pair_cells(int64_t t, int K, int E, int R, int epr, int S,
+                                              const int64_t *__restrict__ topk_idx,
+                                              const float *__restrict__ topk_weights,
+                                              const int32_t *__restrict__ topk_slot,
+                                              const int32_t *__restrict__ rank_mask, int &cell,
+                                              float &w)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    cell = -1;
+    w = 0.0f;
+    if (lane < K) {
+        const int e = ll_valid_id(topk_idx[t * K + lane], E);
+        const int s = topk_slot[t * K + lane];
+        w = topk_weights[t * K + lane];
+        bool ok = e >= 0 && s >= 0 && s < S;
+        if (ok && rank_mask != nullptr)
+            ok = rank_mask[e / epr] == 0;
+        cell = ok ? ll_cell(e, epr, R, S, s) : -1;
     }
 }
 
-template <int VPT>
-__global__ __launch_bounds__(kLLBlock) void ll_combine_kernel(
+// One workgroup per (token, chunk of 256 vectors).  Each wave resolves the
+// token's K cells itself (lanes 0..K-1, no LDS, no barrier); each lane then
+// issues its K loads before the fused multiply-adds, which run in ascending
+// slot order from +0.
+constexpr int kCombBlock = 256;  // threads of a combine workgroup (one 16-byte vector each)
+
+template <int BT>
+__global__ __launch_bounds__(BT) void ll_combine_kernel(
     const u32x4 *__restrict__ packed_y, int V, int K, int E, int R, int epr, int S,
     const int64_t *__restrict__ topk_idx, const float *__restrict__ topk_weights,
     const int32_t *__restrict__ topk_slot, const int32_t *__restrict__ rank_mask,
     u32x4 *__restrict__ out)
 {
-    __shared__ int64_t s_cell[kMaxTopk];
-    __shared__ float s_w[kMaxTopk];
-    const int tid = threadIdx.x;
     const int64_t t = blockIdx.x;
-    if (tid < K) {
-        const int64_t e = topk_idx[t * K + tid];
-        const int s = topk_slot[t * K + tid];
-        const bool ok = e >= 0 && e < E && s >= 0 && s < S &&
-                        !(rank_mask != nullptr && rank_mask[int(e) / epr] != 0);
-        s_cell[tid] = ok ? ((int64_t(int(e) % epr) * R + int(e) / epr) * S + s) : -1;
-        s_w[tid] = topk_weights[t * K + tid];
-    }
-    __syncthreads();
-
-    const int base = blockIdx.y * kLLBlock * VPT;
-    float acc[VPT][8];
+    int cell;
+    float w;
+    ll_pair_cells(t, K, E, R, epr, S, topk_idx, topk_weights, topk_slot, rank_mask, cell, w);
+    const int idx = blockIdx.y * BT + threadIdx.x;
+    float acc[8];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i)
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            acc[i][q] = 0.0f;
+    for (int q = 0; q < 8; ++q)
+        acc[q] = 0.0f;
 
     constexpr int kGroup = 8;
     for (int k0 = 0; k0 < K; k0 += kGroup) {
-        u32x4 v[kGroup][VPT];
+        u32x4 v[kGroup];
+        int ck[kGroup];
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
-            const int k = k0 + g;
-            const int64_t cell = k < K ? s_cell[k] : -1;
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int idx = base + i * kLLBlock + tid;
-                v[g][i] = (cell >= 0 && idx < V) ? packed_y[cell * V + idx] : u32x4{0, 0, 0, 0};
-            }
+            ck[g] = k0 + g < K ? ll_readlane(cell, k0 + g) : -1;
+            v[g] = (ck[g] >= 0 && idx < V) ? ll_load_row(packed_y + int64_t(ck[g]) * V + idx)
+                                           : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
-            const int k = k0 + g;
-            if (k < K && s_cell[k] >= 0) {
-                const float w = s_w[k];
+            if (ck[g] >= 0) {
+                const float wk = __int_as_float(ll_readlane(__float_as_int(w), k0 + g));
 #pragma unroll
-                for (int i = 0; i < VPT; ++i) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[i][2 * q] = __builtin_fmaf(w, bf16_lo(v[g][i][q]), acc[i][2 * q]);
-                        acc[i][2 * q + 1] =
-                            __builtin_fmaf(w, bf16_hi(v[g][i][q]), acc[i][2 * q + 1]);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = __builtin_fmaf(wk, bf16_lo(v[g][q]), acc[2 * q]);
+                    acc[2 * q + 1] = __builtin_fmaf(wk, bf16_hi(v[g][q]), acc[2 * q + 1]);
                 }
             }
         }
     }
-
-    u32x4 *o = out + t * V;
+    if (idx < V) {
+        u32x4 rv;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-        const int idx = base + i * kLLBlock + tid;
-        if (idx < V) {
-            u32x4 rv;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                rv[q] = pack_bf16x2(acc[i][2 * q], acc[i][2 * q + 1]);
-            o[idx] = rv;
-        }
+        for (int q = 0; q < 4; ++q)
+            rv[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        out[t * V + idx] = rv;
     }
 }
 
@@ -596,22 +640,12 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_fp8_kernel(
     const float *__restrict__ topk_weights, const int32_t *__restrict__ topk_slot,
     const int32_t *__restrict__ rank_mask, u32x4 *__restrict__ out)
 {
-    __shared__ int64_t s_cell[kMaxTopk];
-    __shared__ float s_w[kMaxTopk];
-    const int tid = threadIdx.x;
     const int64_t t = blockIdx.x;
-    if (tid < K) {
-        const int64_t e = topk_idx[t * K + tid];
-        const int s = topk_slot[t * K + tid];
-        const bool ok = e >= 0 && e < E && s >= 0 && s < S &&
-                        !(rank_mask != nullptr && rank_mask[int(e) / epr] != 0);
-        s_cell[tid] = ok ? ((int64_t(int(e) % epr) * R + int(e) / epr) * S + s) : -1;
-        s_w[tid] = topk_weights[t * K + tid];
-    }
-    __syncthreads();
-
-    const int idx = blockIdx.y * kLLBlock + tid;  // 8-element group of the row
-    const int nb = V / 16;                          // 128-element blocks per row
+    int cell;
+    float w;
+    ll_pair_cells(t, K, E, R, epr, S, topk_idx, topk_weights, topk_slot, rank_mask, cell, w);
+    const int idx = blockIdx.y * kLLBlock + threadIdx.x;  // 8-element group of the row
+    const int nb = V / 16;                                 // 128-element blocks per row
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -621,28 +655,27 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_fp8_kernel(
     for (int k0 = 0; k0 < K; k0 += kGroup) {
         uint2 c[kGroup];
         float sc[kGroup];
+        int ck[kGroup];
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
-            const int k = k0 + g;
-            const int64_t cell = k < K ? s_cell[k] : -1;
-            const bool live = cell >= 0 && idx < V;
-            c[g] = live ? packed_q[cell * V + idx] : make_uint2(0, 0);
-            sc[g] = live ? packed_scale[cell * nb + idx / 16] : 0.0f;
+            ck[g] = k0 + g < K ? ll_readlane(cell, k0 + g) : -1;
+            const bool live = ck[g] >= 0 && idx < V;
+            c[g] = live ? packed_q[int64_t(ck[g]) * V + idx] : make_uint2(0, 0);
+            sc[g] = live ? packed_scale[int64_t(ck[g]) * nb + idx / 16] : 0.0f;
         }
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
-            const int k = k0 + g;
-            if (k < K && s_cell[k] >= 0) {
-                const float w = s_w[k];
+            if (ck[g] >= 0) {
+                const float wk = __int_as_float(ll_readlane(__float_as_int(w), k0 + g));
                 const uint32_t words[2] = {c[g].x, c[g].y};
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(int(words[h]), false);
                     const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(int(words[h]), true);
-                    acc[4 * h + 0] = __builtin_fmaf(w, d01[0] * sc[g], acc[4 * h + 0]);
-                    acc[4 * h + 1] = __builtin_fmaf(w, d01[1] * sc[g], acc[4 * h + 1]);
-                    acc[4 * h + 2] = __builtin_fmaf(w, d23[0] * sc[g], acc[4 * h + 2]);
-                    acc[4 * h + 3] = __builtin_fmaf(w, d23[1] * sc[g], acc[4 * h + 3]);
+                    acc[4 * h + 0] = __builtin_fmaf(wk, d01[0] * sc[g], acc[4 * h + 0]);
+                    acc[4 * h + 1] = __builtin_fmaf(wk, d01[1] * sc[g], acc[4 * h + 1]);
+                    acc[4 * h + 2] = __builtin_fmaf(wk, d23[0] * sc[g], acc[4 * h + 2]);
+                    acc[4 * h + 3] = __builtin_fmaf(wk, d23[1] * sc[g], acc[4 * h + 3]);
                 }
             }
         }
@@ -656,7 +689,7 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_fp8_kernel(
     }
 }
 
-std::atomic<int> g_ll_mode{0};  // 0 automatic, 1 expert-major, 2 token-major when it fits
+std::atomic<int> g_ll_mode{0};  // 0 automatic, 1 slot scan + copy, 2 one launch when it fits
 
 }  // namespace
 
@@ -668,50 +701,55 @@ bool set_ll_tuning(int mode)
     return true;
 }
 
+// Row slices per token for workgroups of bt threads: about bt vectors
+// (bf16) or bt / 16 blocks (fp8) each, one per lane or 16-lane group.
+int ll_slices(int V, bool fp8, bool rows, int bt)
+{
+    if (!rows)
+        return 1;
+    return fp8 ? (V / 16 + bt / 16 - 1) / (bt / 16) : (V + bt - 1) / bt;
+}
+
 hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
                               const int64_t *topk_idx, const int32_t *rank_mask, void *packed_x,
                               void *packed_q, float *packed_scale, int32_t *packed_count,
                               int32_t *src_info, int32_t *topk_slot, hipStream_t stream)
 {
-    const int E = d.num_experts, R = d.num_ranks;
+    const int T = d.num_tokens, K = d.num_topk, E = d.num_experts, R = d.num_ranks;
+    const int V = d.hidden / 8;
     const bool fp8 = packed_q != nullptr;
-    const int64_t TK = int64_t(d.num_tokens) * d.num_topk;
+    const bool rows = fp8 || packed_x != nullptr;
+    const int64_t TK = int64_t(T) * K;
     if (g_ll_mode.load() != 1 && TK <= kLLTokPairs) {
-        // token-major: slices of about 256 vectors (bf16) or 16 blocks (fp8)
-        const int V = d.hidden / 8;
-        const bool rows = fp8 || packed_x != nullptr;
-        int ny = 1;
-        if (rows)
-            ny = fp8 ? (V / 16 + 15) / 16 : (V + kLLBlock - 1) / kLLBlock;
-        const int64_t blocks = int64_t(d.num_tokens) * ny + (E + kLLWaves - 1) / kLLWaves;
+        constexpr int BT = kTokBlock;
+        const int ny = ll_slices(V, fp8, rows, BT);
+        const int64_t blocks = int64_t(T) * ny + (E + BT / kWave - 1) / (BT / kWave);
         if (log_enabled())
-            log_launch("ll_dispatch token-major T=%d H=%d K=%d E=%d: slices=%d blocks=%lld%s",
-                       d.num_tokens, d.hidden, d.num_topk, E, ny, (long long)blocks,
-                       fp8 ? " fp8" : "");
-        auto tk = fp8 ? ll_dispatch_tok_kernel<true> : ll_dispatch_tok_kernel<false>;
-        hipLaunchKernelGGL(tk, dim3(unsigned(blocks)), dim3(kLLBlock), 0, stream,
-                           static_cast<const u32x4 *>(x), d.num_tokens, V, d.num_topk, E, R,
-                           E / R, num_slots, ny, topk_idx, rank_mask,
-                           static_cast<u32x4 *>(packed_x), static_cast<uint2 *>(packed_q),
-                           packed_scale, packed_count, src_info, topk_slot);
+            log_launch("ll_dispatch one-launch T=%d H=%d K=%d E=%d: slices=%d blocks=%lld%s", T,
+                       d.hidden, K, E, ny, (long long)blocks, fp8 ? " fp8" : "");
+        auto tk = fp8 ? ll_dispatch_tok_kernel<true, BT> : ll_dispatch_tok_kernel<false, BT>;
+        hipLaunchKernelGGL(tk, dim3(unsigned(blocks)), dim3(BT), 0, stream,
+                           static_cast<const u32x4 *>(x), T, V, K, E, R, E / R, num_slots, ny,
+                           topk_idx, rank_mask, static_cast<u32x4 *>(packed_x),
+                           static_cast<uint2 *>(packed_q), packed_scale, packed_count, src_info,
+                           topk_slot);
         return hipGetLastError();
     }
-    auto kernel = fp8 ? ll_dispatch_kernel<true> : ll_dispatch_kernel<false>;
-    // Copy splits per expert, from the expected rows per expert T*K/E: one
-    // workgroup round copies 2048 vectors (bf16) or 64 blocks (fp8).
-    const int64_t rows = (int64_t(d.num_tokens) * d.num_topk + E - 1) / E;
-    const int64_t work = fp8 ? rows * (d.hidden / 128) : rows * (d.hidden / 8);
-    const int64_t per = fp8 ? 64 : 2048;
-    int ny = int((work + per - 1) / per);
-    ny = ny < 1 ? 1 : (ny > 8 ? 8 : ny);
+    const int ny = ll_slices(V, fp8, rows, kLLBlock);
     if (log_enabled())
-        log_launch("ll_dispatch expert-major T=%d H=%d K=%d E=%d: grid=%dx%d%s", d.num_tokens,
-                   d.hidden, d.num_topk, E, E, ny, fp8 ? " fp8" : "");
-    hipLaunchKernelGGL(kernel, dim3(E, ny), dim3(kLLBlock), 0, stream,
-                       static_cast<const u32x4 *>(x), d.num_tokens, d.hidden / 8, d.num_topk, E,
-                       R, E / R, num_slots, topk_idx, rank_mask, static_cast<u32x4 *>(packed_x),
-                       static_cast<uint2 *>(packed_q), packed_scale, packed_count, src_info,
-                       topk_slot);
+        log_launch("ll_dispatch slot scan + copy T=%d H=%d K=%d E=%d: slot blocks=%d copy "
+                   "blocks=%lld%s",
+                   T, d.hidden, K, E, E, rows ? (long long)T * ny : 0LL, fp8 ? " fp8" : "");
+    hipLaunchKernelGGL(ll_slot_kernel, dim3(E), dim3(kLLBlock), 0, stream, T, K, E, R, E / R,
+                       num_slots, topk_idx, rank_mask, packed_count, src_info, topk_slot);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !rows || T == 0)
+        return e;
+    auto ck = fp8 ? ll_copy_kernel<true> : ll_copy_kernel<false>;
+    hipLaunchKernelGGL(ck, dim3(unsigned(int64_t(T) * ny)), dim3(kLLBlock), 0, stream,
+                       static_cast<const u32x4 *>(x), V, K, E, R, E / R, num_slots, ny, topk_idx,
+                       topk_slot, static_cast<u32x4 *>(packed_x), static_cast<uint2 *>(packed_q),
+                       packed_scale);
     return hipGetLastError();
 }
 
@@ -744,12 +782,12 @@ hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed
         return hipSuccess;
     const int E = d.num_experts, R = d.num_ranks;
     const int V = d.hidden / 8;
-    constexpr int VPT = 1;
-    const int chunks = (V + kLLBlock * VPT - 1) / (kLLBlock * VPT);
+    constexpr int BT = kCombBlock;
+    const int chunks = (V + BT - 1) / BT;
     if (log_enabled())
         log_launch("ll_combine T=%d H=%d K=%d: grid=%dx%d", d.num_tokens, d.hidden, d.num_topk,
                    d.num_tokens, chunks);
-    hipLaunchKernelGGL((ll_combine_kernel<VPT>), dim3(d.num_tokens, chunks), dim3(kLLBlock), 0,
+    hipLaunchKernelGGL(ll_combine_kernel<BT>, dim3(d.num_tokens, chunks), dim3(BT), 0,
                        stream, static_cast<const u32x4 *>(packed_y), V, d.num_topk, E, R, E / R,
                        num_slots, topk_idx, topk_weights, topk_slot, rank_mask,
                        static_cast<u32x4 *>(out));

@@ -86,11 +86,11 @@ def run_normal_path(inp, seed=0, gpu_topk=None):
 
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 4])
-def test_normal_path_configs(cfg):
+def test_normal_path_configs(cfg, layout_mode):
     run_normal_path(config_inputs(cfg))
 
 
-def test_layout_config3():
+def test_layout_config3(layout_mode):
     inp = config_inputs(3, with_x=False)
     ora = oracle.layout(inp.topk_idx, inp.E, inp.R, inp.C)
     buf = epm.Buffer(inp.R, inp.E, inp.C)
@@ -121,7 +121,7 @@ RANDOM_CASES = [
 
 
 @pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: "T%d_H%d_E%d_K%d_R%d_C%d" % c[:6])
-def test_normal_path_random(case):
+def test_normal_path_random(case, layout_mode):
     T, H, E, K, R, C, mask, dup = case
     run_normal_path(random_case(7 + T, T, H, E, K, R, C, mask=mask, dup=dup), seed=T)
 
@@ -168,8 +168,8 @@ LL_CASES = [
     (200, 2048, 64, 6, 8, 256, 0.1, 0.0),
     (64, 7168, 288, 8, 144, 64, 0.05, 0.0),
     (300, 16384, 32, 8, 32, 300, 0.0, 0.3),
-    (512, 520, 96, 8, 12, 512, 0.1, 0.2),     # T*K = 4096: the largest token-major batch
-    (600, 256, 64, 8, 16, 640, 0.05, 0.1),    # T*K = 4800: expert-major in every mode
+    (512, 520, 96, 8, 12, 512, 0.1, 0.2),     # T*K = 4096: the largest one-launch batch
+    (600, 256, 64, 8, 16, 640, 0.05, 0.1),    # T*K = 4800: slot scan + copy in every mode
     (64, 128, 8192, 64, 512, 64, 0.05, 0.05),  # the largest expert count, top-k, ranks
     (32, 64, 8, 8, 4, 32, 0.0, 0.9),     # repeated experts overflow the slots: 39 pairs dropped
     (4096, 64, 8, 1, 4, 4096, 0.0, 0.0),  # the largest slot count the library accepts
@@ -201,7 +201,7 @@ def _sweep_cases(n=40, seed=2024):
 
 
 @pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "s%d_T%d_H%d_E%d_K%d_R%d_C%d" % c[:7])
-def test_random_sweep(case):
+def test_random_sweep(case, layout_mode):
     """Seeded random shapes (odd row lengths, R up to 200, masks, repeated
     experts): the normal path end to end, and the low-latency path when the
     batch fits its slots, against the oracle."""
@@ -212,7 +212,7 @@ def test_random_sweep(case):
         run_ll(inp, seed=i)
 
 
-def test_out_of_range_ids_act_as_masked(ll_mode):
+def test_out_of_range_ids_act_as_masked(ll_mode, layout_mode):
     """Expert ids outside [-1, E) are invalid input, which the library ignores
     (as masked slots) so that no access leaves its buffer.  Both paths on a
     table salted with such ids (E, E + 1, 2^40, -2, -2^40) equal the oracle on
@@ -429,7 +429,7 @@ def test_ep_trace_ranges_in_a_fresh_process():
     assert "trace ok" in r.stdout
 
 
-def test_layout_capacity_out():
+def test_layout_capacity_out(layout_mode):
     inp = config_inputs(0)
     d = abi.dims(inp.T, 8, inp.K, inp.E, inp.R, inp.C)
     topk = dev(inp.topk_idx)
@@ -449,7 +449,7 @@ def test_layout_capacity_out():
     np.testing.assert_array_equal(host(src), ora.recv_src_idx)
 
 
-def test_guard_bands_and_determinism():
+def test_guard_bands_and_determinism(layout_mode):
     """Rows outside [0, N) of the packed buffer, and the bytes around the
     combine output, stay untouched; two runs give identical bytes."""
     inp = random_case(21, 777, 264, 96, 6, 24, 5, mask=0.1, dup=0.1)
