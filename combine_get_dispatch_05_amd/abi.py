@@ -29,7 +29,7 @@ EXPORTS = (
     "ep_handle_dims", "ep_handle_nbytes", "ep_handle_free", "ep_pool_trim", "ep_status_str",
     "ep_last_hip_error", "ep_version", "ep_set_tuning", "ep_tuning_list", "ep_ll_dispatch_fp8",
     "ep_ll_combine_fp8", "ep_mask_update", "ep_mask_clean", "ep_mask_query", "ep_lb_prefetch_weights",
-    "ep_lb_reduce_grads",
+    "ep_lb_reduce_grads", "ep_pool_stats",
 )
 
 
@@ -93,6 +93,8 @@ def _load():
         "ep_handle_nbytes": (ctypes.c_size_t, [vp]),
         "ep_handle_free": (None, [vp]),
         "ep_pool_trim": (ctypes.c_int, []),
+        "ep_pool_stats": (ctypes.c_int, [ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32),
+                                         ctypes.POINTER(ctypes.c_size_t)]),
         "ep_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "ep_last_hip_error": (ctypes.c_char_p, []),
         "ep_version": (ctypes.c_int, []),
@@ -153,6 +155,14 @@ def set_tuning(op: str, *shape: int) -> None:
     """Override the launch shape of ``op`` (no arguments: back to default)."""
     vals = list(shape) + [-1] * (3 - len(shape)) if shape else [-1, -1, -1]
     check(_lib.ep_set_tuning(op.encode(), *vals), "ep_set_tuning")
+
+
+def pool_stats() -> tuple:
+    """(bytes kept, arenas kept, byte cap) of the current device's handle pool."""
+    kb, n, cap = ctypes.c_size_t(), ctypes.c_int32(), ctypes.c_size_t()
+    check(_lib.ep_pool_stats(ctypes.byref(kb), ctypes.byref(n), ctypes.byref(cap)),
+          "ep_pool_stats")
+    return int(kb.value), int(n.value), int(cap.value)
 
 
 def version() -> tuple:

@@ -199,12 +199,12 @@ class Buffer:
         out = abi.LayoutOut(ntpr.data_ptr(), ntpe.data_ptr(), itr.data_ptr(), None, None, None,
                             None, None, 0)
         raw = ctypes.c_void_p()
-        abi.check(abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk_idx),
-                                                   abi.ptr(self._mask), ctypes.byref(out),
-                                                   ctypes.byref(raw) if keep_handle else None,
-                                                   abi.current_stream()),
-                  "ep_get_dispatch_layout")
-        h = Handle(raw.value, d, dev) if keep_handle else None
+        rc = abi.lib().ep_get_dispatch_layout(ctypes.byref(d), abi.ptr(topk_idx),
+                                              abi.ptr(self._mask), ctypes.byref(out),
+                                              ctypes.byref(raw) if keep_handle else None,
+                                              abi.current_stream())
+        h = Handle(raw.value, d, dev) if keep_handle and raw.value else None
+        abi.check(rc, "ep_get_dispatch_layout")
         return ntpr, ntpe, itr.view(torch.bool), h
 
     # ------------------------------------------------------------ dispatch
@@ -244,14 +244,15 @@ class Buffer:
         rtw = torch.empty((cap, K), dtype=torch.float32, device=dev) if topk_weights is not None else None
         n = ctypes.c_int64(-1)
         mask = abi.ptr(self._mask) if handle is None else None
-        abi.check(abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), abi.ptr(topk_idx),
-                                        abi.ptr(topk_weights), mask, ctypes.byref(raw),
-                                        abi.ptr(recv_x),
-                                        abi.ptr(rti), abi.ptr(rtw), cap, ctypes.byref(n),
-                                        abi.current_stream()),
-                  "ep_dispatch")
-        if handle is None:
+        rc = abi.lib().ep_dispatch(ctypes.byref(d), abi.ptr(x), abi.ptr(topk_idx),
+                                   abi.ptr(topk_weights), mask, ctypes.byref(raw),
+                                   abi.ptr(recv_x),
+                                   abi.ptr(rti), abi.ptr(rtw), cap, ctypes.byref(n),
+                                   abi.current_stream())
+        if handle is None and raw.value:
+            # owned from here on, so an error below still frees it
             handle = Handle(raw.value, d, dev)
+        abi.check(rc, "ep_dispatch")
         N = int(n.value)
         lay_counts = None
         if topk_idx is not None:

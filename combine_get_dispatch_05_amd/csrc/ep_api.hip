@@ -15,10 +15,12 @@
 #include <dlfcn.h>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "ep_internal.h"
 
@@ -106,20 +108,45 @@ int hip_fail(hipError_t e)
 // only to a later request on that same stream: stream order then puts the
 // new user's work after every kernel that used the arena, so no event (and
 // no event marker on the stream) is needed.  A request on another stream
-// gets a fresh allocation.  Destroying a stream waits for its work, so an
-// arena tagged with a destroyed stream is idle.  Trimming synchronizes the
-// device before it frees anything.
+// gets a fresh allocation, or an arena known to be idle.
+//
+// The pool is capped per device (kept bytes and arena count).  A free that
+// takes it past the cap synchronizes the device once -- every arena freed
+// before that point is then idle -- frees the oldest arenas until the pool
+// is at half its byte cap and within its count, and marks the rest idle, so
+// any stream may reuse them.  Only that path waits; the same-stream reuse
+// path never does.  Trimming likewise synchronizes before it frees.
 
 struct Arena {
     void *ptr = nullptr;
     size_t bytes = 0;
     hipStream_t freed_on = nullptr;
+    bool idle = false;  // no work uses it any more: any stream may take it
+    uint64_t seq = 0;   // order of freeing (oldest first out)
+    LayoutCounters lc;  // the one-launch layout counters at the arena's start
 };
 
 struct DevicePool {
     std::mutex mu;
-    std::multimap<size_t, Arena> free_list;
+    std::vector<Arena> free_list;
+    size_t kept = 0;  // bytes in free_list
+    uint64_t seq = 0;
 };
+
+constexpr size_t kPoolMaxArenas = 64;
+
+// Byte cap of each device's pool: EP_POOL_CAP_MB (read once), default 256 MiB.
+size_t pool_cap_bytes()
+{
+    static const size_t cap = [] {
+        const char *v = std::getenv("EP_POOL_CAP_MB");
+        long long mb = v != nullptr ? std::atoll(v) : 256;
+        if (mb < 1)
+            mb = 1;
+        return size_t(mb) << 20;
+    }();
+    return cap;
+}
 
 // Pools live until the process ends (never destroyed, so no HIP call runs
 // from a static destructor after the runtime has gone).
@@ -142,10 +169,11 @@ size_t round_arena(size_t b)
 
 int trim_pool(DevicePool &P)
 {
-    std::multimap<size_t, Arena> drop;
+    std::vector<Arena> drop;
     {
         std::lock_guard<std::mutex> g(P.mu);
         drop.swap(P.free_list);
+        P.kept = 0;
     }
     if (drop.empty())
         return EP_OK;
@@ -153,9 +181,44 @@ int trim_pool(DevicePool &P)
     hipError_t e = hipDeviceSynchronize();
     if (e != hipSuccess)
         rc = hip_fail(e);
-    for (auto &kv : drop)
-        (void)hipFree(kv.second.ptr);
+    for (auto &a : drop)
+        (void)hipFree(a.ptr);
     return rc;
+}
+
+// Over the cap: one device-wide synchronization makes every arena freed
+// before it idle; the oldest go back to HIP until the pool is at half its
+// byte cap and within its arena count, and the others become reusable on any
+// stream.  The current device is the pool's.
+void shrink_pool(DevicePool &P)
+{
+    const size_t cap = pool_cap_bytes();
+    uint64_t upto = 0;
+    {
+        std::lock_guard<std::mutex> g(P.mu);
+        upto = P.seq;
+    }
+    if (hipDeviceSynchronize() != hipSuccess)
+        return;  // leave the pool as it is; the error surfaces at the next call
+    std::vector<Arena> drop;
+    {
+        std::lock_guard<std::mutex> g(P.mu);
+        std::sort(P.free_list.begin(), P.free_list.end(),
+                  [](const Arena &a, const Arena &b) { return a.seq < b.seq; });
+        size_t i = 0;
+        while (i < P.free_list.size() && P.free_list[i].seq <= upto &&
+               (P.kept > cap / 2 || P.free_list.size() - i > kPoolMaxArenas / 2)) {
+            P.kept -= P.free_list[i].bytes;
+            drop.push_back(P.free_list[i]);
+            ++i;
+        }
+        P.free_list.erase(P.free_list.begin(), P.free_list.begin() + i);
+        for (Arena &a : P.free_list)
+            if (a.seq <= upto)
+                a.idle = true;
+    }
+    for (auto &a : drop)
+        (void)hipFree(a.ptr);
 }
 
 int arena_get(int dev, size_t bytes, hipStream_t stream, Arena *out)
@@ -164,13 +227,20 @@ int arena_get(int dev, size_t bytes, hipStream_t stream, Arena *out)
     DevicePool &P = pool_for(dev);
     {
         std::lock_guard<std::mutex> g(P.mu);
-        for (auto it = P.free_list.lower_bound(bytes);
-             it != P.free_list.end() && it->first <= 2 * bytes; ++it) {
-            if (it->second.freed_on == stream) {
-                *out = it->second;
-                P.free_list.erase(it);
-                return EP_OK;
-            }
+        size_t best = P.free_list.size();
+        for (size_t i = 0; i < P.free_list.size(); ++i) {
+            const Arena &a = P.free_list[i];
+            if (a.bytes < bytes || a.bytes > 2 * bytes || !(a.idle || a.freed_on == stream))
+                continue;
+            if (best == P.free_list.size() || a.bytes < P.free_list[best].bytes)
+                best = i;
+        }
+        if (best < P.free_list.size()) {
+            *out = P.free_list[best];
+            P.kept -= out->bytes;
+            P.free_list.erase(P.free_list.begin() + best);
+            out->idle = false;
+            return EP_OK;
         }
     }
     void *p = nullptr;
@@ -186,19 +256,103 @@ int arena_get(int dev, size_t bytes, hipStream_t stream, Arena *out)
     }
     if (e != hipSuccess)
         return hip_fail(e);
+    // the one-launch layout's counters start at zero in a new arena
+    e = hipMemsetAsync(p, 0, kLayoutCtrBytes, stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return hip_fail(e);
+    }
     out->ptr = p;
     out->bytes = bytes;
     out->freed_on = stream;
+    out->idle = false;
+    out->lc = LayoutCounters();
     return EP_OK;
 }
 
 void arena_put(int dev, Arena a, hipStream_t stream)
 {
     a.freed_on = stream;
+    a.idle = false;
     DevicePool &P = pool_for(dev);
-    std::lock_guard<std::mutex> g(P.mu);
-    P.free_list.emplace(a.bytes, a);
+    bool over = false;
+    {
+        std::lock_guard<std::mutex> g(P.mu);
+        a.seq = ++P.seq;
+        P.free_list.push_back(a);
+        P.kept += a.bytes;
+        over = P.kept > pool_cap_bytes() || P.free_list.size() > kPoolMaxArenas;
+    }
+    if (over)
+        shrink_pool(P);
 }
+
+// ------------------------------------------------------- pinned N slots
+//
+// N goes back to the host through pinned, coherent host memory: on a fresh
+// dispatch the layout kernel stores it there directly (a system-scope
+// store), so no copy is enqueued, and the host synchronizes the stream once.
+// (Polling the slot instead of synchronizing was measured no faster.)
+// Slots come from a process-wide free list (pages of kSlotsPerPage,
+// allocated once, never released) and are held only for the duration of one
+// call.
+
+constexpr int64_t kNoValue = INT64_MIN;
+constexpr int kSlotsPerPage = 64;
+
+struct Slot {
+    int64_t *host = nullptr;  // where the host reads it
+    int64_t *dev = nullptr;   // the same memory as the GPU addresses it
+};
+
+struct SlotPool {
+    std::mutex mu;
+    std::vector<Slot> free;
+};
+
+SlotPool &slot_pool()
+{
+    static SlotPool *p = new SlotPool();
+    return *p;
+}
+
+int slot_get(Slot *out)
+{
+    SlotPool &P = slot_pool();
+    std::lock_guard<std::mutex> g(P.mu);
+    if (P.free.empty()) {
+        void *page = nullptr;
+        hipError_t e = hipHostMalloc(&page, kSlotsPerPage * 64,
+                                     hipHostMallocPortable | hipHostMallocCoherent);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        void *dpage = nullptr;
+        e = hipHostGetDevicePointer(&dpage, page, 0);
+        if (e != hipSuccess) {
+            (void)hipHostFree(page);
+            return hip_fail(e);
+        }
+        // one 64-byte line per slot
+        for (int i = 0; i < kSlotsPerPage; ++i) {
+            Slot sl;
+            sl.host = reinterpret_cast<int64_t *>(static_cast<char *>(page) + 64 * i);
+            sl.dev = reinterpret_cast<int64_t *>(static_cast<char *>(dpage) + 64 * i);
+            P.free.push_back(sl);
+        }
+    }
+    *out = P.free.back();
+    P.free.pop_back();
+    __atomic_store_n(out->host, kNoValue, __ATOMIC_RELAXED);
+    return EP_OK;
+}
+
+void slot_put(const Slot &slot)
+{
+    SlotPool &P = slot_pool();
+    std::lock_guard<std::mutex> g(P.mu);
+    P.free.push_back(slot);
+}
+
 
 // ------------------------------------------------------------ validation
 
@@ -269,8 +423,11 @@ bool check_enabled()
 // hashes back (synchronizes the stream): a debug check only.
 int same_table(ep_handle *h, const int64_t *topk_idx, hipStream_t stream, bool *same);
 
+// Makes a handle and enqueues its layout.  want_n: the caller needs N right
+// away; the layout then also stores N into a pinned host slot and this call
+// waits for it (the one host synchronization of a fresh dispatch).
 int create_handle(const ep_dims &d, const int64_t *topk_idx, const int32_t *rank_mask,
-                  hipStream_t stream, ep_handle **out)
+                  hipStream_t stream, bool want_n, ep_handle **out)
 {
     ep_handle *h = new (std::nothrow) ep_handle();
     if (h == nullptr)
@@ -290,16 +447,43 @@ int create_handle(const ep_dims &d, const int64_t *topk_idx, const int32_t *rank
         return rc;
     }
     h->bufs = layout_bufs_at(h->arena.ptr, off);
-    e = launch_layout(h->shape, topk_idx, rank_mask, h->bufs, stream);
+    h->last_stream = stream;
+    Slot slot;
+    if (want_n) {
+        rc = slot_get(&slot);
+        if (rc != EP_OK) {
+            ep_handle_free(h);
+            return rc;
+        }
+    }
+    e = launch_layout(h->shape, topk_idx, rank_mask, h->bufs, slot.dev, h->arena.lc, stream);
     if (e == hipSuccess && check_enabled() && topk_idx != nullptr) {
         e = launch_topk_hash(topk_idx, int64_t(d.num_tokens) * d.num_topk, h->bufs.topk_hash,
                              stream);
         h->hashed = e == hipSuccess;
     }
-    h->last_stream = stream;
     if (e != hipSuccess) {
+        if (want_n) {
+            // a layout kernel enqueued before the failure may still store
+            // into the slot: let it finish before the slot is reused
+            (void)hipStreamSynchronize(stream);
+            slot_put(slot);
+        }
         ep_handle_free(h);
         return hip_fail(e);
+    }
+    if (want_n) {
+        // the layout kernel stores N into the slot: one stream synchronization
+        // (measured faster than polling the slot from the host)
+        hipError_t e2 = hipStreamSynchronize(stream);
+        const int64_t n = __atomic_load_n(slot.host, __ATOMIC_ACQUIRE);
+        slot_put(slot);
+        rc = e2 != hipSuccess ? hip_fail(e2) : (n == kNoValue ? hip_fail(hipErrorUnknown) : EP_OK);
+        if (rc != EP_OK) {
+            ep_handle_free(h);
+            return rc;
+        }
+        h->num_recv.store(n);
     }
     *out = h;
     return EP_OK;
@@ -320,14 +504,23 @@ int same_table(ep_handle *h, const int64_t *topk_idx, hipStream_t stream, bool *
     return EP_OK;
 }
 
+// N of a handle: cached on the host after the first read.  Otherwise it is
+// copied from the handle into a pinned slot and the stream synchronized
+// (measured faster than polling the slot for this copy).
 int read_num_recv(ep_handle *h, hipStream_t stream, int64_t *n)
 {
     int64_t v = h->num_recv.load();
     if (v < 0) {
-        hipError_t e = hipMemcpyAsync(&v, h->bufs.num_recv, sizeof(int64_t), hipMemcpyDeviceToHost,
-                                      stream);
+        Slot slot;
+        int rc = slot_get(&slot);
+        if (rc != EP_OK)
+            return rc;
+        hipError_t e = hipMemcpyAsync(slot.host, h->bufs.num_recv, sizeof(int64_t),
+                                      hipMemcpyDeviceToHost, stream);
         if (e == hipSuccess)
             e = hipStreamSynchronize(stream);
+        v = __atomic_load_n(slot.host, __ATOMIC_ACQUIRE);
+        slot_put(slot);
         if (e != hipSuccess)
             return hip_fail(e);
         h->num_recv.store(v);
@@ -427,13 +620,16 @@ int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, const i
         if (out == nullptr && handle_out == nullptr)
             return EP_ERR_INVALID;
         hipStream_t stream = static_cast<hipStream_t>(stream_);
+        // a recv_src_idx buffer below the worst case needs N for its check
+        const bool want_n = out != nullptr && out->recv_src_idx != nullptr &&
+                            out->recv_src_cap >= 0 && out->recv_src_cap < max_rows(*dims);
         ep_handle *h = nullptr;
-        rc = create_handle(*dims, topk_idx, rank_mask, stream, &h);
+        rc = create_handle(*dims, topk_idx, rank_mask, stream, want_n, &h);
         if (rc != EP_OK)
             return rc;
         if (out != nullptr)
             rc = copy_layout(h, out, stream);
-        if (handle_out != nullptr)
+        if (handle_out != nullptr && rc == EP_OK)
             *handle_out = h;
         else
             ep_handle_free(h);
@@ -498,30 +694,43 @@ int ep_dispatch(const ep_dims *dims, const void *x, const int64_t *topk_idx,
                     return EP_ERR_INVALID;
             }
         }
+        const bool pack = recv_x != nullptr || recv_topk_idx != nullptr || recv_topk_weights != nullptr;
         if (fresh) {
-            rc = create_handle(*dims, topk_idx, rank_mask, stream, &h);
+            // N is needed now when the caller asks for it or a buffer is
+            // below the worst case: the layout hands it over directly.
+            const bool want_n = num_recv != nullptr || (pack && recv_cap < max_rows(*dims));
+            rc = create_handle(*dims, topk_idx, rank_mask, stream, want_n, &h);
             if (rc != EP_OK)
                 return rc;
-            *handle = h;
         }
-        const bool pack = recv_x != nullptr || recv_topk_idx != nullptr || recv_topk_weights != nullptr;
+        // A handle made here is released again on any error below, so that
+        // an error leaves *handle untouched.
+        auto fail = [&](int code) {
+            if (fresh)
+                ep_handle_free(h);
+            return code;
+        };
         if (pack) {
             rc = check_capacity(h, recv_cap, stream);
             if (rc != EP_OK)
-                return rc;
+                return fail(rc);
             hipError_t e = launch_dispatch(h->shape, dims->hidden, x, h->bufs, topk_idx,
                                            topk_weights, recv_x, recv_topk_idx,
                                            recv_topk_weights, stream);
             if (e != hipSuccess)
-                return hip_fail(e);
+                return fail(hip_fail(e));
             h->dispatched = true;
         }
         h->last_stream = stream;
         if (num_recv != nullptr) {
-            rc = read_num_recv(h, stream, num_recv);
+            int64_t n = 0;
+            rc = read_num_recv(h, stream, &n);
             if (rc != EP_OK)
-                return rc;
+                return fail(rc);
+            *num_recv = n;
         }
+        if (fresh)
+            *handle = h;
         return EP_OK;
     } catch (const std::bad_alloc &) {
         return EP_ERR_NOMEM;
@@ -834,6 +1043,23 @@ int ep_pool_trim(void)
     return trim_pool(pool_for(dev));
 }
 
+int ep_pool_stats(size_t *kept_bytes, int32_t *kept_arenas, size_t *cap_bytes)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e);
+    DevicePool &P = pool_for(dev);
+    std::lock_guard<std::mutex> g(P.mu);
+    if (kept_bytes != nullptr)
+        *kept_bytes = P.kept;
+    if (kept_arenas != nullptr)
+        *kept_arenas = int32_t(P.free_list.size());
+    if (cap_bytes != nullptr)
+        *cap_bytes = pool_cap_bytes();
+    return EP_OK;
+}
+
 int ep_set_tuning(const char *op, int a, int b, int c)
 {
     if (op == nullptr)
@@ -846,6 +1072,11 @@ int ep_set_tuning(const char *op, int a, int b, int c)
         if (a == -1 && b == -1 && c == -1)
             return set_ll_tuning(0) ? EP_OK : EP_ERR_INVALID;
         return (b == 0 && c == 0 && set_ll_tuning(a)) ? EP_OK : EP_ERR_INVALID;
+    }
+    if (std::strcmp(op, "layout") == 0) {
+        if (a == -1 && b == -1 && c == -1)
+            return set_layout_tuning(0) ? EP_OK : EP_ERR_INVALID;
+        return (b == 0 && c == 0 && set_layout_tuning(a)) ? EP_OK : EP_ERR_INVALID;
     }
     return EP_ERR_INVALID;
 }
@@ -866,7 +1097,7 @@ int ep_tuning_list(const char *op, int index, int *a, int *b, int *c)
             combine_tuning_at(index, a, b, c);
         return n;
     }
-    if (std::strcmp(op, "ll") == 0) {
+    if (std::strcmp(op, "ll") == 0 || std::strcmp(op, "layout") == 0) {
         if (index >= 0 && index < 3) {
             *a = index;
             *b = 0;
@@ -893,6 +1124,6 @@ const char *ep_status_str(int status)
 
 const char *ep_last_hip_error(void) { return g_last_hip.c_str(); }
 
-int ep_version(void) { return (2 << 16) | 1; }
+int ep_version(void) { return (2 << 16) | 2; }
 
 }  // extern "C"

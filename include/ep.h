@@ -127,9 +127,10 @@ int64_t ep_max_recv_rows(const ep_dims *dims);
  *
  * out (nullable): fields that are non-NULL receive copies of the layout.  If
  *   out->recv_src_idx is non-NULL and recv_src_cap < ep_max_recv_rows(), the
- *   call synchronizes the stream to learn N and returns EP_ERR_CAPACITY if
- *   N > recv_src_cap (then no output in `out` is written; the handle, if
- *   asked for, is still created and returned).
+ *   call waits for N (the layout kernel stores it into pinned host memory,
+ *   which the host polls) and returns EP_ERR_CAPACITY if N > recv_src_cap;
+ *   then no output in `out` is written and no handle is returned (*handle_out
+ *   is left unchanged; the layout's memory returns to the pool).
  * handle_out (nullable): receives a new handle holding the layout.  Such a
  *   handle may be given to one ep_dispatch together with the same topk_idx
  *   (the "pre-computed layout" of [P1] "Dispatch Operation").
@@ -164,11 +165,15 @@ int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, const i
  *   slot's weight in the same case, else 0.
  * recv_x (nullable): NULL skips the row copy (layout / size query only).
  * recv_cap: rows available in recv_x / recv_topk_*.  If it is below N the
- *   call returns EP_ERR_CAPACITY (a fresh handle is still returned in
- *   *handle).  When recv_cap >= ep_max_recv_rows() no host synchronization
- *   is needed to check it.
- * num_recv (HOST pointer, nullable): receives N; asking for it synchronizes
- *   the stream once per handle (later calls use the cached value).
+ *   call returns EP_ERR_CAPACITY.  When recv_cap >= ep_max_recv_rows() no
+ *   host synchronization is needed to check it.
+ * num_recv (HOST pointer, nullable): receives N; asking for it waits once
+ *   per handle (later calls use the cached value).  On a fresh dispatch the
+ *   layout kernel stores N into pinned host memory, which the host polls
+ *   (no copy is enqueued); on a handle made earlier N is copied there once.
+ * On any error of a fresh dispatch the new handle is released again and
+ *   *handle is left NULL (the layout may already be enqueued; its memory
+ *   returns to the pool in stream order).
  * Debug check ([P4] "Performance Contract and Constraints": a layout is only
  *   valid for the table it came from): with EP_CHECK=1 in the environment,
  *   ep_get_dispatch_layout stores a 64-bit hash of topk_idx in the handle,
@@ -332,12 +337,23 @@ size_t ep_handle_nbytes(const ep_handle *handle);
  * memory returns to the library's per-device pool, tagged with the handle's
  * last stream; only a later handle made on that same stream reuses it, so
  * stream order puts every use of the memory before its reuse.  Nothing is
- * enqueued. */
+ * enqueued.
+ * The pool is capped per device: at most EP_POOL_CAP_MB MiB (environment,
+ * read once; default 256) and 64 arenas.  A free that takes the pool past
+ * either limit synchronizes the device once (the only case in which this
+ * call waits), returns the oldest arenas to HIP until the pool holds at most
+ * half the byte cap and 32 arenas, and makes the arenas it keeps reusable by
+ * handles on any stream (they are idle after that synchronization). */
 void ep_handle_free(ep_handle *handle);
 
 /* Release every pooled device allocation of the calling thread's current
  * device (synchronizes the device first).  Returns an ep_status. */
 int ep_pool_trim(void);
+
+/* The calling thread's current device's pool: bytes and arenas it keeps for
+ * reuse, and its byte cap (each pointer nullable; HOST pointers).  Returns an
+ * ep_status. */
+int ep_pool_stats(size_t *kept_bytes, int32_t *kept_arenas, size_t *cap_bytes);
 
 /* Launch-shape override for the pack ("dispatch") or the reduce ("combine")
  * kernels, process-wide, for every later call.  Results never depend on it.
@@ -350,9 +366,15 @@ int ep_pool_trim(void);
  * that is not compiled in returns EP_ERR_INVALID.  The env vars
  * EP_TUNE_DISPATCH="G,VPT,c" and EP_TUNE_COMBINE="G,VPT,c" set the initial
  * override.
- * op "ll" picks the low-latency dispatch kernel (b = c = 0): a = 0 automatic
- * (token-major when T*K <= 4096, else expert-major), 1 expert-major always,
- * 2 token-major whenever T*K <= 4096.  Both give identical results. */
+ * op "ll" picks the low-latency dispatch kernels (b = c = 0): a = 0 automatic
+ * (one launch when T*K <= 4096, else a per-expert slot scan followed by a
+ * token-major row copy), 1 slot scan + copy always, 2 one launch whenever
+ * T*K <= 4096.  Both give identical results.
+ * op "layout" picks the layout kernels (b = c = 0), for handles made
+ * afterwards: a = 0 automatic (= 1), 1 the count and position kernels (a
+ * scan kernel between them past 16384 tokens), 2 one launch whenever it fits
+ * (up to 8192 tokens; measured slower than two launches on gfx950, kept for
+ * callers that count launches).  Identical results. */
 int ep_set_tuning(const char *op, int a, int b, int c);
 
 /* Enumerate the compiled-in shapes of `op`: writes shape `index` (if in
@@ -366,7 +388,8 @@ const char *ep_status_str(int status);
 const char *ep_last_hip_error(void);
 
 /* ABI version: (major << 16) | minor.  2.0: rank_mask arguments of
- * ep_get_dispatch_layout, ep_dispatch and ep_combine; 2.1: ep_ll_combine_fp8. */
+ * ep_get_dispatch_layout, ep_dispatch and ep_combine; 2.1: ep_ll_combine_fp8;
+ * 2.2: ep_pool_stats and the capped pool. */
 int ep_version(void);
 
 #ifdef __cplusplus

@@ -20,10 +20,35 @@ L = abi.lib()
 S = None  # NULL stream; never used by these calls
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(ep_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_header_is_checked():
+    """include/ holds the library's ABI and the measurement probes' ABI."""
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["ep.h", "ep_probe.h"]
+
+
+def test_probe_header_matches_its_binding_and_library():
+    from combine_get_dispatch_05_amd import probe_abi
+    hdr = os.path.join(ROOT, "include", "ep_probe.h")
+    assert declared_functions(hdr) == sorted(probe_abi.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", probe_abi.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    P = probe_abi.lib()
+    for name in probe_abi.EXPORTS:
+        assert name in exported, name
+    # argument checks run before anything touches the device
+    assert P.ep_probe_write(None, 16, None) == abi.EP_ERR_INVALID
+    assert P.ep_probe_write(ctypes.c_void_p(0x1008), 16, None) == abi.EP_ERR_ALIGN
+    assert P.ep_probe_empty(0, 64, None) == abi.EP_ERR_INVALID
+    assert P.ep_probe_empty(1, 65, None) == abi.EP_ERR_INVALID
+    assert P.ep_probe_pack(None, 4, 8, None, 1, None, None) == abi.EP_ERR_INVALID
+    assert P.ep_probe_ll_copy(ctypes.c_void_p(0x1000), 4, 12, 2, ctypes.c_void_p(0x1000),
+                              None) == abi.EP_ERR_ALIGN
 
 
 def test_header_matches_binding():
@@ -60,7 +85,7 @@ def test_product_package_never_touches_the_oracle():
 
 
 def test_version_and_status_text():
-    assert abi.version() == (2, 1)
+    assert abi.version() == (2, 2)
     for code in range(7):
         assert L.ep_status_str(code)
     assert L.ep_status_str(99) == b"unknown status"
@@ -187,12 +212,13 @@ def test_mask_and_load_balance_rules():
         assert fn(fake, fake, ctypes.c_void_p(0x10004), 4, 8, 16, S) == abi.EP_ERR_ALIGN
 
 
-def test_ll_tuning_modes():
-    assert abi.tunings("ll") == [(0, 0, 0), (1, 0, 0), (2, 0, 0)]
-    assert L.ep_set_tuning(b"ll", 3, 0, 0) == abi.EP_ERR_INVALID
-    assert L.ep_set_tuning(b"ll", 1, 1, 0) == abi.EP_ERR_INVALID
-    assert L.ep_set_tuning(b"ll", 2, 0, 0) == abi.EP_OK
-    abi.set_tuning("ll")  # back to automatic
+@pytest.mark.parametrize("op", ["ll", "layout"])
+def test_path_tuning_modes(op):
+    assert abi.tunings(op) == [(0, 0, 0), (1, 0, 0), (2, 0, 0)]
+    assert L.ep_set_tuning(op.encode(), 3, 0, 0) == abi.EP_ERR_INVALID
+    assert L.ep_set_tuning(op.encode(), 1, 1, 0) == abi.EP_ERR_INVALID
+    assert L.ep_set_tuning(op.encode(), 2, 0, 0) == abi.EP_OK
+    abi.set_tuning(op)  # back to automatic
 
 
 def test_plain_c_program_uses_the_abi():
