@@ -297,6 +297,11 @@ def main():
     copy_gbs = 2 * copy_bytes / (copy_us * 1e-6) / 1e9
     del src, dst
 
+    # --------------------------------------------- same-traffic ceilings
+    ceilings = measure_ceilings(args, L, abi, tr, d, xs, x2s, recv_xs, recv_x2s, rtw, out, cw,
+                                cap, N, by, dc, dd, S, lx, ltopk, lw, packed, lcount, lsrc, lslot,
+                                lout, topk, w)
+
     # ------------------------------------------- NEXT rows (not in ``value``)
     next_report = measure_next(args, L, abi, tr, dc, xs[0], topk, w, d, cap, recv_xs[0], rtw,
                                out, cw, packed, lcount, lsrc, lslot, lout, lx, ltopk, lw, dd, S,
@@ -339,9 +344,119 @@ def main():
         "copy_ceiling": {"bytes_read_plus_written": 2 * copy_bytes, "avg_us": round(copy_us, 2),
                          "gbs": round(copy_gbs, 1),
                          "frac_hbm_peak": round(copy_gbs / HBM_PEAK_GBS, 4)},
+        "ceilings": ceilings,
         "ops": op_report,
     }
     print(json.dumps(rec))
+
+
+def measure_ceilings(args, L, abi, tr, d, xs, x2s, recv_xs, recv_x2s, rtw, out, cw, cap, N, by,
+                     dc, dd, S, lx, ltopk, lw, packed, lcount, lsrc, lslot, lout, topk, w):
+    """Each operation beside a probe kernel (libep_probe.so) that moves the
+    same bytes in the simplest pattern there is, both timed back to back over
+    ``args.steps`` calls with HIP events at the ends, on the same rotating
+    inputs:
+      cached dispatch  vs  pack probe (read each token row once, store it to
+                           n_t planes) and write probe (the N rows' stores alone)
+      combine          vs  reduce probe (read n_t planes per token, fp32 sum,
+                           store one row)
+      LL dispatch      vs  LL copy probe (the same grid and copy, cells known in
+                           advance) and an empty kernel of the same grid
+      LL combine       vs  LL reduce probe (the same grid, cells known)
+    ``frac_of_ceiling`` = probe time / operation time."""
+    import numpy as np
+    import torch
+    from combine_get_dispatch_05_amd import probe_abi
+
+    PL = probe_abi.lib()
+    P = abi.ptr
+    dev = torch.device("cuda", 0)
+    s = abi.current_stream()
+    T, H, K, R = tr.T, tr.H, tr.K, tr.R
+    n = args.steps
+
+    def b2b(fn):
+        for i in range(max(args.warmup, 2)):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for i in range(n):
+            fn(i)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) * 1e3 / n
+
+    # the dispatch's rows per token, from the layout
+    h = ctypes.c_void_p()
+    abi.check(L.ep_dispatch(ctypes.byref(d), P(xs[0]), P(topk), P(w), None, ctypes.byref(h),
+                            P(recv_xs[0]), None, P(rtw), cap, None, s), "dispatch")
+    itr = torch.empty((T, R), dtype=torch.uint8, device=dev)
+    o = abi.LayoutOut(None, None, itr.data_ptr(), None, None, None, None, None, 0)
+    abi.check(L.ep_handle_copy_layout(h, ctypes.byref(o), s), "copy layout")
+    rows = itr.to(torch.int32).sum(dim=1).to(torch.int32).contiguous()
+    kmax = min(K, R)
+    assert int(rows.sum()) == N
+    planes = [torch.empty((kmax, T, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    nb = len(xs)
+
+    rep = {}
+
+    def entry(name, us, nbytes):
+        rep[name] = {"avg_us": round(us, 2), "bytes": nbytes,
+                     "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+    us_op = b2b(lambda i: abi.check(L.ep_dispatch(
+        ctypes.byref(d), P(x2s[i % nb]), None, None, None, ctypes.byref(h), P(recv_x2s[i % 2]),
+        None, None, cap, None, s), "cached dispatch"))
+    entry("dispatch_cached", us_op, by["dispatch_cached"])
+    us_pr = b2b(lambda i: probe_abi.check(PL.ep_probe_pack(P(x2s[i % nb]), T, H, P(rows), kmax,
+                                                           P(planes[i % 2]), s), "pack probe"))
+    entry("pack_probe", us_pr, (T + N) * H * 2)
+    us_w = b2b(lambda i: probe_abi.check(PL.ep_probe_write(P(recv_x2s[i % 2]), N * H * 2, s),
+                                         "write probe"))
+    entry("write_probe", us_w, N * H * 2)
+    us_c = b2b(lambda i: abi.check(L.ep_combine(h, H, P(recv_xs[i % 2]), cap, P(rtw), None, None,
+                                                None, P(out), P(cw), s), "combine"))
+    entry("combine", us_c, by["combine"])
+    us_rp = b2b(lambda i: probe_abi.check(PL.ep_probe_reduce(P(planes[i % 2]), T, H, P(rows),
+                                                             kmax, P(out), s), "reduce probe"))
+    entry("reduce_probe", us_rp, (N + T) * H * 2)
+    L.ep_handle_free(h)
+    del planes
+
+    # low-latency decode batch
+    Td, Hd, Kd, Ed = dc.T, dc.H, dc.K, dc.E
+    cells = torch.empty((Td * Kd, Hd), dtype=torch.bfloat16, device=dev)
+    us_ld = b2b(lambda i: abi.check(L.ep_ll_dispatch(ctypes.byref(dd), S, P(lx), P(ltopk), None,
+                                                     P(packed), P(lcount), P(lsrc), P(lslot), s),
+                                    "ll dispatch"))
+    entry("ll_dispatch", us_ld, by["ll_dispatch"])
+    us_lp = b2b(lambda i: probe_abi.check(PL.ep_probe_ll_copy(P(lx), Td, Hd, Kd, P(cells), s),
+                                          "ll copy probe"))
+    entry("ll_copy_probe", us_lp, Td * Hd * 2 + Td * Kd * Hd * 2)
+    # the LL dispatch's grid: T x 2 row slices + E/8 expert workgroups of 512 threads
+    V = Hd // 8
+    grid = Td * ((V + 511) // 512) + (Ed + 7) // 8
+    us_le = b2b(lambda i: probe_abi.check(PL.ep_probe_empty(grid, 512, s), "empty"))
+    rep["ll_empty_kernel"] = {"avg_us": round(us_le, 2), "blocks": grid, "threads": 512}
+    us_lc = b2b(lambda i: abi.check(L.ep_ll_combine(ctypes.byref(dd), S, P(packed), P(ltopk),
+                                                    P(lw), P(lslot), None, P(lout), s),
+                                    "ll combine"))
+    entry("ll_combine", us_lc, by["ll_combine"])
+    us_lr = b2b(lambda i: probe_abi.check(PL.ep_probe_ll_reduce(P(cells), P(lw), Td, Hd, Kd,
+                                                                P(lout), s), "ll reduce probe"))
+    entry("ll_reduce_probe", us_lr, Td * Kd * Hd * 2 + Td * Hd * 2 + Td * Kd * 4)
+    del cells
+
+    rep["frac_of_ceiling"] = {
+        "dispatch_cached_vs_pack_probe": round(us_pr / us_op, 4),
+        "combine_vs_reduce_probe": round(us_rp / us_c, 4),
+        "ll_dispatch_vs_ll_copy_probe": round(us_lp / us_ld, 4),
+        "ll_combine_vs_ll_reduce_probe": round(us_lr / us_lc, 4),
+    }
+    rep["timed_over"] = f"{n} calls back to back, HIP events at the ends"
+    return rep
 
 
 def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw, packed, lcount,
@@ -371,23 +486,41 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     rep = {}
     T, H, K = tr.T, tr.H, tr.K
     s = abi.current_stream()
-    # the layout with the N readback a fresh dispatch of unknown size needs
-    # (one host sync per call), host wall time per call
-    def layout_and_n():
+    # The layout with the N readback a fresh dispatch of unknown size needs
+    # (ep_dispatch asked for N only: the layout kernel stores N into pinned
+    # host memory, and the call synchronizes once), host wall time per call;
+    # and the same through a handle made without it (N copied back later).
+    def fresh_size_query():
+        hl = ctypes.c_void_p()
+        nn = ctypes.c_int64()
+        abi.check(L.ep_dispatch(ctypes.byref(d), None, P(topk), None, None, ctypes.byref(hl), None,
+                                None, None, 0, ctypes.byref(nn), s), "size query")
+        L.ep_handle_free(hl)
+
+    def layout_then_n():
         hl = ctypes.c_void_p()
         abi.check(L.ep_get_dispatch_layout(ctypes.byref(d), P(topk), None, None, ctypes.byref(hl),
                                            s), "layout")
         nn = ctypes.c_int64()
         abi.check(L.ep_handle_num_recv(hl, ctypes.byref(nn)), "num_recv")
         L.ep_handle_free(hl)
-    for _ in range(max(args.warmup, 2)):
-        layout_and_n()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        layout_and_n()
-    us = (time.perf_counter() - t0) * 1e6 / args.steps
-    rep["layout_with_n_readback"] = {"avg_us": round(us, 2), "mtok_s": round(T / us, 2)}
+
+    def host_us(fn):
+        for _ in range(max(args.warmup, 2)):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        return (time.perf_counter() - t0) * 1e6 / args.steps
+    us = host_us(fresh_size_query)
+    rep["layout_with_n_readback"] = {"avg_us": round(us, 2), "mtok_s": round(T / us, 2),
+                                     "how": "ep_dispatch size query (layout kernel stores N "
+                                            "into pinned host memory, one stream sync)"}
+    us = host_us(layout_then_n)
+    rep["layout_then_handle_num_recv"] = {"avg_us": round(us, 2),
+                                          "how": "ep_get_dispatch_layout, then ep_handle_num_recv "
+                                                 "(N copied into pinned memory, one stream sync)"}
     # combine with two bias rows
     h = ctypes.c_void_p()
     abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), None, ctypes.byref(h),
@@ -560,6 +693,35 @@ def measure_workloads(args, L, abi):
             "combine_gbs": round(b_comb / (us_comb * 1e-6) / 1e9, 1),
         }
         del x, recv, rti, rtw, out, cw
+
+    # low-latency batch past the one-launch limit (T*K = 8192): slot scan +
+    # token-major copy, then the LL combine
+    from gen import generate
+    inp = generate(1024, 7168, 256, 8, 32, 1, seed=0, slots=1024, name="ll_large")
+    T, H, E, K, R, S = inp.T, inp.H, inp.E, inp.K, inp.R, inp.slots
+    epr = E // R
+    d = abi.dims(T, H, K, E, R, 1)
+    x = torch.from_numpy(np.ascontiguousarray(inp.x).view(np.int16)).to(dev)
+    topk = torch.from_numpy(inp.topk_idx).to(dev)
+    w = torch.from_numpy(inp.topk_weights).to(dev)
+    packed = torch.empty((epr, R, S, H), dtype=torch.int16, device=dev)
+    cnt = torch.empty((epr, R), dtype=torch.int32, device=dev)
+    src = torch.empty((epr, R, S), dtype=torch.int32, device=dev)
+    slot = torch.empty((T, K), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H), dtype=torch.int16, device=dev)
+    M = int((inp.topk_idx >= 0).sum())
+    us_d = timed(lambda: abi.check(L.ep_ll_dispatch(ctypes.byref(d), S, P(x), P(topk), None,
+                                                    P(packed), P(cnt), P(src), P(slot), s), "ll"))
+    us_c = timed(lambda: abi.check(L.ep_ll_combine(ctypes.byref(d), S, P(packed), P(topk), P(w),
+                                                   P(slot), None, P(out), s), "ll"))
+    b_d = T * H * 2 + M * H * 2 + T * K * 12 + M * 4
+    b_c = M * H * 2 + T * H * 2 + T * K * 16
+    rep["ll_large"] = {"T": T, "H": H, "E": E, "K": K, "R": R, "slots": S, "M": M,
+                       "ll_dispatch_us": round(us_d, 2), "ll_dispatch_bytes": b_d,
+                       "ll_dispatch_gbs": round(b_d / (us_d * 1e-6) / 1e9, 1),
+                       "ll_combine_us": round(us_c, 2), "ll_combine_bytes": b_c,
+                       "ll_combine_gbs": round(b_c / (us_c * 1e-6) / 1e9, 1)}
+    del packed
     return rep
 
 

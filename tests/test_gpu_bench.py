@@ -20,7 +20,7 @@ def test_bench_line_keeps_the_contract():
     sys.__stderr__.flush()
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3",
                         "--warmup", "1", "--cpu-seconds", "0.5"],
-                       capture_output=True, text=True, timeout=110, cwd=ROOT)
+                       capture_output=True, text=True, timeout=115, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-3000:]
     lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1, r.stdout
@@ -55,6 +55,16 @@ def test_bench_line_keeps_the_contract():
     for name in ("skewed", "large"):
         wl = b["workloads"][name]
         assert wl["N"] > 0 and wl["combine_gbs"] > 0 and wl["dispatch_cached_gbs"] > 0
+    ll = b["workloads"]["ll_large"]
+    assert ll["T"] * ll["K"] > 4096 and ll["ll_dispatch_us"] > 0 and ll["ll_combine_us"] > 0
+    # every operation beside its same-traffic probe
+    ce = b["ceilings"]
+    for op, probe in (("dispatch_cached", "pack_probe"), ("combine", "reduce_probe"),
+                      ("ll_dispatch", "ll_copy_probe"), ("ll_combine", "ll_reduce_probe")):
+        assert ce[op]["avg_us"] > 0 and ce[probe]["avg_us"] > 0
+        frac = ce["frac_of_ceiling"][f"{op}_vs_{probe}"]
+        assert abs(frac - ce[probe]["avg_us"] / ce[op]["avg_us"]) < 0.01
+    assert ce["pack_probe"]["bytes"] == (4096 + N) * 7168 * 2
 
     cpu = b["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["cores"] == 1
