@@ -100,7 +100,7 @@ def _normal_mask_case(case):
 
 
 @pytest.mark.parametrize("case", ["tiny", "skewed", "large", "R512", "T20000"])
-def test_normal_path_rank_mask(case):
+def test_normal_path_rank_mask(case, layout_mode):
     """Ranks masked before the layout receive nothing (layout, dispatch and
     handle bit-exact with the oracle's masked layout); a rank masked later,
     before the combine, drops out of both combine sums."""
@@ -221,6 +221,63 @@ def test_ll_dispatch_fp8(case, ll_mode):
     np.testing.assert_array_equal(f32_bits(sch[used]), f32_bits(o_sc[used]))
     if case != "nonfinite":
         assert not nan_o[used].any()
+
+
+def _fp8_sweep_rows(amax_bits: int, H: int = 2048):
+    """Rows that enumerate every bf16 magnitude from 0 up to the bf16 value
+    `amax_bits`, with both signs, 127 per 128-element block; the first
+    element of every block is +amax itself, so every block's amax (after the
+    1e-4 floor) and hence its scale is fixed.  Trailing unused elements
+    repeat +0."""
+    mags = np.arange(0, amax_bits + 1, dtype=np.uint32)
+    vals = np.concatenate([mags, mags | 0x8000]).astype(np.uint16)
+    per = 127
+    nblk = -(-vals.size // per)
+    vals = np.concatenate([vals, np.zeros(nblk * per - vals.size, np.uint16)])
+    blocks = np.concatenate([np.full((nblk, 1), amax_bits, np.uint16), vals.reshape(nblk, per)],
+                            axis=1)
+    bpr = H // 128
+    T = -(-nblk // bpr)
+    pad = np.zeros((T * bpr - nblk, 128), np.uint16)
+    pad[:, 0] = amax_bits
+    return np.ascontiguousarray(np.concatenate([blocks, pad]).reshape(T, H))
+
+
+# bf16 block maxima: 448 (scale exactly 1: the codes are the e4m3 rounding of
+# the bf16 values themselves, every e4m3 tie and subnormal tie included);
+# 300 and 1.203 (scales that are not powers of two); 446 (products a hair
+# above 448 hit the saturation edge); 9.98e-5 (below the 1e-4 floor).
+@pytest.mark.parametrize("amax_bits", [0x43E0, 0x4396, 0x3F9A, 0x43DF, 0x38D1])
+def test_ll_dispatch_fp8_conversion_sweep(amax_bits, ll_mode):
+    """The FP8 dispatch's codes on rows that sweep every bf16 magnitude up to
+    each block's amax, against the oracle's e4m3 round to nearest even, bit
+    for bit.  Finite blocks are quantized by the hardware's packed
+    fp32->e4m3 conversion, so this pins that conversion to the definition
+    on every value the dispatch can feed it at these scales."""
+    x = _fp8_sweep_rows(amax_bits)
+    T, H = x.shape
+    E, R, K = 8, 2, 2
+    topk = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], axis=1).astype(np.int64)
+    S = T
+    buf = epm.Buffer(R, E)
+    (q, sc), count, hdl, _, _ = buf.low_latency_dispatch(dev_bf16(x), dev(topk), S, E,
+                                                          use_fp8=True)
+    o_q, o_sc, o_cnt, o_src, o_slot = oracle.ll_dispatch_fp8(x, topk, E, R, S)
+    np.testing.assert_array_equal(host(count), o_cnt)
+    np.testing.assert_array_equal(host(hdl.src_info), o_src)
+    used = o_src >= 0
+    qh = q.view(torch.uint8).cpu().numpy()
+    assert not pinlib.e4m3_is_nan(o_q[used]).any()
+    np.testing.assert_array_equal(qh[used], o_q[used])
+    np.testing.assert_array_equal(f32_bits(sc.cpu().numpy()[used]), f32_bits(o_sc[used]))
+    if amax_bits == 0x43E0:
+        # scale 1: the e4m3 midpoints among the inputs (values halfway between
+        # two neighbouring codes) were all rounded to the even code
+        xf = oracle.bf16_to_f32(x.reshape(-1))
+        lo = np.array([oracle.e4m3_to_f32(c) for c in range(0x7F)], np.float64)
+        mids = (lo[:-1] + lo[1:]) / 2
+        n_ties = int(np.isin(np.abs(xf.astype(np.float64)), mids).sum())
+        assert n_ties > 200, n_ties
 
 
 # ------------------------------------------------------------ load balancing
