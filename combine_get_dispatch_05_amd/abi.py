@@ -21,6 +21,7 @@ EP_ERR_CAPACITY = 3
 EP_ERR_HANDLE = 4
 EP_ERR_HIP = 5
 EP_ERR_NOMEM = 6
+EP_ERR_TOO_LARGE = 7
 
 # Every function include/ep.h declares (checked against the header by the tests).
 EXPORTS = (
@@ -29,7 +30,7 @@ EXPORTS = (
     "ep_handle_dims", "ep_handle_nbytes", "ep_handle_free", "ep_pool_trim", "ep_status_str",
     "ep_last_hip_error", "ep_version", "ep_set_tuning", "ep_tuning_list", "ep_ll_dispatch_fp8",
     "ep_ll_combine_fp8", "ep_mask_update", "ep_mask_clean", "ep_mask_query", "ep_lb_prefetch_weights",
-    "ep_lb_reduce_grads", "ep_pool_stats",
+    "ep_lb_reduce_grads", "ep_pool_stats", "ep_get_dispatch_layout_noalloc",
 )
 
 
@@ -75,6 +76,7 @@ def _load():
     sig = {
         "ep_max_recv_rows": (i64, [pdims]),
         "ep_get_dispatch_layout": (ctypes.c_int, [pdims, vp, vp, pout, ctypes.POINTER(vp), vp]),
+        "ep_get_dispatch_layout_noalloc": (ctypes.c_int, [pdims, vp, vp, pout, vp]),
         "ep_dispatch": (ctypes.c_int, [pdims, vp, vp, vp, vp, ctypes.POINTER(vp), vp, vp, vp, i64,
                                        ctypes.POINTER(i64), vp]),
         "ep_combine": (ctypes.c_int, [vp, i32, vp, i64, vp, vp, vp, vp, vp, vp, vp]),

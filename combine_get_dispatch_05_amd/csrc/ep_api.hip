@@ -592,6 +592,34 @@ int copy_layout(ep_handle *h, const ep_layout_out *o, hipStream_t stream)
     return EP_OK;
 }
 
+// ------------------------------------------------------ static scratch
+//
+// The scratch of ep_get_dispatch_layout_noalloc: one static device array per
+// GPU (the code object's own memory, no allocation).  Host code never uses
+// the array's name as an address: each device's address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+
+static __device__ __align__(256) unsigned char scratch[EP_NOALLOC_SCRATCH_BYTES];
+
+int scratch_ptr(int dev, void **out)
+{
+    static std::mutex mu;
+    static std::map<int, void *> ptrs;
+    std::lock_guard<std::mutex> g(mu);
+    auto it = ptrs.find(dev);
+    if (it != ptrs.end()) {
+        *out = it->second;
+        return EP_OK;
+    }
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+        return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    ptrs[dev] = p;
+    *out = p;
+    return EP_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------- ABI
@@ -636,6 +664,68 @@ int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, const i
         return rc;
     } catch (const std::bad_alloc &) {
         return EP_ERR_NOMEM;
+    } catch (...) {
+        return EP_ERR_INVALID;
+    }
+}
+
+int ep_get_dispatch_layout_noalloc(const ep_dims *dims, const int64_t *topk_idx,
+                                   const int32_t *rank_mask, ep_layout_out *out,
+                                   ep_stream_t stream_)
+{
+    TraceRange trace_range("ep_get_dispatch_layout_noalloc");
+    try {
+        int rc = check_dims(dims);
+        if (rc != EP_OK)
+            return rc;
+        if (out == nullptr || (dims->num_tokens > 0 && topk_idx == nullptr))
+            return EP_ERR_INVALID;
+        if (!aligned(topk_idx, 8) || !aligned(rank_mask, 4))
+            return EP_ERR_ALIGN;
+        const void *i32s[6] = {out->num_tokens_per_rank,   out->num_tokens_per_expert,
+                               out->rank_prefix_matrix,    out->channel_prefix_matrix,
+                               out->recv_channel_prefix_matrix, out->recv_src_idx};
+        for (const void *p : i32s)
+            if (!aligned(p, 4))
+                return EP_ERR_ALIGN;
+        if (!aligned(out->send_head, 16) || !aligned(out->is_token_in_rank, 4))
+            return EP_ERR_ALIGN;
+        if (out->recv_src_idx != nullptr && out->recv_src_cap < max_rows(*dims))
+            return EP_ERR_CAPACITY;
+        const LayoutShape shape = layout_shape(*dims, false);
+        size_t off[kArenaFields];
+        if (layout_arena_bytes(shape, off) > size_t(EP_NOALLOC_SCRATCH_BYTES))
+            return EP_ERR_TOO_LARGE;
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return hip_fail(e);
+        void *base = nullptr;
+        rc = scratch_ptr(dev, &base);
+        if (rc != EP_OK)
+            return rc;
+        // the kernels write the caller's buffers; fields left NULL go to scratch
+        LayoutBufs b = layout_bufs_at(base, off);
+        if (out->num_tokens_per_rank != nullptr)
+            b.num_tokens_per_rank = out->num_tokens_per_rank;
+        if (out->num_tokens_per_expert != nullptr)
+            b.num_tokens_per_expert = out->num_tokens_per_expert;
+        if (out->is_token_in_rank != nullptr)
+            b.is_token_in_rank = out->is_token_in_rank;
+        if (out->rank_prefix_matrix != nullptr)
+            b.rank_prefix_matrix = out->rank_prefix_matrix;
+        if (out->channel_prefix_matrix != nullptr)
+            b.channel_prefix_matrix = out->channel_prefix_matrix;
+        if (out->recv_channel_prefix_matrix != nullptr)
+            b.recv_channel_prefix_matrix = out->recv_channel_prefix_matrix;
+        if (out->send_head != nullptr)
+            b.send_head = out->send_head;
+        if (out->recv_src_idx != nullptr)
+            b.recv_src_idx = out->recv_src_idx;
+        LayoutCounters unused;  // the multi-kernel path never touches them
+        e = launch_layout(shape, topk_idx, rank_mask, b, nullptr, unused,
+                          static_cast<hipStream_t>(stream_));
+        return e == hipSuccess ? EP_OK : hip_fail(e);
     } catch (...) {
         return EP_ERR_INVALID;
     }
@@ -1118,12 +1208,13 @@ const char *ep_status_str(int status)
     case EP_ERR_HANDLE: return "handle missing or does not match the dims";
     case EP_ERR_HIP: return "HIP runtime error";
     case EP_ERR_NOMEM: return "out of memory";
+    case EP_ERR_TOO_LARGE: return "problem needs more than the no-allocation layout's static scratch";
     default: return "unknown status";
     }
 }
 
 const char *ep_last_hip_error(void) { return g_last_hip.c_str(); }
 
-int ep_version(void) { return (2 << 16) | 2; }
+int ep_version(void) { return (2 << 16) | 3; }
 
 }  // extern "C"

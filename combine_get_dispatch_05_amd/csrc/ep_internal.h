@@ -53,7 +53,9 @@ struct LayoutShape {
     bool fused;  // one-launch layout (count blocks of 256 tokens), else two kernels (512)
 };
 
-LayoutShape layout_shape(const ep_dims &d);
+// allow_fused: the one-launch layout may be chosen (it needs the arena's
+// counter bookkeeping, so only handle arenas allow it).
+LayoutShape layout_shape(const ep_dims &d, bool allow_fused = true);
 // Byte offsets of every LayoutBufs field inside one arena; returns the total.
 size_t layout_arena_bytes(const LayoutShape &s, size_t off[kArenaFields]);
 LayoutBufs layout_bufs_at(void *base, const size_t off[kArenaFields]);

@@ -753,7 +753,7 @@ bool set_layout_tuning(int mode)
     return true;
 }
 
-LayoutShape layout_shape(const ep_dims &d)
+LayoutShape layout_shape(const ep_dims &d, bool allow_fused)
 {
     LayoutShape s;
     s.T = d.num_tokens;
@@ -768,7 +768,8 @@ LayoutShape layout_shape(const ep_dims &d)
     // all count blocks themselves): its grid-wide wait costs more than the
     // second launch it saves (13.4 against 4.2 + 5.9 us at 4096 tokens).
     const int64_t fused_blocks = (int64_t(s.T) + kFusedCount - 1) / kFusedCount;
-    s.fused = g_layout_mode.load() == 2 && s.T > 0 && fused_blocks <= kSelfScanBlocks;
+    s.fused = allow_fused && g_layout_mode.load() == 2 && s.T > 0 &&
+              fused_blocks <= kSelfScanBlocks;
     const int cb = s.fused ? kFusedCount : kCountBlock;
     s.nB = s.T > 0 ? (s.T + cb - 1) / cb : 1;
     return s;

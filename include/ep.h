@@ -70,7 +70,8 @@ typedef enum ep_status {
     EP_ERR_CAPACITY = 3, /* caller buffer has fewer rows than the result needs */
     EP_ERR_HANDLE = 4,   /* handle does not match the dims, or NULL handle */
     EP_ERR_HIP = 5,      /* a HIP runtime call failed (see ep_last_hip_error) */
-    EP_ERR_NOMEM = 6     /* device or host allocation failed */
+    EP_ERR_NOMEM = 6,    /* device or host allocation failed */
+    EP_ERR_TOO_LARGE = 7 /* needs more than ep_get_dispatch_layout_noalloc's static scratch */
 } ep_status;
 
 /* Problem sizes.  Limits: 0 <= num_tokens <= 2^24; hidden > 0, hidden % 8 == 0,
@@ -142,6 +143,32 @@ int64_t ep_max_recv_rows(const ep_dims *dims);
  */
 int ep_get_dispatch_layout(const ep_dims *dims, const int64_t *topk_idx, const int32_t *rank_mask,
                            ep_layout_out *out, ep_handle **handle_out, ep_stream_t stream);
+
+/*
+ * ep_get_dispatch_layout for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same layout, written into `out`, with no handle, no hipMalloc / hipFree /
+ * host allocation and no host synchronization.  The layout kernels write the
+ * caller's buffers directly; their scratch (and any output field left NULL)
+ * lives in one static device array of EP_NOALLOC_SCRATCH_BYTES per GPU, held
+ * until the process ends.  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race and give
+ * undefined results; calls in one stream's order are fine.  Nothing in the
+ * array needs to start at zero.
+ *   out: required.  Fields as for ep_get_dispatch_layout; recv_src_idx, when
+ *     non-NULL, needs recv_src_cap >= ep_max_recv_rows() (EP_ERR_CAPACITY
+ *     otherwise: N is not read back).  send_head must be 16-byte aligned and
+ *     is_token_in_rank 4-byte aligned (EP_ERR_ALIGN), since the kernels store
+ *     them 4 ranks at a time.
+ *   The layout always takes the count and position kernels (the one-launch
+ *   layout of the "layout" tuning knob is not used here).
+ * A problem whose scratch would exceed EP_NOALLOC_SCRATCH_BYTES returns
+ * EP_ERR_TOO_LARGE before anything is enqueued.
+ */
+#define EP_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ep_get_dispatch_layout_noalloc(const ep_dims *dims, const int64_t *topk_idx,
+                                   const int32_t *rank_mask, ep_layout_out *out,
+                                   ep_stream_t stream);
 
 /*
  * [P1] "Dispatch Operation" and [P4] "Fast Path Dispatch with Handle Reuse":
@@ -389,7 +416,8 @@ const char *ep_last_hip_error(void);
 
 /* ABI version: (major << 16) | minor.  2.0: rank_mask arguments of
  * ep_get_dispatch_layout, ep_dispatch and ep_combine; 2.1: ep_ll_combine_fp8;
- * 2.2: ep_pool_stats and the capped pool. */
+ * 2.2: ep_pool_stats and the capped pool; 2.3: ep_get_dispatch_layout_noalloc
+ * and EP_ERR_TOO_LARGE. */
 int ep_version(void);
 
 #ifdef __cplusplus

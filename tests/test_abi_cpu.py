@@ -85,8 +85,8 @@ def test_product_package_never_touches_the_oracle():
 
 
 def test_version_and_status_text():
-    assert abi.version() == (2, 2)
-    for code in range(7):
+    assert abi.version() == (2, 3)
+    for code in range(8):
         assert L.ep_status_str(code)
     assert L.ep_status_str(99) == b"unknown status"
 
@@ -233,3 +233,24 @@ def test_plain_c_program_uses_the_abi():
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
     assert "abi_check cpu: ok" in r.stdout
+
+
+def test_noalloc_layout_rules_without_device():
+    """ep_get_dispatch_layout_noalloc refuses bad arguments, short buffers
+    and problems beyond its static scratch before any device call."""
+    d = abi.dims(16, 64, 2, 8, 4, 1)
+    fake = ctypes.c_void_p(0x10000)
+    f = L.ep_get_dispatch_layout_noalloc
+    assert f(ctypes.byref(d), fake, None, None, S) == abi.EP_ERR_INVALID  # out is required
+    o = abi.LayoutOut()
+    assert f(ctypes.byref(d), None, None, ctypes.byref(o), S) == abi.EP_ERR_INVALID  # no table
+    o = abi.LayoutOut(None, None, None, None, None, None, 0x10004, None, 0)
+    assert f(ctypes.byref(d), fake, None, ctypes.byref(o), S) == abi.EP_ERR_ALIGN  # send_head
+    o = abi.LayoutOut(None, None, 0x10002, None, None, None, None, None, 0)
+    assert f(ctypes.byref(d), fake, None, ctypes.byref(o), S) == abi.EP_ERR_ALIGN  # membership
+    o = abi.LayoutOut(None, None, None, None, None, None, None, 0x10000, 31)
+    assert f(ctypes.byref(d), fake, None, ctypes.byref(o), S) == abi.EP_ERR_CAPACITY  # 32 rows
+    big = abi.dims(1 << 20, 64, 8, 512, 512, 1)  # [T][R] alone is 512 MiB
+    o = abi.LayoutOut()
+    assert f(ctypes.byref(big), fake, None, ctypes.byref(o), S) == abi.EP_ERR_TOO_LARGE
+    assert L.ep_status_str(abi.EP_ERR_TOO_LARGE).startswith(b"problem needs more")
