@@ -258,19 +258,25 @@ __device__ __forceinline__ void ll_slice(int V, int ny, int yb, int &c0, int &c1
 }
 
 // The first vector of this lane's share of the slice (its load does not
-// depend on the slots, so it is issued before they are known).
-template <bool kFP8>
+// depend on the slots, so it is issued before they are known).  A slice is
+// never empty (checked for every row length and block size the library
+// accepts), and lanes past its end read its last vector again (never
+// stored), so the load is unconditional: no per-lane branch makes later
+// waits conservative.  kRows = false (metadata only): no load at all.
+template <bool kFP8, bool kRows>
 __device__ __forceinline__ u32x4 ll_first(const u32x4 *__restrict__ x, int64_t t, int V, int c0,
-                                          int c1, int b0, int b1, bool rows)
+                                          int c1, int b0, int b1)
 {
     const int tid = threadIdx.x;
     u32x4 v = {0, 0, 0, 0};
+    if (!kRows)
+        return v;
     if (!kFP8) {
-        if (rows && c0 + tid < c1)
-            v = x[t * V + c0 + tid];
+        const int c = c0 + tid;
+        v = x[t * V + (c < c1 ? c : c1 - 1)];
     } else {
-        if (b0 + (tid >> 4) < b1)
-            v = x[t * V + int64_t(b0 + (tid >> 4)) * 16 + (tid & 15)];
+        const int bb = b0 + (tid >> 4);
+        v = x[t * V + int64_t(bb < b1 ? bb : b1 - 1) * 16 + (tid & 15)];
     }
     return v;
 }
@@ -395,14 +401,15 @@ __global__ __launch_bounds__(kLLBlock) void ll_copy_kernel(
     const int yb = blockIdx.x - int(t) * ny;
     int c0, c1, b0, b1;
     ll_slice<kFP8>(V, ny, yb, c0, c1, b0, b1);
-    const u32x4 first = ll_first<kFP8>(x, t, V, c0, c1, b0, b1, true);
-    int cell = -1;
-    if (lane < K) {
-        const int e = ll_valid_id(topk_idx[t * K + lane], E);
-        const int s = topk_slot[t * K + lane];
-        if (e >= 0 && s >= 0 && s < S)
-            cell = ll_cell(e, epr, R, S, s);
-    }
+    // the pair's id and slot (lanes past K read pair K - 1 again) and the
+    // slice's first vector, all in flight before any is looked at
+    const int k = lane < K ? lane : K - 1;
+    int64_t e_raw = topk_idx[t * K + k];
+    int s = topk_slot[t * K + k];
+    const u32x4 first = ll_first<kFP8, true>(x, t, V, c0, c1, b0, b1);
+    asm volatile("" : "+v"(e_raw), "+v"(s));
+    const int e = ll_valid_id(e_raw, E);
+    const int cell = (lane < K && e >= 0 && s >= 0 && s < S) ? ll_cell(e, epr, R, S, s) : -1;
     ll_store_slice<kFP8, kLLBlock>(x, t, V, K, cell, first, c0, c1, b0, b1, packed_x, packed_q,
                                    packed_scale);
 }
@@ -422,7 +429,7 @@ constexpr int kTokBlock = 512;     // threads of a one-launch workgroup
 // quantized once.  The remaining workgroups handle four experts each (one
 // per wave), counting with the same ballots over the whole table: the
 // expert's count and the -1 entries of its unused src_info cells.
-template <bool kFP8, int BT>
+template <bool kFP8, int BT, bool kRows>
 __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
     const u32x4 *__restrict__ x, int T, int V, int K, int E, int R, int epr, int S, int ny,
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask,
@@ -484,28 +491,43 @@ __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
     const int t = b / ny;
     const int yb = b - t * ny;
     const int base = t * K;
-    // lane k < K of every wave: the expert of pair (t, k)
-    int own = -1;
-    if (lane < K)
-        own = ll_valid_id(topk_idx[base + lane], E);
-    // entries that can precede one of the token's pairs: i < base + K - 1
-    // (the count below takes entries i < base + k only, so i >= lim never
-    // counts)
+    // Loads first, in this order, all in flight at once: lane k < K's own
+    // pair (t, k) (lanes past K read slot K - 1 again), the table entries
+    // that can precede one of the token's pairs (i < base + K - 1; the count
+    // below takes entries i < base + k only, so i >= lim never counts; raw,
+    // unconverted, indexes clamped), then the row slice's first vector.
+    int64_t own_raw = topk_idx[base + (lane < K ? lane : K - 1)];
     const int lim = base + K - 1;
+    int64_t raw[kHold];
+#pragma unroll
+    for (int u0 = 0; u0 < kHold; u0 += 4) {
+        if (u0 * BT < lim) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = (u0 + q) * BT + tid;
+                raw[u0 + q] = topk_idx[i < lim ? i : lim - 1];
+            }
+        }
+    }
+    int c0, c1, b0, b1;
+    ll_slice<kFP8>(V, ny, yb, c0, c1, b0, b1);
+    const u32x4 first = ll_first<kFP8, kRows>(x, t, V, c0, c1, b0, b1);
+    // Only now are the ids looked at: without these empty (volatile) uses the
+    // compiler tests each id right after its load, which makes every later
+    // load -- the row slice's too -- wait for it.
+    asm volatile("" : "+v"(own_raw));
     int ids[kHold];
 #pragma unroll
     for (int u0 = 0; u0 < kHold; u0 += 4) {
         if (u0 * BT < lim) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                ids[u0 + q] = ll_id_at(topk_idx, (u0 + q) * BT + tid, lim, E);
+            for (int q = 0; q < 4; ++q) {
+                asm volatile("" : "+v"(raw[u0 + q]));
+                ids[u0 + q] = ll_valid_id(raw[u0 + q], E);
+            }
         }
     }
-    // the row slice's first load, after the table loads so that waiting for
-    // those does not wait for it
-    int c0, c1, b0, b1;
-    ll_slice<kFP8>(V, ny, yb, c0, c1, b0, b1);
-    const u32x4 first = ll_first<kFP8>(x, t, V, c0, c1, b0, b1, packed_x != nullptr);
+    const int own = lane < K ? ll_valid_id(own_raw, E) : -1;
     bool live = own >= 0;
     if (rank_mask != nullptr && live)
         live = rank_mask[own / epr] == 0;
@@ -541,7 +563,7 @@ __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
         if (cell >= 0)
             src_info[cell] = t;
     }
-    if (!kFP8 && packed_x == nullptr)
+    if (!kRows)
         return;
     ll_store_slice<kFP8, BT>(x, t, V, K, cell, first, c0, c1, b0, b1, packed_x, packed_q,
                              packed_scale);
@@ -727,7 +749,9 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
         if (log_enabled())
             log_launch("ll_dispatch one-launch T=%d H=%d K=%d E=%d: slices=%d blocks=%lld%s", T,
                        d.hidden, K, E, ny, (long long)blocks, fp8 ? " fp8" : "");
-        auto tk = fp8 ? ll_dispatch_tok_kernel<true, BT> : ll_dispatch_tok_kernel<false, BT>;
+        auto tk = fp8    ? ll_dispatch_tok_kernel<true, BT, true>
+                  : rows ? ll_dispatch_tok_kernel<false, BT, true>
+                         : ll_dispatch_tok_kernel<false, BT, false>;
         hipLaunchKernelGGL(tk, dim3(unsigned(blocks)), dim3(BT), 0, stream,
                            static_cast<const u32x4 *>(x), T, V, K, E, R, E / R, num_slots, ny,
                            topk_idx, rank_mask, static_cast<u32x4 *>(packed_x),
