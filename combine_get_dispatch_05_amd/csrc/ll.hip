@@ -177,11 +177,20 @@ __device__ __forceinline__ int ll_id_at(const int64_t *__restrict__ topk_idx, in
     return ll_valid_id(topk_idx[i < n ? i : n - 1], E);
 }
 
+// Rank of expert e >= 0 (epr experts per rank): a shift when epr is a power
+// of two (a uniform test), else a division.
+__device__ __forceinline__ int ll_rank(int e, int epr)
+{
+    if ((epr & (epr - 1)) == 0)
+        return e >> __builtin_ctz(unsigned(epr));
+    return e / epr;
+}
+
 // Index of cell (le, r, s) of expert e in the [E/R][R][S] receive layout.
 // E * S <= 8192 * 4096, so it fits an int.
 __device__ __forceinline__ int ll_cell(int e, int epr, int R, int S, int s)
 {
-    const int r = e / epr;
+    const int r = ll_rank(e, epr);
     return ((e - r * epr) * R + r) * S + s;
 }
 
@@ -417,19 +426,28 @@ __global__ __launch_bounds__(kLLBlock) void ll_copy_kernel(
 constexpr int kLLTokPairs = 4096;  // one-launch path for T*K up to this
 constexpr int kTokBlock = 512;     // threads of a one-launch workgroup
 
+// Wave-wide count of the lanes where p holds.
+__device__ __forceinline__ int ll_count(bool p)
+{
+    return __popcll(__builtin_amdgcn_ballot_w64(p));
+}
+
 // One-launch dispatch for decode-sized batches (T*K <= kLLTokPairs), same
 // results as ll_slot_kernel + ll_copy_kernel.  Workgroups [0, T*ny) are
 // token workgroups (t, slice).  The slot of pair (t, k) is the number of
-// earlier pairs, in (token, slot) order, that name its expert.  Every thread
-// loads its share of those earlier entries into registers (coalesced; 4 per
-// thread for 1024 pairs); for each k one wave ballot per register gives the
-// wave's matches, and the four waves' counts meet in LDS behind the one
-// barrier.  The slice of x[t] (its first load issued before the barrier) is
-// then stored to all K destination cells; for FP8 each 128-element block is
-// quantized once.  The remaining workgroups handle four experts each (one
-// per wave), counting with the same ballots over the whole table: the
-// expert's count and the -1 entries of its unused src_info cells.
-template <bool kFP8, int BT, bool kRows>
+// earlier pairs, in (token, slot) order, that name its expert: those of
+// earlier tokens, plus the token's own pairs before k.  Every thread holds
+// kRegs entries of the table in registers (coalesced loads, entries of
+// token t and later replaced by -1); for each k, one ballot per register
+// counts the wave's matches, and lane k keeps the count.  The waves' counts
+// meet in LDS behind the one barrier.  The token's own earlier pairs are one
+// more ballot over the lanes holding its ids.  The slice of x[t] (its first
+// load issued before any id is looked at) is then stored to all K cells; for
+// FP8 each 128-element block is quantized once.  The remaining workgroups
+// handle BT/64 experts each (one per wave), counting with the same ballots
+// over the whole table: the expert's count and the -1 entries of its unused
+// src_info cells.
+template <bool kFP8, int BT, bool kRows, int kRegs>
 __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
     const u32x4 *__restrict__ x, int T, int V, int K, int E, int R, int epr, int S, int ny,
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask,
@@ -438,7 +456,6 @@ __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
     int32_t *__restrict__ topk_slot)
 {
     constexpr int kWaves = BT / kWave;
-    constexpr int kHold = kLLTokPairs / BT;  // top-k entries per thread, at most
     __shared__ int32_t s_part[kMaxTopk][kWaves];  // per-wave match counts
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -448,27 +465,35 @@ __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
     const int ntok = T * ny;
 
     if (b >= ntok) {
-        // experts e0 .. e0+3, one per wave: matches over the whole table
+        // experts e0 .. e0 + kWaves - 1, one per wave: matches over the whole
+        // table (positions past its end hold -1)
         const int e0 = (b - ntok) * kWaves;
-        int ids[kHold];
+        int64_t raw[kRegs];
 #pragma unroll
-        for (int u0 = 0; u0 < kHold; u0 += 4) {
-            if (u0 * BT < TK) {
+        for (int u = 0; u < kRegs; ++u)
+            raw[u] = -1;
+        if (TK > 0) {  // T = 0: the counts are 0 and every cell unused
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    ids[u0 + q] = ll_id_at(topk_idx, (u0 + q) * BT + tid, TK, E);
+            for (int u = 0; u < kRegs; ++u) {
+                const int i = u * BT + tid;
+                raw[u] = topk_idx[i < TK ? i : TK - 1];
             }
         }
+        int ids[kRegs];
+#pragma unroll
+        for (int u = 0; u < kRegs; ++u)
+            ids[u] = u * BT + tid < TK ? ll_valid_id(raw[u], E) : -1;
+        int mine = 0;  // lane j: the count of expert e0 + j
 #pragma unroll
         for (int j = 0; j < kWaves; ++j) {
             int c = 0;
 #pragma unroll
-            for (int u = 0; u < kHold; ++u)
-                if (u * BT < TK)
-                    c += __popcll(wave_ballot(ids[u] == e0 + j && u * BT + tid < TK));
-            if (lane == 0)
-                s_part[j][wid] = c;
+            for (int u = 0; u < kRegs; ++u)
+                c += ll_count(ids[u] == e0 + j);
+            mine = lane == j ? c : mine;
         }
+        if (lane < kWaves)
+            s_part[lane][wid] = mine;
         __syncthreads();
         const int e = e0 + wid;
         if (e < E) {
@@ -490,24 +515,18 @@ __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
 
     const int t = b / ny;
     const int yb = b - t * ny;
-    const int base = t * K;
-    // Loads first, in this order, all in flight at once: lane k < K's own
-    // pair (t, k) (lanes past K read slot K - 1 again), the table entries
-    // that can precede one of the token's pairs (i < base + K - 1; the count
-    // below takes entries i < base + k only, so i >= lim never counts; raw,
-    // unconverted, indexes clamped), then the row slice's first vector.
+    const int base = t * K;  // pairs of earlier tokens
+    // Loads first, all in flight at once: lane k < K's own pair (t, k)
+    // (lanes past K read pair K - 1 again), the table entries of earlier
+    // tokens (indexes clamped; entries from position base on are replaced
+    // by -1 below), then the row slice's first vector.
     int64_t own_raw = topk_idx[base + (lane < K ? lane : K - 1)];
-    const int lim = base + K - 1;
-    int64_t raw[kHold];
+    const int last = base > 0 ? base - 1 : 0;
+    int64_t raw[kRegs];
 #pragma unroll
-    for (int u0 = 0; u0 < kHold; u0 += 4) {
-        if (u0 * BT < lim) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int i = (u0 + q) * BT + tid;
-                raw[u0 + q] = topk_idx[i < lim ? i : lim - 1];
-            }
-        }
+    for (int u = 0; u < kRegs; ++u) {
+        const int i = u * BT + tid;
+        raw[u] = topk_idx[i < base ? i : last];
     }
     int c0, c1, b0, b1;
     ll_slice<kFP8>(V, ny, yb, c0, c1, b0, b1);
@@ -516,46 +535,52 @@ __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
     // compiler tests each id right after its load, which makes every later
     // load -- the row slice's too -- wait for it.
     asm volatile("" : "+v"(own_raw));
-    int ids[kHold];
+    int ids[kRegs];
 #pragma unroll
-    for (int u0 = 0; u0 < kHold; u0 += 4) {
-        if (u0 * BT < lim) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                asm volatile("" : "+v"(raw[u0 + q]));
-                ids[u0 + q] = ll_valid_id(raw[u0 + q], E);
-            }
-        }
+    for (int u = 0; u < kRegs; ++u) {
+        asm volatile("" : "+v"(raw[u]));
+        ids[u] = u * BT + tid < base ? ll_valid_id(raw[u], E) : -1;
     }
     const int own = lane < K ? ll_valid_id(own_raw, E) : -1;
     bool live = own >= 0;
     if (rank_mask != nullptr && live)
-        live = rank_mask[own / epr] == 0;
+        live = rank_mask[ll_rank(own, epr)] == 0;
+    const int cell0 = live ? ll_cell(own, epr, R, S, 0) : -1;
 
-    for (int k = 0; k < K; ++k) {
-        const int ek = ll_readlane(own, k);
-        int c = 0;
-        if (ek >= 0) {
-            const int lk = base + k;  // entries before pair (t, k)
+    // lane k: matches of pair k's expert among this wave's entries (mine),
+    // and among the token's pairs before k (dup)
+    // Eight pairs per round, with no branch among them, so that their
+    // readlane -> compare -> count chains overlap.  Rounds may run past K
+    // (never past lane 63: K <= 64 and rounds start at multiples of 8); those
+    // counts land in lanes >= K, which never read them.
+    int mine = 0, dup = 0;
+    for (int k0 = 0; k0 < K; k0 += 8) {
 #pragma unroll
-            for (int u = 0; u < kHold; ++u)
-                if (u * BT < lim)
-                    c += __popcll(wave_ballot(ids[u] == ek && u * BT + tid < lk));
+        for (int j = 0; j < 8; ++j) {
+            const int k = k0 + j;
+            const int ek = ll_readlane(own, k);
+            int c = 0;
+#pragma unroll
+            for (int u = 0; u < kRegs; ++u)
+                c += ll_count(ids[u] == ek);
+            const int d = __popcll(__builtin_amdgcn_ballot_w64(own == ek) & ((1ull << k) - 1));
+            mine = lane == k ? c : mine;
+            dup = lane == k ? d : dup;
         }
-        if (lane == 0)
-            s_part[k][wid] = c;
     }
+    if (lane < K)
+        s_part[lane][wid] = mine;
     __syncthreads();
 
     int cell = -1, slot = -1;
     if (lane < K && live) {
-        int cnt = 0;
+        int cnt = dup;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
             cnt += s_part[lane][w];
         if (cnt < S) {
             slot = cnt;
-            cell = ll_cell(own, epr, R, S, cnt);
+            cell = cell0 + cnt;
         }
     }
     if (yb == 0 && wid == 0 && lane < K) {
@@ -567,6 +592,18 @@ __global__ __launch_bounds__(BT) void ll_dispatch_tok_kernel(
         return;
     ll_store_slice<kFP8, BT>(x, t, V, K, cell, first, c0, c1, b0, b1, packed_x, packed_q,
                              packed_scale);
+}
+
+// The one-launch kernel for a table of TK entries: kRegs = TK / BT rounded
+// up to a power of two.
+template <bool kFP8, int BT, bool kRows>
+auto ll_tok_kernel_for(int64_t TK)
+{
+    const int64_t regs = (TK + BT - 1) / BT;
+    return regs <= 1   ? ll_dispatch_tok_kernel<kFP8, BT, kRows, 1>
+           : regs <= 2 ? ll_dispatch_tok_kernel<kFP8, BT, kRows, 2>
+           : regs <= 4 ? ll_dispatch_tok_kernel<kFP8, BT, kRows, 4>
+                       : ll_dispatch_tok_kernel<kFP8, BT, kRows, kLLTokPairs / BT>;
 }
 
 // Packed rows are read once by the combine.
@@ -749,9 +786,9 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
         if (log_enabled())
             log_launch("ll_dispatch one-launch T=%d H=%d K=%d E=%d: slices=%d blocks=%lld%s", T,
                        d.hidden, K, E, ny, (long long)blocks, fp8 ? " fp8" : "");
-        auto tk = fp8    ? ll_dispatch_tok_kernel<true, BT, true>
-                  : rows ? ll_dispatch_tok_kernel<false, BT, true>
-                         : ll_dispatch_tok_kernel<false, BT, false>;
+        auto tk = fp8    ? ll_tok_kernel_for<true, BT, true>(TK)
+                  : rows ? ll_tok_kernel_for<false, BT, true>(TK)
+                         : ll_tok_kernel_for<false, BT, false>(TK);
         hipLaunchKernelGGL(tk, dim3(unsigned(blocks)), dim3(BT), 0, stream,
                            static_cast<const u32x4 *>(x), T, V, K, E, R, E / R, num_slots, ny,
                            topk_idx, rank_mask, static_cast<u32x4 *>(packed_x),
