@@ -33,6 +33,12 @@ namespace {
 
 constexpr int kLLBlock = 256;
 constexpr int kLLWaves = kLLBlock / kWave;
+// Threads of a workgroup that moves one row slice: the dispatch's token
+// workgroups, the copy and both combines.  All of them cut a row into the
+// same slices and number their workgroups (token, slice) in the same order.
+// Workgroup i runs on XCD i mod 8, so the combine reads each cell line on
+// the XCD whose L2 wrote it in the dispatch.
+constexpr int kTokBlock = 512;
 
 __device__ __forceinline__ int ll_wave_inclusive_scan(int v)
 {
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(kLLBlock) void ll_slot_kernel(
 // slice of x[t] once and stores it to the cells of the token's pairs, which
 // come from topk_slot.
 template <bool kFP8>
-__global__ __launch_bounds__(kLLBlock) void ll_copy_kernel(
+__global__ __launch_bounds__(kTokBlock) void ll_copy_kernel(
     const u32x4 *__restrict__ x, int V, int K, int E, int R, int epr, int S, int ny,
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ topk_slot,
     u32x4 *__restrict__ packed_x, uint2 *__restrict__ packed_q, float *__restrict__ packed_scale)
@@ -419,12 +425,11 @@ __global__ __launch_bounds__(kLLBlock) void ll_copy_kernel(
     asm volatile("" : "+v"(e_raw), "+v"(s));
     const int e = ll_valid_id(e_raw, E);
     const int cell = (lane < K && e >= 0 && s >= 0 && s < S) ? ll_cell(e, epr, R, S, s) : -1;
-    ll_store_slice<kFP8, kLLBlock>(x, t, V, K, cell, first, c0, c1, b0, b1, packed_x, packed_q,
+    ll_store_slice<kFP8, kTokBlock>(x, t, V, K, cell, first, c0, c1, b0, b1, packed_x, packed_q,
                                    packed_scale);
 }
 
 constexpr int kLLTokPairs = 4096;  // one-launch path for T*K up to this
-constexpr int kTokBlock = 512;     // threads of a one-launch workgroup
 
 // Wave-wide count of the lanes where p holds.
 __device__ __forceinline__ int ll_count(bool p)
@@ -633,24 +638,24 @@ __device__ __forceinline__ void ll_pair_cells(int64_t t, int K, int E, int R, in
     }
 }
 
-// One workgroup per (token, chunk of 256 vectors).  Each wave resolves the
-// token's K cells itself (lanes 0..K-1, no LDS, no barrier); each lane then
-// issues its K loads before the fused multiply-adds, which run in ascending
-// slot order from +0.
-constexpr int kCombBlock = 256;  // threads of a combine workgroup (one 16-byte vector each)
-
-template <int BT>
-__global__ __launch_bounds__(BT) void ll_combine_kernel(
-    const u32x4 *__restrict__ packed_y, int V, int K, int E, int R, int epr, int S,
+// One workgroup per (token, row slice), the dispatch's slices in the
+// dispatch's order (kTokBlock).  Each wave resolves the token's K cells
+// itself (lanes 0..K-1, no LDS, no barrier); each lane then issues its K
+// loads before the fused multiply-adds, which run in ascending slot order
+// from +0.
+__global__ __launch_bounds__(kTokBlock) void ll_combine_kernel(
+    const u32x4 *__restrict__ packed_y, int V, int K, int E, int R, int epr, int S, int ny,
     const int64_t *__restrict__ topk_idx, const float *__restrict__ topk_weights,
     const int32_t *__restrict__ topk_slot, const int32_t *__restrict__ rank_mask,
     u32x4 *__restrict__ out)
 {
-    const int64_t t = blockIdx.x;
+    const int64_t t = blockIdx.x / ny;
+    int c0, c1, b0, b1;
+    ll_slice<false>(V, ny, int(blockIdx.x - t * ny), c0, c1, b0, b1);
+    const int idx = c0 + threadIdx.x;  // this lane's vector of the row
     int cell;
     float w;
     ll_pair_cells(t, K, E, R, epr, S, topk_idx, topk_weights, topk_slot, rank_mask, cell, w);
-    const int idx = blockIdx.y * BT + threadIdx.x;
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -663,8 +668,8 @@ __global__ __launch_bounds__(BT) void ll_combine_kernel(
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
             ck[g] = k0 + g < K ? ll_readlane(cell, k0 + g) : -1;
-            v[g] = (ck[g] >= 0 && idx < V) ? ll_load_row(packed_y + int64_t(ck[g]) * V + idx)
-                                           : u32x4{0, 0, 0, 0};
+            v[g] = (ck[g] >= 0 && idx < c1) ? ll_load_row(packed_y + int64_t(ck[g]) * V + idx)
+                                            : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
@@ -678,7 +683,7 @@ __global__ __launch_bounds__(BT) void ll_combine_kernel(
             }
         }
     }
-    if (idx < V) {
+    if (idx < c1) {
         u32x4 rv;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -692,19 +697,24 @@ __global__ __launch_bounds__(BT) void ll_combine_kernel(
 // 8-byte word of codes per cell); each code is decoded exactly with the
 // packed hardware conversion (checked against the e4m3 definition for all
 // 256 codes), multiplied by its block's scale in fp32, and added with the
-// same fma sum in ascending k as the bf16 combine.
-__global__ __launch_bounds__(kLLBlock) void ll_combine_fp8_kernel(
+// same fma sum in ascending k as the bf16 combine.  Workgroups as in the
+// bf16 combine: (token, slice of blocks), the FP8 dispatch's slices in its
+// order; lane j of a slice takes group 16 * b0 + j, as in the dispatch.
+__global__ __launch_bounds__(kTokBlock) void ll_combine_fp8_kernel(
     const uint2 *__restrict__ packed_q, const float *__restrict__ packed_scale, int V, int K,
-    int E, int R, int epr, int S, const int64_t *__restrict__ topk_idx,
+    int E, int R, int epr, int S, int ny, const int64_t *__restrict__ topk_idx,
     const float *__restrict__ topk_weights, const int32_t *__restrict__ topk_slot,
     const int32_t *__restrict__ rank_mask, u32x4 *__restrict__ out)
 {
-    const int64_t t = blockIdx.x;
+    const int64_t t = blockIdx.x / ny;
+    int c0, c1, b0, b1;
+    ll_slice<true>(V, ny, int(blockIdx.x - t * ny), c0, c1, b0, b1);
+    const int idx = 16 * b0 + threadIdx.x;  // 8-element group of the row
+    const int lim = 16 * b1;
+    const int nb = V / 16;  // 128-element blocks per row
     int cell;
     float w;
     ll_pair_cells(t, K, E, R, epr, S, topk_idx, topk_weights, topk_slot, rank_mask, cell, w);
-    const int idx = blockIdx.y * kLLBlock + threadIdx.x;  // 8-element group of the row
-    const int nb = V / 16;                                 // 128-element blocks per row
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
@@ -718,7 +728,7 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_fp8_kernel(
 #pragma unroll
         for (int g = 0; g < kGroup; ++g) {
             ck[g] = k0 + g < K ? ll_readlane(cell, k0 + g) : -1;
-            const bool live = ck[g] >= 0 && idx < V;
+            const bool live = ck[g] >= 0 && idx < lim;
             c[g] = live ? packed_q[int64_t(ck[g]) * V + idx] : make_uint2(0, 0);
             sc[g] = live ? packed_scale[int64_t(ck[g]) * nb + idx / 16] : 0.0f;
         }
@@ -739,7 +749,7 @@ __global__ __launch_bounds__(kLLBlock) void ll_combine_fp8_kernel(
             }
         }
     }
-    if (idx < V) {
+    if (idx < lim) {
         u32x4 rv;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -796,7 +806,7 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
                            topk_slot);
         return hipGetLastError();
     }
-    const int ny = ll_slices(V, fp8, rows, kLLBlock);
+    const int ny = ll_slices(V, fp8, rows, kTokBlock);
     if (log_enabled())
         log_launch("ll_dispatch slot scan + copy T=%d H=%d K=%d E=%d: slot blocks=%d copy "
                    "blocks=%lld%s",
@@ -807,7 +817,7 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
     if (e != hipSuccess || !rows || T == 0)
         return e;
     auto ck = fp8 ? ll_copy_kernel<true> : ll_copy_kernel<false>;
-    hipLaunchKernelGGL(ck, dim3(unsigned(int64_t(T) * ny)), dim3(kLLBlock), 0, stream,
+    hipLaunchKernelGGL(ck, dim3(unsigned(int64_t(T) * ny)), dim3(kTokBlock), 0, stream,
                        static_cast<const u32x4 *>(x), V, K, E, R, E / R, num_slots, ny, topk_idx,
                        topk_slot, static_cast<u32x4 *>(packed_x), static_cast<uint2 *>(packed_q),
                        packed_scale);
@@ -823,14 +833,14 @@ hipError_t launch_ll_combine_fp8(const ep_dims &d, int num_slots, const void *pa
         return hipSuccess;
     const int E = d.num_experts, R = d.num_ranks;
     const int V = d.hidden / 8;
-    const int chunks = (V + kLLBlock - 1) / kLLBlock;
+    const int ny = ll_slices(V, true, true, kTokBlock);
     if (log_enabled())
-        log_launch("ll_combine fp8 T=%d H=%d K=%d: grid=%dx%d", d.num_tokens, d.hidden,
-                   d.num_topk, d.num_tokens, chunks);
-    hipLaunchKernelGGL(ll_combine_fp8_kernel, dim3(d.num_tokens, chunks), dim3(kLLBlock), 0,
-                       stream, static_cast<const uint2 *>(packed_q), packed_scale, V, d.num_topk,
-                       E, R, E / R, num_slots, topk_idx, topk_weights, topk_slot, rank_mask,
-                       static_cast<u32x4 *>(out));
+        log_launch("ll_combine fp8 T=%d H=%d K=%d: slices=%d blocks=%lld", d.num_tokens,
+                   d.hidden, d.num_topk, ny, (long long)d.num_tokens * ny);
+    hipLaunchKernelGGL(ll_combine_fp8_kernel, dim3(unsigned(int64_t(d.num_tokens) * ny)),
+                       dim3(kTokBlock), 0, stream, static_cast<const uint2 *>(packed_q),
+                       packed_scale, V, d.num_topk, E, R, E / R, num_slots, ny, topk_idx,
+                       topk_weights, topk_slot, rank_mask, static_cast<u32x4 *>(out));
     return hipGetLastError();
 }
 
@@ -843,15 +853,14 @@ hipError_t launch_ll_combine(const ep_dims &d, int num_slots, const void *packed
         return hipSuccess;
     const int E = d.num_experts, R = d.num_ranks;
     const int V = d.hidden / 8;
-    constexpr int BT = kCombBlock;
-    const int chunks = (V + BT - 1) / BT;
+    const int ny = ll_slices(V, false, true, kTokBlock);
     if (log_enabled())
-        log_launch("ll_combine T=%d H=%d K=%d: grid=%dx%d", d.num_tokens, d.hidden, d.num_topk,
-                   d.num_tokens, chunks);
-    hipLaunchKernelGGL(ll_combine_kernel<BT>, dim3(d.num_tokens, chunks), dim3(BT), 0,
-                       stream, static_cast<const u32x4 *>(packed_y), V, d.num_topk, E, R, E / R,
-                       num_slots, topk_idx, topk_weights, topk_slot, rank_mask,
-                       static_cast<u32x4 *>(out));
+        log_launch("ll_combine T=%d H=%d K=%d: slices=%d blocks=%lld", d.num_tokens, d.hidden,
+                   d.num_topk, ny, (long long)d.num_tokens * ny);
+    hipLaunchKernelGGL(ll_combine_kernel, dim3(unsigned(int64_t(d.num_tokens) * ny)),
+                       dim3(kTokBlock), 0, stream, static_cast<const u32x4 *>(packed_y), V,
+                       d.num_topk, E, R, E / R, num_slots, ny, topk_idx, topk_weights, topk_slot,
+                       rank_mask, static_cast<u32x4 *>(out));
     return hipGetLastError();
 }
 
