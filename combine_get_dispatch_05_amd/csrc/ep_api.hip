@@ -290,10 +290,10 @@ void arena_put(int dev, Arena a, hipStream_t stream)
 // ------------------------------------------------------- pinned N slots
 //
 // N goes back to the host through pinned, coherent host memory: on a fresh
-// dispatch the layout kernel stores it there directly (a system-scope
-// store), so no copy is enqueued, and the host synchronizes the stream once.
-// (Polling the slot instead of synchronizing was measured no faster.)
-// Slots come from a process-wide free list (pages of kSlotsPerPage,
+// dispatch the layout's count kernel stores it there directly (a
+// system-scope store, once, as soon as the counts are known), so no copy is
+// enqueued and the host need not wait for the position kernel: it polls the
+// slot.  Slots come from a process-wide free list (pages of kSlotsPerPage,
 // allocated once, never released) and are held only for the duration of one
 // call.
 
@@ -351,6 +351,30 @@ void slot_put(const Slot &slot)
     SlotPool &P = slot_pool();
     std::lock_guard<std::mutex> g(P.mu);
     P.free.push_back(slot);
+}
+
+// Waits for the GPU to store a value into the slot.  Every kSlotQueryEvery
+// polls it also asks whether the stream is still working: a stream that has
+// finished (or failed) without storing one ends the wait with an error.
+constexpr unsigned kSlotQueryEvery = 256;
+
+hipError_t slot_wait(const Slot &slot, hipStream_t stream, int64_t *v)
+{
+    for (unsigned i = 1;; ++i) {
+        *v = __atomic_load_n(slot.host, __ATOMIC_ACQUIRE);
+        if (*v != kNoValue)
+            return hipSuccess;
+        if (i % kSlotQueryEvery == 0) {
+            const hipError_t q = hipStreamQuery(stream);
+            if (q != hipErrorNotReady) {
+                *v = __atomic_load_n(slot.host, __ATOMIC_ACQUIRE);
+                if (*v != kNoValue)
+                    return hipSuccess;
+                return q == hipSuccess ? hipErrorUnknown : q;
+            }
+        }
+        __builtin_ia32_pause();
+    }
 }
 
 
@@ -473,16 +497,28 @@ int create_handle(const ep_dims &d, const int64_t *topk_idx, const int32_t *rank
         return hip_fail(e);
     }
     if (want_n) {
-        // the layout kernel stores N into the slot: one stream synchronization
-        // (measured faster than polling the slot from the host)
-        hipError_t e2 = hipStreamSynchronize(stream);
-        const int64_t n = __atomic_load_n(slot.host, __ATOMIC_ACQUIRE);
-        slot_put(slot);
-        rc = e2 != hipSuccess ? hip_fail(e2) : (n == kNoValue ? hip_fail(hipErrorUnknown) : EP_OK);
-        if (rc != EP_OK) {
-            ep_handle_free(h);
-            return rc;
+        // the layout stores N into the slot once.  Two kernels: the count
+        // kernel does, and the host polls for it while the positions are
+        // still being written.  One launch: N comes at its end, and one
+        // stream synchronization was measured faster than polling.
+        int64_t n = kNoValue;
+        hipError_t e2;
+        if (h->shape.fused) {
+            e2 = hipStreamSynchronize(stream);
+            n = __atomic_load_n(slot.host, __ATOMIC_ACQUIRE);
+            if (e2 == hipSuccess && n == kNoValue)
+                e2 = hipErrorUnknown;
+        } else {
+            e2 = slot_wait(slot, stream, &n);
         }
+        if (e2 != hipSuccess) {
+            // nothing stores into the slot any more: the stream has ended
+            (void)hipStreamSynchronize(stream);
+            slot_put(slot);
+            ep_handle_free(h);
+            return hip_fail(e2);
+        }
+        slot_put(slot);
         h->num_recv.store(n);
     }
     *out = h;

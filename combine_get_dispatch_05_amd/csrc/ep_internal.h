@@ -29,7 +29,7 @@ constexpr int kMaxHidden = 1 << 20;
 constexpr int kArenaFields = 17;
 constexpr size_t kLayoutCtrBytes = 256;
 struct LayoutBufs {
-    uint64_t *layout_ctr;                // [4] tickets, count units done, -, wait-timeout flag
+    uint64_t *layout_ctr;                // [4] tickets, count units done, count blocks done, wait-timeout flag
     int32_t *num_tokens_per_rank;        // [R]
     int32_t *num_tokens_per_expert;      // [E]
     uint8_t *is_token_in_rank;           // [T][R]
@@ -71,11 +71,14 @@ void log_launch(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
 struct LayoutCounters {
     uint64_t tickets = 0;
     uint64_t done = 0;
+    uint64_t counted = 0;  // count blocks that summed into the early N
 };
 
 // rank_mask [R] int32 (nullable): nonzero ranks are masked.  num_recv_host
-// (nullable): pinned, coherent host memory that also receives N, so that a
-// caller waiting for N can poll it instead of copying it back.
+// (nullable): pinned, coherent host memory that also receives N, exactly
+// once, so that a caller waiting for N can poll it instead of copying it
+// back.  On the two-kernel path the count kernel's last block stores it, as
+// soon as the counts are known and before the positions are.
 hipError_t launch_layout(const LayoutShape &s, const int64_t *topk_idx, const int32_t *rank_mask,
                          const LayoutBufs &b, int64_t *num_recv_host, LayoutCounters &lc,
                          hipStream_t stream);

@@ -255,15 +255,55 @@ __device__ __forceinline__ void count_body(
         blk_ecount[size_t(blk) * E + i] = s_ecount[i];
 }
 
+// With num_recv_host (a caller waiting for N), each block then bumps a
+// done counter (ctr[2], which only grows: counted_base is its value before
+// this launch), and the block that finishes last sums every block's per-rank
+// counts -- N is their sum -- and stores N into that pinned host memory
+// while the position kernel is still to run.
 template <int NW>
 __global__ __launch_bounds__(kCountBlock) void layout_count_kernel(
     const int64_t *__restrict__ topk_idx, const int32_t *__restrict__ rank_mask, int T, int K,
     int E, int R, int epr, int epr_shift, int nW, uint64_t *__restrict__ wave_mask,
     int32_t *__restrict__ wave_base, int32_t *__restrict__ blk_count,
-    int32_t *__restrict__ blk_ecount)
+    int32_t *__restrict__ blk_ecount, uint64_t *__restrict__ ctr, uint64_t counted_base,
+    int64_t *num_recv_host)
 {
     count_body<NW, kCountBlock>(blockIdx.x, topk_idx, rank_mask, T, K, E, R, epr, epr_shift, nW,
                                 wave_mask, wave_base, blk_count, blk_ecount);
+    if (num_recv_host == nullptr)
+        return;
+    constexpr int kWaves = kCountBlock / kWave;
+    __shared__ int s_last;
+    __shared__ int64_t s_part[kWaves];
+    const int tid = threadIdx.x;
+    __syncthreads();  // every wave's blk_count stores are done
+    if (tid == 0) {
+        const uint64_t before = __hip_atomic_fetch_add(&ctr[2], uint64_t(1), __ATOMIC_RELEASE,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+        s_last = before - counted_base == uint64_t(gridDim.x - 1);
+        if (s_last)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    const int n = int(gridDim.x) * R;
+    int64_t sum = 0;
+    for (int i = tid; i < n; i += kCountBlock)
+        sum += blk_count[i];
+#pragma unroll
+    for (int sft = kWave / 2; sft > 0; sft >>= 1)
+        sum += __shfl_xor((long long)sum, sft, kWave);
+    if ((tid & (kWave - 1)) == 0)
+        s_part[tid >> 6] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int64_t N = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            N += s_part[w];
+        __hip_atomic_store(num_recv_host, N, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
 }
 
 constexpr int kPosBlock = 256;
@@ -719,17 +759,26 @@ hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
         }
         return e;
     }
-    if (s.T > 0)
+    // N for the host: from the count kernel when there is one, else (no
+    // tokens) from the scan kernel, which then writes the whole layout
+    if (s.T > 0) {
         hipLaunchKernelGGL(layout_count_kernel<NW>, dim3(s.nB), dim3(kCountBlock),
                            size_t(s.E) * sizeof(int32_t), stream, topk_idx, rank_mask, s.T, s.K, s.E, s.R,
                            s.epr, epr_shift, s.nW, b.wave_mask, b.wave_base, b.blk_count,
-                           b.blk_ecount);
+                           b.blk_ecount, b.layout_ctr, lc.counted, num_recv_host);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        if (num_recv_host != nullptr)
+            lc.counted += unsigned(s.nB);
+    }
+    int64_t *const totals_host = s.T > 0 ? nullptr : num_recv_host;
     const bool self_scan = s.T > 0 && s.nB <= kSelfScanBlocks;
     if (!self_scan)
         hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kPosBlock), 0, stream, s.T, s.E, s.R,
                            s.C, s.nB, b.blk_count, b.blk_ecount, b.num_tokens_per_rank,
                            b.num_tokens_per_expert, b.rank_prefix_matrix, b.channel_prefix_matrix,
-                           b.recv_channel_prefix_matrix, b.num_recv, num_recv_host);
+                           b.recv_channel_prefix_matrix, b.num_recv, totals_host);
     auto pos_kernel = self_scan ? layout_pos_kernel<NW, true> : layout_pos_kernel<NW, false>;
     if (s.T > 0)
         hipLaunchKernelGGL(pos_kernel, dim3(unsigned(s.nW) << sub_shift), dim3(kPosBlock), 0, stream,
@@ -737,7 +786,7 @@ hipError_t launch_layout_nw(const LayoutShape &s, const int64_t *topk_idx,
                            b.blk_ecount, b.is_token_in_rank, b.send_head, b.recv_src_idx,
                            b.dst_row, b.dst_rank, b.num_tokens_per_rank, b.num_tokens_per_expert,
                            b.rank_prefix_matrix, b.channel_prefix_matrix,
-                           b.recv_channel_prefix_matrix, b.num_recv, num_recv_host);
+                           b.recv_channel_prefix_matrix, b.num_recv, totals_host);
     return hipGetLastError();
 }
 
