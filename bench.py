@@ -487,9 +487,10 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     T, H, K = tr.T, tr.H, tr.K
     s = abi.current_stream()
     # The layout with the N readback a fresh dispatch of unknown size needs
-    # (ep_dispatch asked for N only: the layout kernel stores N into pinned
-    # host memory, and the call synchronizes once), host wall time per call;
-    # and the same through a handle made without it (N copied back later).
+    # (ep_dispatch asked for N only: the count kernel stores N into pinned
+    # host memory and the host polls it), host wall time per call, in a loop
+    # and on an idle stream; and the same through a handle made without it
+    # (N copied back later, one stream sync).
     def fresh_size_query():
         hl = ctypes.c_void_p()
         nn = ctypes.c_int64()
@@ -513,10 +514,25 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
         for _ in range(args.steps):
             fn()
         return (time.perf_counter() - t0) * 1e6 / args.steps
+    def idle_us(fn):
+        for _ in range(max(args.warmup, 2)):
+            fn()
+        tot = 0.0
+        for _ in range(args.steps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            tot += time.perf_counter() - t0
+        torch.cuda.synchronize()
+        return tot * 1e6 / args.steps
     us = host_us(fresh_size_query)
+    us_idle = idle_us(fresh_size_query)
     rep["layout_with_n_readback"] = {"avg_us": round(us, 2), "mtok_s": round(T / us, 2),
-                                     "how": "ep_dispatch size query (layout kernel stores N "
-                                            "into pinned host memory, one stream sync)"}
+                                     "idle_stream_us": round(us_idle, 2),
+                                     "how": "ep_dispatch size query (the count kernel stores N "
+                                            "into pinned host memory, the host polls it); "
+                                            "avg_us: calls back to back, idle_stream_us: each "
+                                            "call made on an idle stream"}
     us = host_us(layout_then_n)
     rep["layout_then_handle_num_recv"] = {"avg_us": round(us, 2),
                                           "how": "ep_get_dispatch_layout, then ep_handle_num_recv "

@@ -52,6 +52,7 @@ def test_bench_line_keeps_the_contract():
 
     # informational parts: the layout with its N readback, the other workloads
     assert b["next"]["layout_with_n_readback"]["avg_us"] > 0
+    assert b["next"]["layout_with_n_readback"]["idle_stream_us"] > 0
     for name in ("skewed", "large"):
         wl = b["workloads"][name]
         assert wl["N"] > 0 and wl["combine_gbs"] > 0 and wl["dispatch_cached_gbs"] > 0
