@@ -128,8 +128,9 @@ int64_t ep_max_recv_rows(const ep_dims *dims);
  *
  * out (nullable): fields that are non-NULL receive copies of the layout.  If
  *   out->recv_src_idx is non-NULL and recv_src_cap < ep_max_recv_rows(), the
- *   call waits for N (the layout kernel stores it into pinned host memory,
- *   which the host polls) and returns EP_ERR_CAPACITY if N > recv_src_cap;
+ *   call waits for N (the layout's count kernel stores it into pinned host
+ *   memory, which the host polls; the positions may still be being written
+ *   when it returns) and returns EP_ERR_CAPACITY if N > recv_src_cap;
  *   then no output in `out` is written and no handle is returned (*handle_out
  *   is left unchanged; the layout's memory returns to the pool).
  * handle_out (nullable): receives a new handle holding the layout.  Such a
@@ -196,8 +197,9 @@ int ep_get_dispatch_layout_noalloc(const ep_dims *dims, const int64_t *topk_idx,
  *   host synchronization is needed to check it.
  * num_recv (HOST pointer, nullable): receives N; asking for it waits once
  *   per handle (later calls use the cached value).  On a fresh dispatch the
- *   layout kernel stores N into pinned host memory, which the host polls
- *   (no copy is enqueued); on a handle made earlier N is copied there once.
+ *   layout's count kernel stores N into pinned host memory, which the host
+ *   polls (no copy is enqueued, and the call does not wait for the position
+ *   kernel); on a handle made earlier N is copied there once and polled.
  * On any error of a fresh dispatch the new handle is released again and
  *   *handle is left NULL (the layout may already be enqueued; its memory
  *   returns to the pool in stream order).
@@ -350,7 +352,9 @@ int ep_lb_reduce_grads(const void *redundant_grads, void *expert_grads, const in
  * shapes and capacity rule as ep_get_dispatch_layout. */
 int ep_handle_copy_layout(ep_handle *handle, ep_layout_out *out, ep_stream_t stream);
 
-/* N of the handle.  Synchronizes the handle's last stream the first time. */
+/* N of the handle.  The first time, waits for the handle's last stream to
+ * reach the copy of N into pinned host memory (work enqueued after it may
+ * still be running when the call returns); later calls use the cached value. */
 int ep_handle_num_recv(ep_handle *handle, int64_t *num_recv);
 
 /* The handle's dims (host copy). */
