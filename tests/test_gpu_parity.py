@@ -395,6 +395,10 @@ def test_ep_log_lines(monkeypatch, capfd):
     err = capfd.readouterr().err
     for tag in ("[ep] layout T=128", "[ep] dispatch_pack T=128", "[ep] combine T=128"):
         assert tag in err, err
+    # the rows-only dispatch through the handle logs the scatter kernel
+    buf.dispatch(x, handle=h)
+    torch.cuda.synchronize()
+    assert "[ep] dispatch_scatter T=128" in capfd.readouterr().err
     h.free()
     monkeypatch.delenv("EP_LOG")
     _, _, _, _, h2, _ = buf.dispatch(x, topk, w)
