@@ -272,8 +272,8 @@ def main():
     # the largest byte count of the step), timed with events over K steps.
     dom_us = float(np.mean(roof_us))
     achieved = by["dispatch"] / (dom_us * 1e-6) / 1e9
-    traffic = load_traffic("dispatch.hip", "dispatch:dispatch_pack_kernel")
-    roofline = {"bound": "hbm", "kernel": "dispatch_pack_kernel (dispatch with top-k outputs)",
+    traffic = load_traffic("dispatch.hip", "dispatch:dispatch_scatter_kernel")
+    roofline = {"bound": "hbm", "kernel": "dispatch_scatter_kernel (dispatch with top-k outputs)",
                 "avg_us": round(dom_us, 2), "timed_over": f"{args.steps} steps, events around the "
                 "dispatch call only", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}

@@ -9,12 +9,12 @@
 // outputs is the handle-reuse fast path of "How DeepEP Optimizes Handle
 // Reuse for Repeated Dispatches" ("Fast Path Dispatch with Handle Reuse").
 //
-// Two kernels give the same rows.  dispatch_scatter_kernel (the default for
-// the rows-only, handle-reuse dispatch) is destination-major: one thread per
-// 16-byte vector of a few destination rows, with workgroups dealt to XCDs so
-// that each token row is read from HBM once and re-read from L2 (see the
-// kernel).  The token-major kernel below is the default for the dispatch
-// with top-k outputs.
+// Two kernels give the same rows.  dispatch_scatter_kernel (the default) is
+// destination-major: one thread per 16-byte vector of a few destination
+// rows, with workgroups dealt to XCDs so that each token row is read from
+// HBM once and re-read from L2 (see the kernel).  The token-major kernel
+// below stays as a set of tuning shapes and as the fallback for grids too
+// large for the first.
 //
 // Token-major: a group of G lanes (one or more whole wavefronts) owns one
 // token.  It reads the token's row from HBM once into VGPRs (VPT 16-byte
@@ -107,7 +107,8 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
     const int32_t *__restrict__ dst_row, const int32_t *__restrict__ dst_rank,
     const int64_t *__restrict__ topk_idx, const float *__restrict__ topk_weights,
     u32x4 *__restrict__ recv_x, int64_t *__restrict__ recv_topk_idx,
-    float *__restrict__ recv_topk_weights)
+    float *__restrict__ recv_topk_weights, const int32_t *__restrict__, const int32_t *__restrict__,
+    int, int)
 {
     constexpr int kGroups = kPackBlock / G;
     const int lane = threadIdx.x & (kWave - 1);
@@ -184,8 +185,16 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
 // destinations.  Every thread issues one 16-byte load and kDestGroup 16-byte
 // nontemporal stores.  Many short workgroups with few stores each write HBM
 // faster than long-lived groups that each store a row many times: rows-only
-// dispatch at 4096 tokens, H = 7168, R = 64, x cold, 97 against 104 us.  The
-// chunk-0 workgroup of a destination writes its top-k outputs.
+// dispatch at 4096 tokens, H = 7168, R = 64, x cold, 97 against 104 us.
+//
+// With top-k outputs the first ntk workgroups (a multiple of 8, so the row
+// workgroups keep their XCDs) write them row-major: BT / K consecutive
+// destination rows each, lane (row, k) -- the row's source token from
+// recv_src_idx, its rank by a binary search of the rank segment ends
+// (rank_prefix_matrix, whose last entry is N).  Every line of the top-k
+// outputs is then written by one workgroup; written by the row workgroups
+// instead (one 64- and one 32-byte piece per row and workgroup) they cost
+// 13 us at the training-scale batch.
 constexpr int kDestGroup = 2;
 
 template <int BT, bool kTopk>
@@ -194,9 +203,42 @@ __global__ __launch_bounds__(BT) void dispatch_scatter_kernel(
     const int32_t *__restrict__ dst_row, const int32_t *__restrict__ dst_rank,
     const int64_t *__restrict__ topk_idx, const float *__restrict__ topk_weights,
     u32x4 *__restrict__ recv_x, int64_t *__restrict__ recv_topk_idx,
-    float *__restrict__ recv_topk_weights)
+    float *__restrict__ recv_topk_weights, const int32_t *__restrict__ recv_src_idx,
+    const int32_t *__restrict__ rank_prefix, int R, int ntk)
 {
-    const unsigned b = blockIdx.x;
+    unsigned b = blockIdx.x;
+    if (kTopk) {
+        if (b < unsigned(ntk)) {
+            __shared__ int32_t s_end[kMaxRanks];
+            const int tid = threadIdx.x;
+            for (int r = tid; r < R; r += BT)
+                s_end[r] = rank_prefix[r];
+            __syncthreads();
+            const int q = BT / K;  // rows of this workgroup
+            const int jr = tid / K;
+            const int k = tid - jr * K;
+            const int64_t j = int64_t(b) * q + jr;
+            if (jr >= q || j >= s_end[R - 1])
+                return;
+            int lo = 0, hi = R - 1;  // rank of row j: the first segment ending past it
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_end[mid] > j)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            const int64_t t = recv_src_idx[j];
+            const int64_t e = topk_idx[t * K + k];
+            const bool mine = e >= 0 && e < E && int(e) / epr == lo;
+            if (recv_topk_idx != nullptr)
+                recv_topk_idx[j * K + k] = mine ? e - int64_t(lo) * epr : -1;
+            if (recv_topk_weights != nullptr)
+                recv_topk_weights[j * K + k] = mine ? topk_weights[t * K + k] : 0.0f;
+            return;
+        }
+        b -= unsigned(ntk);
+    }
     const unsigned groups = unsigned((kmax + kDestGroup - 1) / kDestGroup);
     const unsigned per_tok = groups * unsigned(ny);
     const unsigned i = b >> 3;
@@ -212,6 +254,8 @@ __global__ __launch_bounds__(BT) void dispatch_scatter_kernel(
     u32x4 v = {0, 0, 0, 0};
     if (recv_x != nullptr)
         v = x[int64_t(t) * V + (c < V ? c : V - 1)];
+    if (recv_x == nullptr || c >= V)
+        return;
     for (int j = 0; j < kDestGroup; ++j) {
         const int k = g * kDestGroup + j;
         if (k >= kmax)
@@ -219,18 +263,7 @@ __global__ __launch_bounds__(BT) void dispatch_scatter_kernel(
         const int row = dst_row[int64_t(t) * kmax + k];  // rows are packed first, then -1
         if (row < 0)
             break;
-        if (recv_x != nullptr && c < V)
-            __builtin_nontemporal_store(v, recv_x + int64_t(row) * V + c);
-        if (kTopk && yb == 0 && int(threadIdx.x) < K) {
-            const int r = dst_rank[int64_t(t) * kmax + k];
-            const int64_t e = topk_idx[int64_t(t) * K + threadIdx.x];
-            const bool mine = e >= 0 && e < E && int(e) / epr == r;
-            if (recv_topk_idx != nullptr)
-                recv_topk_idx[int64_t(row) * K + threadIdx.x] = mine ? e - int64_t(r) * epr : -1;
-            if (recv_topk_weights != nullptr)
-                recv_topk_weights[int64_t(row) * K + threadIdx.x] =
-                    mine ? topk_weights[int64_t(t) * K + threadIdx.x] : 0.0f;
-        }
+        __builtin_nontemporal_store(v, recv_x + int64_t(row) * V + c);
     }
 }
 
@@ -238,7 +271,7 @@ __global__ __launch_bounds__(BT) void dispatch_scatter_kernel(
 // chunk count ny where the token-major kernel takes S.
 typedef void (*PackFn)(const u32x4 *, int, int, int, int, int, int, int, const int32_t *,
                        const int32_t *, const int64_t *, const float *, u32x4 *, int64_t *,
-                       float *);
+                       float *, const int32_t *, const int32_t *, int, int);
 
 // A launch shape.  Token-major: G lanes per group, VPT vectors per lane, S
 // groups per token (row slices), NTS / NTL nontemporal stores / loads, P
@@ -275,25 +308,32 @@ int pack_code(const PackCfg &c)
     return c.scatter * 10000 + c.S * 1000 + c.NTL * 100 + c.NTS * 10 + c.P / 256;
 }
 
-// Workgroups of the scatter kernel for this shape, or 0 when the grid
-// would not fit (the token-major kernel then takes the launch).
+// Top-k writer workgroups of the scatter kernel: BT / K rows each for the
+// T * kmax rows there can be, rounded up to a multiple of 8.
+int64_t scatter_topk_blocks(const LayoutShape &s, int bt)
+{
+    const int64_t q = bt / s.K;
+    const int64_t n = (int64_t(s.T) * s.kmax + q - 1) / q;
+    return (n + 7) / 8 * 8;
+}
+
+// Workgroups of the scatter kernel's rows for this shape, or 0 when the
+// grid (with its top-k writers) would not fit (the token-major kernel then
+// takes the launch).
 int64_t scatter_blocks(const LayoutShape &s, int V, int bt)
 {
     const int64_t ny = (V + bt - 1) / bt;
     const int64_t b = int64_t((s.T + 7) / 8) * 8 * ((s.kmax + kDestGroup - 1) / kDestGroup) * ny;
-    return b < (int64_t(1) << 31) ? b : 0;
+    return b + scatter_topk_blocks(s, bt) < (int64_t(1) << 31) ? b : 0;
 }
 
 std::atomic<int> g_over_g{-2}, g_over_v{-1}, g_over_c{-1};  // -2: env not read yet
 
 // Launch shape for a row of V vectors.  An override (ep_set_tuning, or the
 // env var EP_TUNE_DISPATCH="G,VPT,code") wins; results never depend on it.
-// Otherwise: the rows-only dispatch takes the scatter kernel with 448
-// threads per workgroup; the dispatch with top-k outputs (where the scatter
-// kernel measured 9 us slower at the training-scale batch: 112 against
-// 103 us) and a grid too large for the scatter kernel take the token-major
-// kernel, with one chunk that covers the row exactly, the most lanes,
-// nontemporal stores and one group per token.
+// Otherwise the scatter kernel with 448 threads per workgroup; a grid too
+// large for it takes the token-major kernel, with one chunk that covers the
+// row exactly, the most lanes, nontemporal stores and one group per token.
 const PackCfg &pick_token_major(int V)
 {
     for (int G : {128, 256, 64})
@@ -307,7 +347,7 @@ const PackCfg &pick_token_major(int V)
     return kPackCfgs[2];
 }
 
-const PackCfg &pick(const LayoutShape &s, int V, bool topk)
+const PackCfg &pick(const LayoutShape &s, int V)
 {
     if (g_over_g.load() == -2) {
         int g = -1, v = -1, c = -1;
@@ -322,7 +362,7 @@ const PackCfg &pick(const LayoutShape &s, int V, bool topk)
     for (const PackCfg &c : kPackCfgs)
         if (c.G == og && c.VPT == ov && pack_code(c) == oc)
             return c.scatter && scatter_blocks(s, V, c.G) == 0 ? pick_token_major(V) : c;
-    if (!topk && scatter_blocks(s, V, kPackCfgs[1].G) > 0)
+    if (scatter_blocks(s, V, kPackCfgs[1].G) > 0)
         return kPackCfgs[1];  // scatter, 448 threads
     return pick_token_major(V);
 }
@@ -364,17 +404,20 @@ hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, cons
         return hipSuccess;
     const int V = hidden / 8;
     const bool topk = recv_topk_idx != nullptr || recv_topk_weights != nullptr;
-    const PackCfg &c = pick(s, V, topk);
+    const PackCfg &c = pick(s, V);
     if (c.scatter) {
         const int ny = (V + c.G - 1) / c.G;
-        const int64_t blocks = scatter_blocks(s, V, c.G);
+        // top-k writers: BT / K rows each, for the T * kmax rows there can be
+        const int64_t ntk = topk ? scatter_topk_blocks(s, c.G) : 0;
+        const int64_t blocks = scatter_blocks(s, V, c.G) + ntk;
         if (log_enabled())
             log_launch("dispatch_scatter T=%d H=%d K=%d R=%d: BT=%d chunks=%d blocks=%lld%s",
                        s.T, hidden, s.K, s.R, c.G, ny, (long long)blocks, topk ? " +topk" : "");
         hipLaunchKernelGGL(topk ? c.topk : c.plain, dim3(unsigned(blocks)), dim3(c.G), 0, stream,
                            static_cast<const u32x4 *>(x), s.T, V, s.K, s.E, s.epr, s.kmax, ny,
                            b.dst_row, b.dst_rank, topk_idx, topk_weights,
-                           static_cast<u32x4 *>(recv_x), recv_topk_idx, recv_topk_weights);
+                           static_cast<u32x4 *>(recv_x), recv_topk_idx, recv_topk_weights,
+                           b.recv_src_idx, b.rank_prefix_matrix, s.R, int(ntk));
         return hipGetLastError();
     }
     const int per_block = kPackBlock / c.G;
@@ -390,7 +433,7 @@ hipError_t launch_dispatch(const LayoutShape &s, int hidden, const void *x, cons
                        static_cast<const u32x4 *>(x), s.T, V, s.K, s.E, s.epr, s.kmax, c.S,
                        b.dst_row,
                        b.dst_rank, topk_idx, topk_weights, static_cast<u32x4 *>(recv_x),
-                       recv_topk_idx, recv_topk_weights);
+                       recv_topk_idx, recv_topk_weights, nullptr, nullptr, 0, 0);
     return hipGetLastError();
 }
 

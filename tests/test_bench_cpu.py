@@ -26,8 +26,8 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_record_follows_the_kernel_source():
     path = os.path.join(bench.PROFILES, "traffic_training_T4096_H7168_K8_R64.json")
-    rec = json.load(open(path)).get("dispatch:dispatch_pack_kernel")
-    got = bench.load_traffic("dispatch.hip", "dispatch:dispatch_pack_kernel")
+    rec = json.load(open(path)).get("dispatch:dispatch_scatter_kernel")
+    got = bench.load_traffic("dispatch.hip", "dispatch:dispatch_scatter_kernel")
     if rec is not None and rec["source_sha"] == bench.kernel_source_sha("dispatch.hip"):
         # measured HBM bytes: the counters scaled by the plain-copy calibration
         exp = int(round((rec["fetch_kib"] * rec["fetch_scale"] +

@@ -393,7 +393,7 @@ def test_ep_log_lines(monkeypatch, capfd):
     buf.combine(rx, h, rtw)
     torch.cuda.synchronize()
     err = capfd.readouterr().err
-    for tag in ("[ep] layout T=128", "[ep] dispatch_pack T=128", "[ep] combine T=128"):
+    for tag in ("[ep] layout T=128", "[ep] dispatch_scatter T=128", "[ep] combine T=128"):
         assert tag in err, err
     # the rows-only dispatch through the handle logs the scatter kernel
     buf.dispatch(x, handle=h)
