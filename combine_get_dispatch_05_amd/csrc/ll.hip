@@ -117,8 +117,11 @@ __device__ __forceinline__ uint2 fp8_block(const u32x4 &v, float &amax_out)
     float amax;
     if (bits < 0x7f80u) {
         // finite block: |x * 448 / amax| stays below 464, where the hardware
-        // conversion rounds to nearest even exactly as e4m3_rne does
-        // (checked over every fp32 input).
+        // conversion rounds to nearest even, saturating, as the e4m3
+        // definition does (test_ll_dispatch_fp8_conversion_sweep compares
+        // the codes bit for bit on every bf16 magnitude up to the block's
+        // amax, for a scale of exactly 1 and for scales that are not powers
+        // of two).
         amax = __uint_as_float(bits << 16);
         amax = amax < 1e-4f ? 1e-4f : amax;
         const float sinv = 448.0f / amax;
