@@ -172,22 +172,124 @@ __global__ __launch_bounds__(kCombineBlock) void combine_kernel(
     }
 }
 
+// Gather form (a tuning shape): workgroup (t, yb) sums chunk yb (BT vectors)
+// of token t's rows, one thread per 16-byte vector: the token's rows are
+// taken kGatherRows at a time, all their loads in flight before any is added,
+// in ascending rank from +0 as above (rows on a rank masked now skipped, so
+// the order of the rest is kept), then the biases, then one rounding.  One
+// load per row and thread, in many short workgroups.  Unweighted, right after
+// a dispatch, it took 87.6 against 91.6 us at the training-scale batch; in
+// the whole step, weighted, it measured the same as the token-major form.
+// The chunk-0 workgroup's lanes k < K also sum weight k of the same rows.
+constexpr int kGatherRows = 8;
+
+template <int BT, bool kBias>
+__global__ __launch_bounds__(BT) void combine_gather_kernel(
+    const u32x4 *__restrict__ y, int T, int V, int K, int kmax, int ny,
+    const int32_t *__restrict__ dst_row, const int32_t *__restrict__ dst_rank,
+    const int32_t *__restrict__ rank_mask, const float *__restrict__ recv_topk_weights,
+    const u32x4 *__restrict__ bias0, const u32x4 *__restrict__ bias1,
+    u32x4 *__restrict__ out, float *__restrict__ combined_topk_weights)
+{
+    const int64_t t = blockIdx.x / ny;
+    const int yb = int(blockIdx.x - t * ny);
+    const int tid = threadIdx.x;
+    const int c = yb * BT + tid;
+    const int cc = c < V ? c : V - 1;  // lanes past the row re-read its last vector (not stored)
+    const int32_t *rl = dst_row + t * kmax;
+    // chunk 0's lanes k < K also sum weight k of the same rows (K <= 64 < BT)
+    const bool wsum = combined_topk_weights != nullptr && yb == 0 && tid < K;
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        acc[q] = 0.0f;
+    float w = 0.0f;
+    // a token with no rows loads nothing (y may then hold no rows at all);
+    // rows past the list or on masked ranks re-read the token's first row
+    const int row0 = rl[0];
+    bool more = row0 >= 0;
+    for (int k0 = 0; more && k0 < kmax; k0 += kGatherRows) {
+        int row[kGatherRows];
+#pragma unroll
+        for (int j = 0; j < kGatherRows; ++j) {
+            const int k = k0 + j;
+            row[j] = k < kmax ? rl[k] : -1;  // rows are packed first, then -1
+            if (row[j] >= 0 && rank_mask != nullptr && rank_mask[dst_rank[t * kmax + k]] != 0)
+                row[j] = -2;  // on a rank masked now: skipped, the list goes on
+        }
+        u32x4 v[kGatherRows];
+        float wv[kGatherRows];
+#pragma unroll
+        for (int j = 0; j < kGatherRows; ++j) {
+            const int64_t r = row[j] >= 0 ? row[j] : row0;
+            v[j] = load_row_vec<true>(y + r * V + cc);
+            wv[j] = wsum ? recv_topk_weights[r * K + tid] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kGatherRows; ++j) {
+            if (row[j] == -1) {
+                more = false;
+                break;
+            }
+            if (row[j] < 0)
+                continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += bf16_lo(v[j][q]);
+                acc[2 * q + 1] += bf16_hi(v[j][q]);
+            }
+            w += wv[j];
+        }
+    }
+    if (kBias) {
+        // after the rank sum, before the one rounding: bias0, then bias1
+        const u32x4 *biases[2] = {bias0, bias1};
+        for (int bi = 0; bi < 2; ++bi) {
+            if (biases[bi] == nullptr)
+                continue;
+            const u32x4 bv = biases[bi][t * V + cc];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += bf16_lo(bv[q]);
+                acc[2 * q + 1] += bf16_hi(bv[q]);
+            }
+        }
+    }
+    if (c < V) {
+        u32x4 r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            r[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        __builtin_nontemporal_store(r, out + t * V + c);
+    }
+    if (wsum)
+        combined_topk_weights[t * K + tid] = w;
+}
+
+// The two kernels share one argument list; the gather kernel takes its
+// chunk count ny where the token-major kernel takes S.
 typedef void (*CombineFn)(const u32x4 *, int, int, int, int, int, const int32_t *,
                           const int32_t *, const int32_t *, const float *, const u32x4 *,
                           const u32x4 *, u32x4 *, float *);
 
-// A launch shape: G lanes per group, VPT vectors per lane, S groups per token
-// (row slices), U rows in flight, NTL nontemporal row loads, and P =
-// persistent block count (0: one group per token slice).  The tuning knob
-// addresses shapes as (G, VPT, S*1000 + U*100 + NTL*10 + P/256).
+// A launch shape.  Token-major: G lanes per group, VPT vectors per lane, S
+// groups per token (row slices), U rows in flight, NTL nontemporal row
+// loads, and P = persistent block count (0: one group per token slice).
+// Gather: G threads per workgroup, one vector each, kGatherRows rows in
+// flight, nontemporal loads.  The tuning knob addresses shapes as (G, VPT,
+// X*10000 + S*1000 + U*100 + NTL*10 + P/256), X = 1 for the gather form.
 struct CombineCfg {
     int G, VPT, S, U, NTL, P;
     CombineFn fn, fn_bias;
+    int gather;
 };
 
 #define EP_COMBINE_CFG(G, VPT, S, U, NTL, P)                                               \
     {G, VPT, S, U, NTL, P, combine_kernel<G, VPT, U, NTL, false>,                          \
-     combine_kernel<G, VPT, U, NTL, true>}
+     combine_kernel<G, VPT, U, NTL, true>, 0}
+#define EP_GATHER_CFG(BT)                                                                    \
+    {BT, 1, 1, kGatherRows, 1, 0, combine_gather_kernel<BT, false>,                          \
+     combine_gather_kernel<BT, true>, 1}
 
 const CombineCfg kCombineCfgs[] = {
     EP_COMBINE_CFG(256, 1, 1, 2, 1, 0), EP_COMBINE_CFG(256, 2, 1, 2, 1, 0),
@@ -198,11 +300,12 @@ const CombineCfg kCombineCfgs[] = {
     EP_COMBINE_CFG(64, 7, 2, 2, 1, 0),  EP_COMBINE_CFG(64, 4, 4, 2, 1, 0),
     EP_COMBINE_CFG(64, 2, 7, 4, 1, 0),  EP_COMBINE_CFG(64, 2, 7, 8, 1, 0),
     EP_COMBINE_CFG(64, 1, 14, 8, 1, 0),
+    EP_GATHER_CFG(448), EP_GATHER_CFG(128),
 };
 
 int combine_code(const CombineCfg &c)
 {
-    return c.S * 1000 + c.U * 100 + c.NTL * 10 + c.P / 256;
+    return c.gather * 10000 + c.S * 1000 + c.U * 100 + c.NTL * 10 + c.P / 256;
 }
 
 std::atomic<int> g_over_g{-2}, g_over_v{-1}, g_over_u{-1};  // -2: env not read yet
@@ -212,7 +315,8 @@ std::atomic<int> g_over_g{-2}, g_over_v{-1}, g_over_u{-1};  // -2: env not read 
 // Otherwise: one chunk that covers the row exactly, one row in flight,
 // nontemporal row loads (measured best on the training-scale rows: the rows
 // are read once, and keeping them out of the caches leaves the caches to the
-// data that is reused).
+// data that is reused).  The gather form measured the same in the step
+// (92.0-93.0 against 92.8-93.1 us, one box), so the token-major form stays.
 const CombineCfg &pick(int V)
 {
     if (g_over_g.load() == -2) {
@@ -229,7 +333,8 @@ const CombineCfg &pick(int V)
         if (c.G == og && c.VPT == ov && combine_code(c) == ou)
             return c;
     for (const CombineCfg &c : kCombineCfgs)
-        if (c.S == 1 && c.U == 1 && c.NTL == 1 && c.P == 0 && c.G * c.VPT == V && c.G >= 128)
+        if (!c.gather && c.S == 1 && c.U == 1 && c.NTL == 1 && c.P == 0 && c.G * c.VPT == V &&
+            c.G >= 128)
             return c;
     if (V <= 256)
         return kCombineCfgs[0];
@@ -276,12 +381,26 @@ hipError_t launch_combine(const LayoutShape &s, int hidden, const void *y, const
         return hipSuccess;
     const int V = hidden / 8;
     const CombineCfg &c = pick(V);
+    const bool bias = bias0 != nullptr || bias1 != nullptr;
+    if (c.gather) {
+        const int ny = (V + c.G - 1) / c.G;
+        const int64_t blocks = int64_t(s.T) * ny;
+        if (log_enabled())
+            log_launch("combine_gather T=%d H=%d K=%d R=%d: BT=%d chunks=%d blocks=%lld%s%s",
+                       s.T, hidden, s.K, s.R, c.G, ny, (long long)blocks, bias ? " +bias" : "",
+                       rank_mask != nullptr ? " +mask" : "");
+        hipLaunchKernelGGL(bias ? c.fn_bias : c.fn, dim3(unsigned(blocks)), dim3(c.G), 0, stream,
+                           static_cast<const u32x4 *>(y), s.T, V, s.K, s.kmax, ny, b.dst_row,
+                           b.dst_rank, rank_mask, recv_topk_weights,
+                           static_cast<const u32x4 *>(bias0), static_cast<const u32x4 *>(bias1),
+                           static_cast<u32x4 *>(out), combined_topk_weights);
+        return hipGetLastError();
+    }
     const int per_block = kCombineBlock / c.G;
     const int64_t groups = int64_t(s.T) * c.S;
     int blocks = int((groups + per_block - 1) / per_block);
     if (c.P > 0 && c.P < blocks)
         blocks = c.P;
-    const bool bias = bias0 != nullptr || bias1 != nullptr;
     if (log_enabled())
         log_launch("combine T=%d H=%d K=%d R=%d: G=%d VPT=%d S=%d U=%d NTL=%d blocks=%d%s%s", s.T,
                    hidden, s.K, s.R, c.G, c.VPT, c.S, c.U, c.NTL, blocks, bias ? " +bias" : "",

@@ -390,8 +390,9 @@ int ep_pool_stats(size_t *kept_bytes, int32_t *kept_arenas, size_t *cap_bytes);
  * kernels, process-wide, for every later call.  Results never depend on it.
  * a = lanes per group G, b = 16-byte vectors per lane VPT, c = a code for
  * the rest: dispatch X*10000 + S*1000 + NTL*100 + NTS*10 + P/256, combine
- * S*1000 + U*100 + NTL*10 + P/256, where X = 1 for the destination-major
- * (scatter) pack (G threads per workgroup, one vector each; the default),
+ * X*10000 + S*1000 + U*100 + NTL*10 + P/256, where X = 1 for the
+ * destination-major (scatter) pack (the default) and the gather-form reduce
+ * (G threads per workgroup, one vector each),
  * S = lane groups per token (row slices), NTS/NTL = nontemporal
  * stores/loads, U = rows in flight and P = persistent block count (0 = one
  * lane group per token slice).  ep_tuning_list enumerates the compiled-in
