@@ -292,7 +292,7 @@ struct PackCfg {
     {BT, 1, 1, 1, 0, 0, dispatch_scatter_kernel<BT, false>, dispatch_scatter_kernel<BT, true>, 1}
 
 const PackCfg kPackCfgs[] = {
-    EP_SCATTER_CFG(128), EP_SCATTER_CFG(448),
+    EP_SCATTER_CFG(128), EP_SCATTER_CFG(448), EP_SCATTER_CFG(896),
     EP_PACK_CFG(256, 1, 1, 1, 0, 0),  EP_PACK_CFG(256, 2, 1, 1, 0, 0),
     EP_PACK_CFG(256, 4, 1, 1, 0, 0),  EP_PACK_CFG(128, 4, 1, 1, 0, 0),
     EP_PACK_CFG(128, 7, 1, 1, 0, 0),  EP_PACK_CFG(128, 7, 1, 0, 0, 0),
@@ -331,9 +331,12 @@ std::atomic<int> g_over_g{-2}, g_over_v{-1}, g_over_c{-1};  // -2: env not read 
 
 // Launch shape for a row of V vectors.  An override (ep_set_tuning, or the
 // env var EP_TUNE_DISPATCH="G,VPT,code") wins; results never depend on it.
-// Otherwise the scatter kernel with 448 threads per workgroup; a grid too
-// large for it takes the token-major kernel, with one chunk that covers the
-// row exactly, the most lanes, nontemporal stores and one group per token.
+// Otherwise the scatter kernel with 896 threads per workgroup when they cut
+// the row into whole chunks (H = 7168: one chunk per row; 96 against 99 us
+// for 448 threads in the training-scale step, 102-121 us for 256, 512 or
+// 640), else with 448; a grid too large for it takes the token-major kernel,
+// with one chunk that covers the row exactly, the most lanes, nontemporal
+// stores and one group per token.
 const PackCfg &pick_token_major(int V)
 {
     for (int G : {128, 256, 64})
@@ -362,8 +365,9 @@ const PackCfg &pick(const LayoutShape &s, int V)
     for (const PackCfg &c : kPackCfgs)
         if (c.G == og && c.VPT == ov && pack_code(c) == oc)
             return c.scatter && scatter_blocks(s, V, c.G) == 0 ? pick_token_major(V) : c;
-    if (scatter_blocks(s, V, kPackCfgs[1].G) > 0)
-        return kPackCfgs[1];  // scatter, 448 threads
+    const PackCfg &sc = V % kPackCfgs[2].G == 0 ? kPackCfgs[2] : kPackCfgs[1];  // 896, 448
+    if (scatter_blocks(s, V, sc.G) > 0)
+        return sc;
     return pick_token_major(V);
 }
 
