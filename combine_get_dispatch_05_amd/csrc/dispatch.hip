@@ -175,8 +175,8 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
     }
 }
 
-// Destination-major, XCD-grouped (the default for the rows-only dispatch):
-// workgroup b writes one chunk of BT vectors of kDestGroup destination rows
+// Destination-major, XCD-grouped (the default): workgroup b writes one
+// chunk of BT vectors of kDestGroup destination rows
 // of one token -- token t, destinations [kDestGroup*g, kDestGroup*(g+1)) of
 // its kmax slots (slots past the token's row count are skipped), chunk yb of
 // ny.  The hardware deals workgroup b to XCD b mod 8, and token t's
@@ -185,7 +185,9 @@ __global__ __launch_bounds__(kPackBlock) void dispatch_pack_kernel(
 // destinations.  Every thread issues one 16-byte load and kDestGroup 16-byte
 // nontemporal stores.  Many short workgroups with few stores each write HBM
 // faster than long-lived groups that each store a row many times: rows-only
-// dispatch at 4096 tokens, H = 7168, R = 64, x cold, 97 against 104 us.
+// dispatch at 4096 tokens, H = 7168, R = 64, x cold, 95 against 104 us in
+// the whole step (896 threads, two destinations per workgroup; one
+// destination exposed the row load's latency once per store: 135 us).
 //
 // With top-k outputs the first ntk workgroups (a multiple of 8, so the row
 // workgroups keep their XCDs) write them row-major: BT / K consecutive
