@@ -1255,6 +1255,6 @@ const char *ep_status_str(int status)
 
 const char *ep_last_hip_error(void) { return g_last_hip.c_str(); }
 
-int ep_version(void) { return (2 << 16) | 3; }
+int ep_version(void) { return (2 << 16) | 4; }
 
 }  // extern "C"

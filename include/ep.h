@@ -424,7 +424,8 @@ const char *ep_last_hip_error(void);
 /* ABI version: (major << 16) | minor.  2.0: rank_mask arguments of
  * ep_get_dispatch_layout, ep_dispatch and ep_combine; 2.1: ep_ll_combine_fp8;
  * 2.2: ep_pool_stats and the capped pool; 2.3: ep_get_dispatch_layout_noalloc
- * and EP_ERR_TOO_LARGE. */
+ * and EP_ERR_TOO_LARGE; 2.4: the destination-major dispatch and gather-form
+ * combine tuning shapes (code X*10000). */
 int ep_version(void);
 
 #ifdef __cplusplus

@@ -53,7 +53,7 @@ static uint16_t bf16_exact(float f) /* f exactly representable in bf16 */
 
 static int cpu_checks(void)
 {
-    CHECK(ep_version() == ((2 << 16) | 3));
+    CHECK(ep_version() == ((2 << 16) | 4));
     CHECK(strcmp(ep_status_str(EP_OK), "ok") == 0);
     CHECK(strcmp(ep_status_str(42), "unknown status") == 0);
     ep_dims d = {16, 64, 2, 8, 4, 1};
