@@ -536,7 +536,8 @@ def measure_next(args, L, abi, tr, dc, x, topk, w, d, cap, recv_x, rtw, out, cw,
     us = host_us(layout_then_n)
     rep["layout_then_handle_num_recv"] = {"avg_us": round(us, 2),
                                           "how": "ep_get_dispatch_layout, then ep_handle_num_recv "
-                                                 "(N copied into pinned memory, one stream sync)"}
+                                                 "(N copied into pinned memory, which the host "
+                                                 "polls)"}
     # combine with two bias rows
     h = ctypes.c_void_p()
     abi.check(L.ep_dispatch(ctypes.byref(d), P(x), P(topk), P(w), None, ctypes.byref(h),
