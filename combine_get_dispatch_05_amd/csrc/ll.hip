@@ -331,19 +331,30 @@ __global__ __launch_bounds__(kLLBlock) void ll_slot_kernel(
     const int i1 = i0 + chunk < TK ? i0 + chunk : TK;
     const bool held = chunk <= kSlotHold;
 
-    // ids of the chunk: batches of 8 loads in flight
+    // ids of the chunk: every load issued (in batches of 8, indexes clamped
+    // into the chunk) before any id is looked at
     int v[kSlotHold];
     int mine = 0;
     if (held) {
+        int64_t raw[kSlotHold];
 #pragma unroll
         for (int q0 = 0; q0 < kSlotHold; q0 += 8) {
             if (q0 < chunk) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    v[q0 + q] = ll_id_at(topk_idx, i0 + q0 + q, i1, E);
+                for (int q = 0; q < 8; ++q) {
+                    const int i = i0 + q0 + q;
+                    raw[q0 + q] = topk_idx[i < i1 ? i : i1 - 1];
+                }
+            }
+        }
 #pragma unroll
-                for (int q = 0; q < 8; ++q)
+        for (int q0 = 0; q0 < kSlotHold; q0 += 8) {
+            if (q0 < chunk) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    v[q0 + q] = ll_valid_id(raw[q0 + q], E);
                     mine += (v[q0 + q] == e && i0 + q0 + q < i1) ? 1 : 0;
+                }
             }
         }
     } else {
