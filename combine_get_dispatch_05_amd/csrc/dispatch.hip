@@ -294,7 +294,8 @@ struct PackCfg {
     {BT, 1, 1, 1, 0, 0, dispatch_scatter_kernel<BT, false>, dispatch_scatter_kernel<BT, true>, 1}
 
 const PackCfg kPackCfgs[] = {
-    EP_SCATTER_CFG(128), EP_SCATTER_CFG(448), EP_SCATTER_CFG(896),
+    EP_SCATTER_CFG(128), EP_SCATTER_CFG(448), EP_SCATTER_CFG(896), EP_SCATTER_CFG(640),
+    EP_SCATTER_CFG(768),
     EP_PACK_CFG(256, 1, 1, 1, 0, 0),  EP_PACK_CFG(256, 2, 1, 1, 0, 0),
     EP_PACK_CFG(256, 4, 1, 1, 0, 0),  EP_PACK_CFG(128, 4, 1, 1, 0, 0),
     EP_PACK_CFG(128, 7, 1, 1, 0, 0),  EP_PACK_CFG(128, 7, 1, 0, 0, 0),
