@@ -347,10 +347,20 @@ const PackCfg &pick_token_major(int V)
             if (!c.scatter && c.G == G && c.G * c.VPT == V && c.S == 1 && c.NTS == 1 &&
                 c.NTL == 0 && c.P == 0)
                 return c;
-    for (const PackCfg &c : kPackCfgs)  // the first token-major shapes: 256 x 1, 2, 4
-        if (!c.scatter && c.G == 256 && c.VPT == (V <= 256 ? 1 : V <= 512 ? 2 : 4))
+    const int vpt = V <= 256 ? 1 : V <= 512 ? 2 : 4;  // 256 lanes x 1, 2 or 4 (all compiled in)
+    for (const PackCfg &c : kPackCfgs)
+        if (!c.scatter && c.G == 256 && c.VPT == vpt && c.S == 1 && c.P == 0)
             return c;
-    return kPackCfgs[2];
+    __builtin_unreachable();
+}
+
+// The compiled-in scatter shape with bt threads (448 and 896 are).
+const PackCfg &scatter_cfg(int bt)
+{
+    for (const PackCfg &c : kPackCfgs)
+        if (c.scatter && c.G == bt)
+            return c;
+    __builtin_unreachable();
 }
 
 const PackCfg &pick(const LayoutShape &s, int V)
@@ -368,7 +378,7 @@ const PackCfg &pick(const LayoutShape &s, int V)
     for (const PackCfg &c : kPackCfgs)
         if (c.G == og && c.VPT == ov && pack_code(c) == oc)
             return c.scatter && scatter_blocks(s, V, c.G) == 0 ? pick_token_major(V) : c;
-    const PackCfg &sc = V % kPackCfgs[2].G == 0 ? kPackCfgs[2] : kPackCfgs[1];  // 896, 448
+    const PackCfg &sc = scatter_cfg(V % 896 == 0 ? 896 : 448);
     if (scatter_blocks(s, V, sc.G) > 0)
         return sc;
     return pick_token_major(V);
