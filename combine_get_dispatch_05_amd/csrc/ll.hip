@@ -31,26 +31,12 @@ namespace ep {
 
 namespace {
 
-constexpr int kLLBlock = 256;
-constexpr int kLLWaves = kLLBlock / kWave;
 // Threads of a workgroup that moves one row slice: the dispatch's token
 // workgroups, the copy and both combines.  All of them cut a row into the
 // same slices and number their workgroups (token, slice) in the same order.
 // Workgroup i runs on XCD i mod 8, so the combine reads each cell line on
 // the XCD whose L2 wrote it in the dispatch.
 constexpr int kTokBlock = 512;
-
-__device__ __forceinline__ int ll_wave_inclusive_scan(int v)
-{
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(v, o, kWave);
-        if (lane >= o)
-            v += n;
-    }
-    return v;
-}
 
 // OCP FP8 E4M3 ("e4m3fn") code of an fp32 value: round to nearest, ties to
 // even, saturating at +-448 (no infinities in this format; 0x7F is NaN).
@@ -177,15 +163,6 @@ __device__ __forceinline__ int ll_valid_id(int64_t v, int E)
     return (v >= 0 && v < E) ? int(v) : -1;
 }
 
-// Entry i of the flattened top-k table as ll_valid_id, for i < n; the index
-// is clamped to n - 1 (n >= 1), so the load is unconditional and a batch of
-// these calls keeps all of its loads in flight.  Callers exclude i >= n
-// where they use the value.
-__device__ __forceinline__ int ll_id_at(const int64_t *__restrict__ topk_idx, int i, int n, int E)
-{
-    return ll_valid_id(topk_idx[i < n ? i : n - 1], E);
-}
-
 // Rank of expert e >= 0 (epr experts per rank): a shift when epr is a power
 // of two (a uniform test), else a division.
 __device__ __forceinline__ int ll_rank(int e, int epr)
@@ -299,120 +276,119 @@ __device__ __forceinline__ u32x4 ll_first(const u32x4 *__restrict__ x, int64_t t
     return v;
 }
 
-constexpr int kSlotHold = 32;  // top-k entries a thread of the slot scan keeps in registers
-
-// Slot scan for batches of any size, one workgroup per expert: each thread
-// owns a contiguous chunk of the flattened [T][K] table, counts the pairs
-// naming the workgroup's expert, and one block-wide exclusive scan of those
-// counts gives every thread the first slot of its chunk, so slots follow
+// Slot scan for batches of any size, one workgroup per expert.  The
+// flattened [T][K] table is read in rounds of kHold * kSlotBlock entries
+// (kHold picked per launch from the table size), coalesced: entry
+// j * kSlotBlock + tid of the round goes to thread tid, so the
+// round's entries in index order are ordered by (j, wave, lane).  Each wave
+// takes one ballot per j of the entries naming the workgroup's expert; the
+// per-(j, wave) counts go to LDS and, behind one barrier, every wave scans
+// them (two per lane), so a matching lane's slot is the matches before its
+// row and wave plus a popcount of the ballot below its lane: slots follow
 // (token, slot) order.  Writes the expert's count, src_info (-1 in unused
 // cells) and topk_slot of its pairs; workgroup 0 also marks masked and
 // invalid slots.  A masked rank ("Dynamic Rank Masking") takes part in
 // nothing: its experts' pairs get no slot and its counts are 0.  The rows
 // are copied afterwards by ll_copy_kernel, token-major, so each token row is
 // read once.
-__global__ __launch_bounds__(kLLBlock) void ll_slot_kernel(
+constexpr int kSlotBlock = 512;
+constexpr int kSlotWaves = kSlotBlock / kWave;
+constexpr int kSlotMaxHold = 16;  // table entries per thread and round, at most
+
+template <int kHold>
+__global__ __launch_bounds__(kSlotBlock) void ll_slot_kernel(
     int T, int K, int E, int R, int epr, int S, const int64_t *__restrict__ topk_idx,
     const int32_t *__restrict__ rank_mask, int32_t *__restrict__ packed_count,
     int32_t *__restrict__ src_info, int32_t *__restrict__ topk_slot)
 {
-    __shared__ int32_t s_wsum[kLLWaves];
+    constexpr int kRound = kSlotBlock * kHold;
+    constexpr int kCounts = kHold * kSlotWaves;
+    static_assert(kCounts <= 2 * kWave, "at most two (row, wave) counts per lane");
+    // counts of (row j, wave w) at j * kSlotWaves + w; two buffers, so that a
+    // round's writes never meet the previous round's reads
+    __shared__ int32_t s_cnt[2][kCounts];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wid = tid >> 6;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int e = blockIdx.x;
     const int le = e % epr;
     const int r = e / epr;
     const bool masked = rank_mask != nullptr && rank_mask[r] != 0;
     const int cell0 = (le * R + r) * S;
     const int TK = T * K;
-    const int chunk = (TK + kLLBlock - 1) / kLLBlock;
-    const int i0 = tid * chunk < TK ? tid * chunk : TK;
-    const int i1 = i0 + chunk < TK ? i0 + chunk : TK;
-    const bool held = chunk <= kSlotHold;
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    int carry = 0;  // matches in earlier rounds
 
-    // ids of the chunk: every load issued (in batches of 8, indexes clamped
-    // into the chunk) before any id is looked at
-    int v[kSlotHold];
-    int mine = 0;
-    if (held) {
-        int64_t raw[kSlotHold];
+    for (int base = 0, round = 0; base < TK; base += kRound, ++round) {
+        // every load in flight (indexes clamped into the table) before any test
+        int64_t raw[kHold];
 #pragma unroll
-        for (int q0 = 0; q0 < kSlotHold; q0 += 8) {
-            if (q0 < chunk) {
+        for (int j = 0; j < kHold; ++j) {
+            const int i = base + j * kSlotBlock + tid;
+            raw[j] = topk_idx[i < TK ? i : TK - 1];
+        }
+        int32_t *cnt = s_cnt[round & 1];
+        uint64_t m[kHold];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int i = i0 + q0 + q;
-                    raw[q0 + q] = topk_idx[i < i1 ? i : i1 - 1];
+        for (int j = 0; j < kHold; ++j) {
+            const int i = base + j * kSlotBlock + tid;
+            m[j] = __builtin_amdgcn_ballot_w64(i < TK && raw[j] == e);
+            if (lane == 0)
+                cnt[j * kSlotWaves + wid] = __popcll(m[j]);
+        }
+        __syncthreads();
+        // exclusive scan of the round's counts in (j, wave) order: lane l
+        // holds positions l and l + 64 (0 past the end)
+        const int c_lo = lane < kCounts ? cnt[lane] : 0;
+        const int c_hi = lane + kWave < kCounts ? cnt[lane + kWave] : 0;
+        int s_lo = c_lo, s_hi = c_hi;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int n_lo = __shfl_up(s_lo, o, kWave);
+            const int n_hi = __shfl_up(s_hi, o, kWave);
+            if (lane >= o) {
+                s_lo += n_lo;
+                s_hi += n_hi;
+            }
+        }
+        const int tot_lo = __builtin_amdgcn_readlane(s_lo, kWave - 1);
+        const int ex_lo = carry + s_lo - c_lo;
+        const int ex_hi = carry + tot_lo + s_hi - c_hi;
+#pragma unroll
+        for (int j = 0; j < kHold; ++j) {
+            if (m[j] == 0)
+                continue;
+            const int idx = j * kSlotWaves + wid;
+            const int pre = idx < kWave ? __builtin_amdgcn_readlane(ex_lo, idx)
+                                        : __builtin_amdgcn_readlane(ex_hi, idx - kWave);
+            if ((m[j] >> lane) & 1) {
+                const int i = base + j * kSlotBlock + tid;
+                const int s = pre + __popcll(m[j] & below);
+                if (!masked && s < S) {
+                    topk_slot[i] = s;
+                    src_info[cell0 + s] = i / K;
+                } else {
+                    topk_slot[i] = -1;
                 }
             }
         }
+        if (e == 0) {
+            // masked or invalid slots: workgroup 0 marks them
 #pragma unroll
-        for (int q0 = 0; q0 < kSlotHold; q0 += 8) {
-            if (q0 < chunk) {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    v[q0 + q] = ll_valid_id(raw[q0 + q], E);
-                    mine += (v[q0 + q] == e && i0 + q0 + q < i1) ? 1 : 0;
-                }
+            for (int j = 0; j < kHold; ++j) {
+                const int i = base + j * kSlotBlock + tid;
+                if (i < TK && ll_valid_id(raw[j], E) < 0)
+                    topk_slot[i] = -1;
             }
         }
-    } else {
-        for (int i = i0; i < i1; i += 8) {
-            int w[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                w[q] = ll_id_at(topk_idx, i + q, i1, E);
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                mine += (w[q] == e && i + q < i1) ? 1 : 0;
-        }
-    }
-    mine = masked ? 0 : mine;
-
-    const int incl = ll_wave_inclusive_scan(mine);
-    if (lane == kWave - 1)
-        s_wsum[wid] = incl;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kLLWaves; ++w) {
-        const int c = s_wsum[w];
-        before += w < wid ? c : 0;
-        total += c;
-    }
-    int s = before + incl - mine;  // first slot of this thread's chunk
-
-    auto place = [&](int i, int val) {
-        if (val == e) {
-            if (!masked && s < S) {
-                topk_slot[i] = s;
-                src_info[cell0 + s] = i / K;
-            } else {
-                topk_slot[i] = -1;
-            }
-            s += masked ? 0 : 1;
-        } else if (e == 0 && val < 0) {
-            topk_slot[i] = -1;  // masked or invalid slots: workgroup 0 marks them
-        }
-    };
-    if (held) {
-#pragma unroll
-        for (int q0 = 0; q0 < kSlotHold; q0 += 8)
-            if (q0 < chunk)
-#pragma unroll
-                for (int q = 0; q < 8; ++q)
-                    if (i0 + q0 + q < i1)
-                        place(i0 + q0 + q, v[q0 + q]);
-    } else {
-        for (int i = i0; i < i1; ++i)
-            place(i, ll_valid_id(topk_idx[i], E));
+        carry += tot_lo + __builtin_amdgcn_readlane(s_hi, kWave - 1);
     }
 
+    const int total = masked ? 0 : carry;
     const int used = total < S ? total : S;
     if (tid == 0)
         packed_count[le * R + r] = total;
-    for (int q = used + tid; q < S; q += kLLBlock)
+    for (int q = used + tid; q < S; q += kSlotBlock)
         src_info[cell0 + q] = -1;
 }
 
@@ -825,8 +801,13 @@ hipError_t launch_ll_dispatch(const ep_dims &d, int num_slots, const void *x,
         log_launch("ll_dispatch slot scan + copy T=%d H=%d K=%d E=%d: slot blocks=%d copy "
                    "blocks=%lld%s",
                    T, d.hidden, K, E, E, rows ? (long long)T * ny : 0LL, fp8 ? " fp8" : "");
-    hipLaunchKernelGGL(ll_slot_kernel, dim3(E), dim3(kLLBlock), 0, stream, T, K, E, R, E / R,
-                       num_slots, topk_idx, rank_mask, packed_count, src_info, topk_slot);
+    const int64_t per_thread = (TK + kSlotBlock - 1) / kSlotBlock;
+    auto sk = per_thread <= 2   ? ll_slot_kernel<2>
+              : per_thread <= 4 ? ll_slot_kernel<4>
+              : per_thread <= 8 ? ll_slot_kernel<8>
+                                : ll_slot_kernel<kSlotMaxHold>;
+    hipLaunchKernelGGL(sk, dim3(E), dim3(kSlotBlock), 0, stream, T, K, E, R, E / R, num_slots,
+                       topk_idx, rank_mask, packed_count, src_info, topk_slot);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !rows || T == 0)
         return e;
