@@ -174,6 +174,8 @@ LL_CASES = [
     (32, 64, 8, 8, 4, 32, 0.0, 0.9),     # repeated experts overflow the slots: 39 pairs dropped
     (4096, 64, 8, 1, 4, 4096, 0.0, 0.0),  # the largest slot count the library accepts
     (4, 1 << 20, 8, 2, 4, 4, 0.0, 0.0),   # the longest row (H = 2^20)
+    (4096, 64, 64, 4, 8, 4096, 0.05, 0.1),  # T*K = 16384: the slot scan takes two rounds
+    (3000, 72, 40, 7, 8, 3000, 0.1, 0.1),   # T*K = 21000: three rounds, the last one ragged
 ]
 
 
