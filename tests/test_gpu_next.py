@@ -34,11 +34,15 @@ def _announce(request):
 # ------------------------------------------------------------ rank masking
 
 
-@pytest.mark.parametrize("case", ["decode", "random"])
+@pytest.mark.parametrize("case", ["decode", "random", "random_two_rounds"])
 def test_ll_rank_mask(case, ll_mode):
     if case == "decode":
         inp = config_inputs(3)
         masked = [3, 17, 31]
+    elif case == "random_two_rounds":
+        # T*K = 10000 top-k entries: the slot scan reads the table in two rounds
+        inp = random_case(9, 2500, 64, 32, 4, 8, 1, mask=0.05, dup=0.2, slots=2500)
+        masked = [2, 6]
     else:
         inp = random_case(8, 50, 136, 16, 4, 8, 1, mask=0.1, dup=0.3, slots=60)
         masked = [1, 4, 5]
