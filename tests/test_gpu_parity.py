@@ -185,6 +185,59 @@ def test_ll_random(case, ll_mode):
     run_ll(random_case(3 + T, T, H, E, K, R, 1, mask=mask, dup=dup, slots=S), seed=T)
 
 
+def test_ll_large_batch_full_size_sampled():
+    """The large low-latency batch at full size (T = 1024, H = 7168, K = 8,
+    R = 32, 1024 slots; the slot scan then the copy), as the benchmark runs
+    it: counts, src_info and topk_slot bit-exact against the oracle in full;
+    for 48 sampled tokens, every one of their cells equal to the token's row,
+    and the weighted combine (of the dispatched rows and of random expert
+    outputs) equal to the oracle's, which runs on a small problem made of
+    those tokens with its cells filled from the same expert outputs."""
+    from gen import generate
+    inp = generate(1024, 7168, 256, 8, 32, 1, seed=0, slots=1024, name="ll_large")
+    T, H, E, K, R, S = inp.T, inp.H, inp.E, inp.K, inp.R, inp.slots
+    epr = E // R
+    _, o_cnt, o_src, o_slot = oracle.ll_dispatch(inp.x, inp.topk_idx, E, R, S, with_buf=False)
+    buf = epm.Buffer(R, E)
+    x, topk, w = dev_bf16(inp.x), dev(inp.topk_idx), dev(inp.topk_weights)
+    packed, count, hdl, _, _ = buf.low_latency_dispatch(x, topk, S, E)
+    np.testing.assert_array_equal(host(count), o_cnt)
+    np.testing.assert_array_equal(host(hdl.src_info), o_src)
+    np.testing.assert_array_equal(host(hdl.topk_slot), o_slot)
+
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(T, 48, replace=False))
+    # cells of the sampled pairs, flattened over [E/R][R][S]
+    e = inp.topk_idx[toks]
+    sl = o_slot[toks]
+    ok = (e >= 0) & (sl >= 0)
+    cell = np.where(ok, ((e % epr) * R + e // epr) * S + sl, 0).astype(np.int64)
+    flat = packed.view(epr * R * S, H)
+    got = host_bits(flat[dev(cell.reshape(-1))]).reshape(len(toks), K, H)
+    for i, t in enumerate(toks):
+        for k in range(K):
+            if ok[i, k]:
+                np.testing.assert_array_equal(got[i, k], inp.x[t])
+
+    # the oracle's combine on the sampled tokens alone
+    sub_topk = np.ascontiguousarray(inp.topk_idx[toks])
+    sub_w = np.ascontiguousarray(inp.topk_weights[toks])
+    Ts = len(toks)
+    _, _, _, s_slot = oracle.ll_dispatch(inp.x[toks], sub_topk, E, R, Ts, with_buf=False)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    y = torch.randn((epr, R, S, H), generator=g, device="cuda", dtype=torch.bfloat16)
+    for what, rows in (("dispatched rows", packed), ("random expert outputs", y)):
+        out, _, _ = buf.low_latency_combine(rows, topk, w, hdl)
+        vals = host_bits(rows.view(epr * R * S, H)[dev(cell.reshape(-1))]).reshape(Ts, K, H)
+        small = np.zeros((epr, R, Ts, H), np.uint16)
+        for i in range(Ts):
+            for k in range(K):
+                if ok[i, k] and s_slot[i, k] >= 0:
+                    small[e[i, k] % epr, e[i, k] // epr, s_slot[i, k]] = vals[i, k]
+        want = oracle.ll_combine(small, sub_topk, sub_w, E, R)
+        assert_bf16_close(host_bits(out)[toks], want, what="ll combine, large batch, " + what)
+
+
 def _sweep_cases(n=40, seed=2024):
     rng = np.random.default_rng(seed)
     out = []
