@@ -25,7 +25,9 @@ marker costs the stream about 5 us).  A second pass of the same steps brackets
 only the dispatch call, which launches one kernel, with HIP events on the
 launch stream: that is the roofline figure.  Per-operation times come from a
 third, instrumented pass with events around every call (each call launches
-one kernel, except the layout: two).
+one kernel, except the layout: two); for the cached dispatch, the combine and
+the two LL operations ``back_to_back_us`` adds the time per call of the same
+operation timed back to back (one event pair around many calls).
 
 Algorithmic bytes (what the method must move; x read once, only the N copied
 rows' positions read):
@@ -308,6 +310,13 @@ def main():
                                epr)
 
     workloads = None if args.no_workloads else measure_workloads(args, L, abi)
+
+    # The same operations timed back to back (one event pair around many
+    # calls): for the latency-bound ones the per-call event markers above
+    # cost as much as the kernel.
+    for op in ("dispatch_cached", "combine", "ll_dispatch", "ll_combine"):
+        if isinstance(ceilings, dict) and isinstance(ceilings.get(op), dict):
+            op_report[op]["back_to_back_us"] = ceilings[op]["avg_us"]
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None

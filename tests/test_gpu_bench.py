@@ -66,6 +66,8 @@ def test_bench_line_keeps_the_contract():
         frac = ce["frac_of_ceiling"][f"{op}_vs_{probe}"]
         assert abs(frac - ce[probe]["avg_us"] / ce[op]["avg_us"]) < 0.01
     assert ce["pack_probe"]["bytes"] == (4096 + N) * 7168 * 2
+    for op in ("dispatch_cached", "combine", "ll_dispatch", "ll_combine"):
+        assert b["ops"][op]["back_to_back_us"] == ce[op]["avg_us"]
 
     cpu = b["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["cores"] == 1
